@@ -1,0 +1,490 @@
+"""Pins of the oracle (CPU only): each test checks the oracle against something other than itself.
+
+* published FNV-1a vectors and closed forms for the block hash;
+* hand-derived block-manager outcomes;
+* closed forms and a hand-worked example for attention;
+* PyTorch's fp64 scaled_dot_product_attention on the CPU (a library special case);
+* pure-Python brute force (math.exp, no NumPy) on tiny shapes;
+* invariances: physical block permutation, shared prefixes.
+"""
+
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import allocator as OA
+from oracle import attention as OT
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- hash
+def _golden_fnv():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "fnv1a64.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        data, h = line.split()
+        rows.append((b"" if data == "-" else bytes.fromhex(data), int(h, 16)))
+    return rows
+
+
+@pytest.mark.parametrize("data,expected", _golden_fnv())
+def test_fnv1a64_published_vectors(data, expected):
+    assert OA.fnv1a64(data) == expected
+
+
+def test_block_hash_closed_forms():
+    prime, off, m = 0x100000001B3, 0xCBF29CE484222325, 1 << 64
+    # all-zero input: xor with 0 is a no-op, so the hash is offset * prime^(8 + 4*256)
+    assert OA.block_hash(0, [0] * 256) == off * pow(prime, 1032, m) % m
+    # prev = 1 sets only the first byte (little-endian u64)
+    assert OA.block_hash(1, [0] * 256) == ((off ^ 1) * pow(prime, 1032, m)) % m
+    # token 1 in the first slot sets byte 8 (little-endian i32 after the 8 prev bytes)
+    h = off * pow(prime, 8, m) % m
+    h = ((h ^ 1) * prime) % m
+    assert OA.block_hash(0, [1] + [0] * 255) == h * pow(prime, 1023, m) % m
+    # token -1 is 0xffffffff (two's complement)
+    assert OA.block_hash(0, [-1] + [0] * 255) == OA.fnv1a64(bytes(8) + b"\xff" * 4 + bytes(1020))
+
+
+# ------------------------------------------------------------------------ allocator
+def _alloc(n, order=None, prefix=True, **kw):
+    return OA.Allocator(n, list(range(n)) if order is None else order, prefix_cache=prefix, **kw)
+
+
+def test_tiny_workload_needs_six_blocks():
+    cfg = W.config("tiny_fp32")
+    a = _alloc(8, order=[5, 2, 7, 0, 3, 6, 1, 4])
+    for b, L in enumerate(cfg["ctx"]):
+        a.add_seq(b, list(range(1000 * b, 1000 * b + L - 1)))
+        a.append(b, 99)
+    assert a.num_free() == 2
+    tables = a.block_tables(range(4), 3)
+    # FIFO: ctx 1 -> 0 prompt blocks, append pops 5; ctx 255 -> 2; ctx 256 -> 7; ctx 600 -> 0, 3, 6
+    assert tables == [[5, -1, -1], [2, -1, -1], [7, -1, -1], [0, 3, 6]]
+    a.check_invariants()
+
+
+def test_slot_is_block_times_256_plus_offset():
+    a = _alloc(4, order=[3, 1, 0, 2])
+    a.add_seq(7, list(range(300)))
+    cu, lk, slots = a.prefill_slots([7])
+    assert cu == [0, 300] and lk == [300]
+    assert slots == [3 * 256 + p for p in range(256)] + [1 * 256 + p for p in range(44)]
+    assert a.append(7, 5) == 1 * 256 + 44
+
+
+def test_prefix_hit_shares_blocks_and_counts_refs():
+    base = list(range(512))
+    a = _alloc(10)
+    assert a.add_seq(0, base + [1, 2, 3]) == 0
+    assert a.add_seq(1, base + [9] * 100) == 512
+    t = a.block_tables([0, 1], 3)
+    assert t[0][:2] == t[1][:2] and t[0][2] != t[1][2]
+    assert a.ref[t[0][0]] == 2 and a.ref[t[0][1]] == 2 and a.ref[t[1][2]] == 1
+    cu, lk, slots = a.prefill_slots([1])
+    assert cu == [0, 100] and lk == [612] and slots[0] == t[1][2] * 256
+    a.check_invariants()
+
+
+def test_block_holding_last_prompt_token_never_hits():
+    base = list(range(512))
+    a = _alloc(10)
+    a.add_seq(0, base)
+    # identical 512-token prompt: block 1 holds the last token, so only block 0 hits
+    assert a.add_seq(1, base) == 256
+    a.check_invariants()
+
+
+def test_hits_must_be_a_contiguous_prefix():
+    const = lambda prev, toks: 42  # every full block collides on one hash value
+    a = _alloc(10, hash_fn=const)
+    a.add_seq(0, [1] * 256 + [2] * 256 + [3])
+    # block 0 differs (guard rejects), so block 1 may not hit even though its tokens match
+    assert a.add_seq(1, [7] * 256 + [2] * 256 + [3]) == 0
+    a.check_invariants()
+
+
+def test_collision_guard_compares_tokens():
+    const = lambda prev, toks: 42
+    a = _alloc(10, hash_fn=const)
+    a.add_seq(0, [1] * 256 + [5])
+    assert a.add_seq(1, [2] * 256 + [5]) == 0     # same hash, other tokens: miss
+    assert a.add_seq(2, [2] * 256 + [6]) == 256   # last writer (seq 1's block) wins
+    a.check_invariants()
+
+
+def test_lazy_release_and_fifo_reuse():
+    a = _alloc(6, order=[4, 1, 5, 0, 2, 3])
+    a.add_seq(0, list(range(600)))          # blocks 4, 1, 5
+    a.free_seq(0)                            # back to the tail in reverse: 5, 1, 4
+    assert list(a.free) == [0, 2, 3, 5, 1, 4]
+    # a prompt with the same first 512 tokens hits the freed (still hashed) blocks 4 and 1
+    assert a.add_seq(1, list(range(512)) + [7]) == 512
+    assert a.block_tables([1], 3) == [[4, 1, 0]]
+    assert list(a.free) == [2, 3, 5]
+    a.check_invariants()
+
+
+def test_popped_block_forgets_its_hash():
+    a = _alloc(2, order=[0, 1])
+    a.add_seq(0, list(range(256)) + [1])      # block 0 hashed, block 1 partial
+    a.free_seq(0)                              # free: 1, 0
+    a.add_seq(1, [9] * 300)                    # pops 1, then 0 (its old entry is dropped)
+    a.free_seq(1)
+    assert a.add_seq(2, list(range(256)) + [1]) == 0
+    a.check_invariants()
+
+
+def test_no_blocks_is_atomic():
+    a = _alloc(3)
+    a.add_seq(0, list(range(300)))
+    snap = (list(a.free), list(a.ref), dict(a.table), set(a.seqs))
+    with pytest.raises(OA.AllocError) as e:
+        a.add_seq(1, list(range(1000, 1600)))
+    assert e.value.kind == "NO_BLOCKS"
+    assert (list(a.free), list(a.ref), dict(a.table), set(a.seqs)) == snap
+
+
+def test_no_blocks_counts_hit_blocks_taken_from_the_free_list():
+    a = _alloc(3)
+    a.add_seq(0, list(range(512)) + [1])  # uses all 3 blocks
+    a.free_seq(0)
+    # needs blocks 0,1 as hits (taken from the free list) + 2 misses: 4 > 3
+    with pytest.raises(OA.AllocError):
+        a.add_seq(1, list(range(512)) + [2] * 300)
+    a.check_invariants()
+
+
+def test_error_kinds():
+    a = _alloc(4)
+    a.add_seq(0, [1, 2])
+    with pytest.raises(OA.AllocError) as e:
+        a.add_seq(0, [1])
+    assert e.value.kind == "DUP_SEQ"
+    a.free_seq(0)
+    with pytest.raises(OA.AllocError) as e:
+        a.free_seq(0)
+    assert e.value.kind == "UNKNOWN_SEQ"
+    with pytest.raises(OA.AllocError) as e:
+        a.append(5, 1)
+    assert e.value.kind == "UNKNOWN_SEQ"
+    a.add_seq(1, list(range(600)))
+    with pytest.raises(OA.AllocError) as e:
+        a.block_tables([1], 2)
+    assert e.value.kind == "SMALL_BUFFER"
+
+
+def test_append_hashes_full_block_for_later_reuse():
+    a = _alloc(8)
+    a.add_seq(0, list(range(255)))
+    a.append(0, 255)                          # block 0 now full -> registered
+    a.append(0, 256)                          # pops a new block
+    assert a.add_seq(1, list(range(256)) + [5]) == 256
+    a.check_invariants()
+
+
+def test_random_ops_keep_invariants():
+    rnd = random.Random(3)
+    a = _alloc(64, order=list(np.random.default_rng(3).permutation(64)))
+    live, nid = [], 0
+    for _ in range(400):
+        op = rnd.random()
+        try:
+            if op < 0.35:
+                n = rnd.randint(0, 900)
+                toks = [rnd.randint(0, 3) for _ in range(min(n, 512))] + [rnd.randint(0, 99) for _ in range(max(0, n - 512))]
+                a.add_seq(nid, toks)
+                live.append(nid)
+                nid += 1
+            elif op < 0.8 and live:
+                a.append(rnd.choice(live), rnd.randint(0, 99))
+            elif live:
+                a.free_seq(live.pop(rnd.randrange(len(live))))
+        except OA.AllocError as e:
+            assert e.kind == "NO_BLOCKS"
+        a.check_invariants()
+
+
+# ------------------------------------------------------------------------- attention
+def _rand_paged(rng, B, Hq, Hkv, D, lens, nb=None):
+    """Random contiguous per-sequence K/V plus a random paged placement of them."""
+    need = sum(-(-L // 256) for L in lens)
+    nb = nb or need + 3
+    perm = rng.permutation(nb)
+    kc = rng.standard_normal((nb, Hkv, 256, D))
+    vc = rng.standard_normal((nb, Hkv, 256, D))
+    maxb = max(1, max(-(-L // 256) for L in lens))
+    bt = -np.ones((B, maxb), dtype=np.int64)
+    k_seq, v_seq, used = [], [], 0
+    for b, L in enumerate(lens):
+        nbk = -(-L // 256)
+        bt[b, :nbk] = perm[used:used + nbk]
+        used += nbk
+        k = rng.standard_normal((L, Hkv, D))
+        v = rng.standard_normal((L, Hkv, D))
+        for j in range(L):
+            blk, off = bt[b, j // 256], j % 256
+            kc[blk, :, off] = k[j]
+            vc[blk, :, off] = v[j]
+        k_seq.append(k)
+        v_seq.append(v)
+    q = rng.standard_normal((B, Hq, D))
+    return q, kc, vc, bt, k_seq, v_seq
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """torch SDPA in fp64 on the CPU: q [Hq][Nq][D], k/v [Hq][L][D]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=None if mask is None else torch.from_numpy(mask)[None], scale=scale)[0].numpy()
+
+
+def test_hand_worked_example():
+    r2 = math.sqrt(2.0)
+    kc = np.zeros((1, 1, 256, 2))
+    vc = np.zeros((1, 1, 256, 2))
+    kc[0, 0, 1] = [r2 * math.log(3.0), 0.0]
+    vc[0, 0, 0] = [4.0, 0.0]
+    vc[0, 0, 1] = [0.0, 4.0]
+    out = OT.decode(np.array([[[1.0, 0.0]]]), kc, vc, [[0]], [2], 1.0 / r2)
+    assert np.allclose(out[0, 0], [1.0, 3.0], atol=1e-14)
+
+
+def test_context_one_returns_the_new_value_exactly():
+    rng = np.random.default_rng(0)
+    q, kc, vc, bt, _, v_seq = _rand_paged(rng, 3, 4, 2, 8, [1, 1, 1])
+    out = OT.decode(q, kc, vc, bt, [1, 1, 1], 0.3)
+    for b in range(3):
+        for h in range(4):
+            assert np.array_equal(out[b, h], v_seq[b][0, h // 2])
+
+
+def test_zero_query_or_equal_keys_average_the_values():
+    rng = np.random.default_rng(1)
+    q, kc, vc, bt, k_seq, v_seq = _rand_paged(rng, 2, 2, 1, 4, [300, 7])
+    out = OT.decode(np.zeros_like(q), kc, vc, bt, [300, 7], 0.5)
+    for b in range(2):
+        assert np.allclose(out[b, 0], v_seq[b][:, 0].mean(axis=0), atol=1e-13)
+    kc2 = np.broadcast_to(kc[:1, :, :1], kc.shape).copy()  # every key row identical
+    out2 = OT.decode(q, kc2, vc, bt, [300, 7], 0.5)
+    for b in range(2):
+        assert np.allclose(out2[b, 1], v_seq[b][:, 0].mean(axis=0), atol=1e-13)
+
+
+def test_zero_context_gives_zero_output():
+    rng = np.random.default_rng(2)
+    q, kc, vc, bt, _, _ = _rand_paged(rng, 2, 2, 2, 4, [0, 3])
+    out = OT.decode(q, kc, vc, bt, [0, 3], 0.5)
+    assert np.all(out[0] == 0)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (4, 4), (8, 1)])
+def test_paged_decode_equals_torch_sdpa_on_contiguous(Hq, Hkv):
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    lens = [1, 255, 256, 257, 600]
+    D = 16
+    q, kc, vc, bt, k_seq, v_seq = _rand_paged(rng, len(lens), Hq, Hkv, D, lens)
+    scale = 1.0 / math.sqrt(D)
+    out = OT.decode(q, kc, vc, bt, lens, scale)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        k = np.repeat(k_seq[b].transpose(1, 0, 2), G, axis=0)  # [Hq][L][D], head h reads h // G
+        v = np.repeat(v_seq[b].transpose(1, 0, 2), G, axis=0)
+        ref = _sdpa(q[b][:, None, :], k, v, scale)[:, 0]
+        assert np.max(np.abs(out[b] - ref)) < 1e-12
+
+
+def test_decode_invariant_under_block_permutation():
+    rng = np.random.default_rng(5)
+    lens = [40, 513, 256]
+    q, kc, vc, bt, _, _ = _rand_paged(rng, 3, 4, 2, 8, lens)
+    out = OT.decode(q, kc, vc, bt, lens, 0.35)
+    pi = rng.permutation(kc.shape[0])
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[pi], vc2[pi] = kc, vc
+    bt2 = np.where(bt >= 0, pi[np.maximum(bt, 0)], -1)
+    assert np.array_equal(OT.decode(q, kc2, vc2, bt2, lens, 0.35), out)
+
+
+def _brute(qv, keys, vals, scale):
+    """Pure Python: softmax attention of one query with math.exp and explicit sums."""
+    s = [scale * sum(a * b for a, b in zip(qv, k)) for k in keys]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    z = sum(e)
+    return [sum(e[j] * vals[j][d] for j in range(len(keys))) / z for d in range(len(vals[0]))]
+
+
+def test_decode_matches_pure_python_brute_force():
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        B = rng.integers(1, 3)
+        D = int(rng.integers(1, 5))
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * int(rng.integers(1, 3))
+        lens = [int(x) for x in rng.integers(1, 6, size=B)]
+        q, kc, vc, bt, k_seq, v_seq = _rand_paged(rng, B, Hq, Hkv, D, lens)
+        out = OT.decode(q, kc, vc, bt, lens, 0.7)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                ref = _brute(q[b, h].tolist(), k_seq[b][:, g].tolist(), v_seq[b][:, g].tolist(), 0.7)
+                assert np.allclose(out[b, h], ref, rtol=0, atol=1e-13)
+
+
+def test_int8_dequantised_decode():
+    rng = np.random.default_rng(9)
+    lens = [300, 20]
+    nb, Hkv, D = 4, 2, 8
+    kq = rng.integers(-127, 128, size=(nb, Hkv, 256, D)).astype(np.int8)
+    vq = rng.integers(-127, 128, size=(nb, Hkv, 256, D)).astype(np.int8)
+    ks = rng.random((nb, Hkv)).astype(np.float32)
+    vs = rng.random((nb, Hkv)).astype(np.float32)
+    bt = [[2, 0], [3, -1]]
+    q = rng.standard_normal((2, 4, D))
+    out = OT.decode(q, kq, vq, bt, lens, 0.3, ks, vs)
+    kd = kq.astype(np.float64) * ks.astype(np.float64)[:, :, None, None]
+    vd = vq.astype(np.float64) * vs.astype(np.float64)[:, :, None, None]
+    for b, L in enumerate(lens):
+        rows = [bt[b][j // 256] for j in range(L)]
+        offs = [j % 256 for j in range(L)]
+        for h in range(4):
+            k = kd[rows, h // 2, offs]
+            v = vd[rows, h // 2, offs]
+            ref = _sdpa(q[b, h][None, None], k[None], v[None], 0.3)[0, 0]
+            assert np.max(np.abs(out[b, h] - ref)) < 1e-12
+
+
+def _bottom_right_mask(n_q, Lk):
+    i = np.arange(n_q)[:, None]
+    j = np.arange(Lk)[None, :]
+    return np.where(j <= Lk - n_q + i, 0.0, -np.inf)
+
+
+def test_prefill_equals_sdpa_with_bottom_right_causal_mask():
+    rng = np.random.default_rng(11)
+    Hq, Hkv, D = 4, 2, 8
+    lens_k = [300, 5, 520]
+    n_q = [45, 5, 264]  # first and last have a cached prefix
+    q_all, kc, vc, bt, k_seq, v_seq = _rand_paged(rng, 3, Hq, Hkv, D, lens_k)
+    cu = np.concatenate([[0], np.cumsum(n_q)])
+    q = rng.standard_normal((cu[-1], Hq, D))
+    out = OT.prefill(q, kc, vc, bt, cu, lens_k, 0.4)
+    for b in range(3):
+        k = np.repeat(k_seq[b].transpose(1, 0, 2), 2, axis=0)
+        v = np.repeat(v_seq[b].transpose(1, 0, 2), 2, axis=0)
+        qb = q[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+        ref = _sdpa(qb, k, v, 0.4, _bottom_right_mask(n_q[b], lens_k[b])).transpose(1, 0, 2)
+        assert np.max(np.abs(out[cu[b]:cu[b + 1]] - ref)) < 1e-12
+    # with no cached prefix the mask is torch's own is_causal
+    qb = q[cu[1]:cu[2]].transpose(1, 0, 2)
+    k = np.repeat(k_seq[1].transpose(1, 0, 2), 2, axis=0)
+    v = np.repeat(v_seq[1].transpose(1, 0, 2), 2, axis=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qb)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        is_causal=True, scale=0.4)[0].numpy().transpose(1, 0, 2)
+    assert np.max(np.abs(out[cu[1]:cu[2]] - ref)) < 1e-12
+    # non-causal sees every key
+    out_nc = OT.prefill(q, kc, vc, bt, cu, lens_k, 0.4, causal=False)
+    qb = q[cu[0]:cu[1]].transpose(1, 0, 2)
+    k = np.repeat(k_seq[0].transpose(1, 0, 2), 2, axis=0)
+    v = np.repeat(v_seq[0].transpose(1, 0, 2), 2, axis=0)
+    assert np.max(np.abs(out_nc[cu[0]:cu[1]] - _sdpa(qb, k, v, 0.4).transpose(1, 0, 2))) < 1e-12
+
+
+def test_prefill_last_row_equals_decode():
+    rng = np.random.default_rng(12)
+    lens = [77, 600]
+    q_dec, kc, vc, bt, _, _ = _rand_paged(rng, 2, 4, 2, 8, lens)
+    q = np.concatenate([np.zeros((76, 4, 8)), q_dec[0][None], np.zeros((599, 4, 8)), q_dec[1][None]])
+    cu = [0, 77, 677]
+    pre = OT.prefill(q, kc, vc, bt, cu, lens, 0.25)
+    dec = OT.decode(q_dec, kc, vc, bt, lens, 0.25)
+    assert np.max(np.abs(pre[76] - dec[0])) < 1e-13 and np.max(np.abs(pre[676] - dec[1])) < 1e-13
+
+
+def test_kv_store_copies_rows_and_skips_negative_slots():
+    rng = np.random.default_rng(13)
+    kc = np.full((3, 2, 256, 4), 7.5)
+    vc = np.full((3, 2, 256, 4), -7.5)
+    kn = rng.standard_normal((4, 2, 4))
+    vn = rng.standard_normal((4, 2, 4))
+    slots = [2 * 256 + 5, -1, 0, 256 + 255]
+    k2, v2 = OT.kv_store(kc, vc, kn, vn, slots)
+    assert np.array_equal(k2[2, :, 5], kn[0]) and np.array_equal(v2[0, :, 0], vn[2])
+    assert np.array_equal(k2[1, :, 255], kn[3])
+    touched = np.zeros((3, 256), bool)
+    for s in slots:
+        if s >= 0:
+            touched[s // 256, s % 256] = True
+    assert np.all(k2.transpose(0, 2, 1, 3)[~touched] == 7.5)
+    assert np.all(v2.transpose(0, 2, 1, 3)[~touched] == -7.5)
+    assert np.all(kc == 7.5)  # input untouched
+
+
+def test_shared_prefix_outputs_identical_and_prefix_cache_transparent():
+    """Group members agree on their first 512 positions; a cached prefix changes no suffix output."""
+    cfg = W.config("prefill_prefix", B=3, ctx=[700, 530, 600], Hq=2, Hkv=1, D=8, group=8)
+    wl = W.prefill_workload(cfg, 0)
+    res = {}
+    for prefix in (False, True):
+        a = OA.Allocator(wl["num_blocks"], wl["free_order"], prefix_cache=prefix)
+        ncached = [a.add_seq(i, p["tokens"]) for i, p in enumerate(wl["prompts"])]
+        cu, lk, slots = a.prefill_slots(range(3))
+        kn = np.concatenate([W.bf16_bits_to_f32(p["k"][c:]) for p, c in zip(wl["prompts"], ncached)])
+        vn = np.concatenate([W.bf16_bits_to_f32(p["v"][c:]) for p, c in zip(wl["prompts"], ncached)])
+        qn = np.concatenate([W.bf16_bits_to_f32(p["q"][c:]) for p, c in zip(wl["prompts"], ncached)])
+        kc = np.zeros((wl["num_blocks"], 1, 256, 8))
+        vc = np.zeros_like(kc)
+        kc, vc = OT.kv_store(kc, vc, kn, vn, slots)
+        out = OT.prefill(qn, kc, vc, a.block_tables(range(3), 3), cu, lk, 0.3)
+        res[prefix] = (ncached, cu, out)
+    nc, cu, out = res[False]
+    assert nc == [0, 0, 0]
+    for i in (1, 2):
+        assert np.array_equal(out[cu[i]:cu[i] + 512], out[cu[0]:cu[0] + 512])
+    nc1, cu1, out1 = res[True]
+    assert nc1 == [0, 512, 512]
+    for i in (1, 2):
+        n = cu[i + 1] - cu[i]
+        assert np.allclose(out1[cu1[i]:cu1[i + 1]], out[cu[i] + 512:cu[i] + n], atol=1e-13, rtol=0)
+
+
+# ------------------------------------------------------------------------ generators
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 3
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]  # exact ties round to even
+    ours = W.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_int8_encoding_rules():
+    rng = np.random.default_rng(1)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((300, 2, 16)).astype(np.float32)))
+    x[256:, 1] = 0.0  # second block of head 1 is all zero
+    codes, tok_s, blk_s = W.int8_encode(x, 300)
+    assert codes.min() >= -127 and codes.max() <= 127
+    assert blk_s[1, 1] == 0 and np.all(codes[256:, 1] == 0)
+    for i, (lo, hi) in enumerate([(0, 256), (256, 300)]):
+        for g in range(2):
+            s = blk_s[i, g]
+            if s == 0:
+                continue
+            assert s == np.float32(np.abs(x[lo:hi, g]).max() / 127.0)
+            assert np.all(tok_s[lo:hi, g] == s)
+            err = np.abs(codes[lo:hi, g].astype(np.float64) * s - x[lo:hi, g])
+            assert err.max() <= s / 2 * (1 + 1e-6)
+            assert np.abs(codes[lo:hi, g]).max() == 127
+
+
+def test_pack_chunks_greedy():
+    assert W.pack_chunks([1000, 3000, 200, 4096, 1], 4096) == [[0, 1], [2], [3], [4]]

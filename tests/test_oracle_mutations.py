@@ -1,0 +1,222 @@
+"""Planted mistakes in the oracle (CPU only): each must make at least one pin fail.
+
+This shows the pins in test_oracle.py are strong enough to catch the plausible
+slips -- a dropped term, a wrong index or sign, a swapped operand -- in the
+oracle they pin.  Mutants are patched into the oracle modules for the duration
+of one check and restored afterwards.
+"""
+
+from collections import deque
+
+import numpy as np
+import pytest
+
+from oracle import allocator as OA
+from oracle import attention as OT
+from tests import test_oracle as P
+
+BLOCK = 256
+
+
+def _attend_no_scale(q, k, v, scale):
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[-1])
+    s = k @ q
+    p = np.exp(s - s.max())
+    return (p / p.sum()) @ v
+
+
+def _attend_unnormalised(q, k, v, scale):
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[-1])
+    s = scale * (k @ q)
+    return np.exp(s - s.max()) @ v
+
+
+def _attend_keys_as_values(q, k, v, scale):
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[-1])
+    s = scale * (k @ q)
+    p = np.exp(s - s.max())
+    return (p / p.sum()) @ k
+
+
+def _attend_drop_last_key(q, k, v, scale):
+    return OT_attend_orig(q, k[:-1], v[:-1], scale) if k.shape[0] > 1 else OT_attend_orig(q, k, v, scale)
+
+
+def _slot_offset_shift(row, pos):
+    return int(row[pos // BLOCK]) * BLOCK + (pos + 1) % BLOCK
+
+
+def _slot_wrong_block(row, pos):
+    return int(row[(pos // BLOCK + 1) % len(row)]) * BLOCK + pos % BLOCK if row[-1] >= 0 else int(row[0]) * BLOCK + pos % BLOCK
+
+
+def _decode_gqa_modulo(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None):
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(context_lens[b])
+        for h in range(Hq):
+            g = h % Hkv
+            k = OT.gather(k_cache, block_tables[b], L, g, k_scale)
+            v = OT.gather(v_cache, block_tables[b], L, g, v_scale)
+            out[b, h] = OT.attend(q[b, h], k, v, scale)
+    return out
+
+
+def _prefill_causal_off_by_one(q, k_cache, v_cache, block_tables, cu, lk, scale, causal=True):
+    q = np.asarray(q, dtype=np.float64)
+    Nq, Hq, D = q.shape
+    G = Hq // k_cache.shape[1]
+    out = np.zeros((Nq, Hq, D))
+    for b in range(len(lk)):
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        n_q, L = q1 - q0, int(lk[b])
+        for h in range(Hq):
+            k = OT.gather(k_cache, block_tables[b], L, h // G)
+            v = OT.gather(v_cache, block_tables[b], L, h // G)
+            for i in range(n_q):
+                vis = max(1, L - n_q + i) if causal else L
+                out[q0 + i, h] = OT.attend(q[q0 + i, h], k[:vis], v[:vis], scale)
+    return out
+
+
+def _prefill_top_left(q, k_cache, v_cache, block_tables, cu, lk, scale, causal=True):
+    q = np.asarray(q, dtype=np.float64)
+    Nq, Hq, D = q.shape
+    G = Hq // k_cache.shape[1]
+    out = np.zeros((Nq, Hq, D))
+    for b in range(len(lk)):
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        L = int(lk[b])
+        for h in range(Hq):
+            k = OT.gather(k_cache, block_tables[b], L, h // G)
+            v = OT.gather(v_cache, block_tables[b], L, h // G)
+            for i in range(q1 - q0):
+                vis = i + 1 if causal else L
+                out[q0 + i, h] = OT.attend(q[q0 + i, h], k[:vis], v[:vis], scale)
+    return out
+
+
+def _gather_scale_ignored(cache, row, length, head, scale=None):
+    return OT_gather_orig(cache, row, length, head, None)
+
+
+def _fnv1(data):  # FNV-1 (multiply before xor) instead of FNV-1a
+    h = 0xCBF29CE484222325
+    for byte in data:
+        h = (h * 0x100000001B3) & ((1 << 64) - 1)
+        h ^= byte
+    return h
+
+
+def _block_hash_big_endian(prev, tokens):
+    data = bytearray(int(prev).to_bytes(8, "big"))
+    for t in tokens:
+        data += int(t).to_bytes(4, "big", signed=True)
+    return OA.fnv1a64(bytes(data))
+
+
+def _block_hash_unchained(prev, tokens):
+    return OA_block_hash_orig(0, tokens)
+
+
+def _pop_lifo(self):
+    b = self.free.pop()
+    old = self.bhash[b]
+    if old is not None and self.table.get(old) == b:
+        del self.table[old]
+    self.bhash[b] = None
+    self.btokens[b] = None
+    self.ref[b] = 1
+    return b
+
+
+def _free_forward(self, seq_id):
+    s = self.seqs.pop(seq_id, None)
+    if s is None:
+        raise OA.AllocError("UNKNOWN_SEQ", str(seq_id))
+    for b in s.blocks:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+
+def _pop_keeps_hash(self):
+    b = self.free.popleft()
+    self.ref[b] = 1
+    return b
+
+
+OT_attend_orig = OT.attend
+OT_gather_orig = OT.gather
+OA_block_hash_orig = OA.block_hash
+
+ATTN_PINS = [
+    P.test_hand_worked_example,
+    P.test_context_one_returns_the_new_value_exactly,
+    P.test_zero_query_or_equal_keys_average_the_values,
+    lambda: P.test_paged_decode_equals_torch_sdpa_on_contiguous(4, 2),
+    P.test_decode_matches_pure_python_brute_force,
+    P.test_int8_dequantised_decode,
+    P.test_prefill_equals_sdpa_with_bottom_right_causal_mask,
+]
+ALLOC_PINS = [
+    P.test_tiny_workload_needs_six_blocks,
+    P.test_slot_is_block_times_256_plus_offset,
+    P.test_prefix_hit_shares_blocks_and_counts_refs,
+    P.test_block_holding_last_prompt_token_never_hits,
+    P.test_lazy_release_and_fifo_reuse,
+    P.test_popped_block_forgets_its_hash,
+    P.test_append_hashes_full_block_for_later_reuse,
+    P.test_shared_prefix_outputs_identical_and_prefix_cache_transparent,
+]
+HASH_PINS = [lambda: [P.test_fnv1a64_published_vectors(d, e) for d, e in P._golden_fnv()],
+             P.test_block_hash_closed_forms]
+
+MUTANTS = {
+    "attend without the softmax scale": (OT, "attend", _attend_no_scale, ATTN_PINS),
+    "attend without normalisation": (OT, "attend", _attend_unnormalised, ATTN_PINS),
+    "attend weights the keys, not the values": (OT, "attend", _attend_keys_as_values, ATTN_PINS),
+    "attend drops the newest key": (OT, "attend", _attend_drop_last_key, ATTN_PINS),
+    "slot offset shifted by one": (OT, "slot_of", _slot_offset_shift, ATTN_PINS),
+    "slot reads the wrong table entry": (OT, "slot_of", _slot_wrong_block, ATTN_PINS),
+    "GQA head mapping h % Hkv": (OT, "decode", _decode_gqa_modulo, ATTN_PINS),
+    "int8 scale ignored": (OT, "gather", _gather_scale_ignored, ATTN_PINS),
+    "causal window one short": (OT, "prefill", _prefill_causal_off_by_one, ATTN_PINS),
+    "causal mask aligned top-left": (OT, "prefill", _prefill_top_left, ATTN_PINS),
+    "FNV-1 instead of FNV-1a": (OA, "fnv1a64", _fnv1, HASH_PINS),
+    "block hash big-endian": (OA, "block_hash", _block_hash_big_endian, HASH_PINS),
+    "block hash not chained": (OA, "block_hash", _block_hash_unchained, HASH_PINS + ALLOC_PINS),
+    "free list popped LIFO": (OA.Allocator, "_pop_fresh", _pop_lifo, ALLOC_PINS),
+    "free_seq in forward order": (OA.Allocator, "free_seq", _free_forward, ALLOC_PINS),
+    "popped block keeps its hash": (OA.Allocator, "_pop_fresh", _pop_keeps_hash, ALLOC_PINS),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    owner, attr, mutant, pins = MUTANTS[name]
+    monkeypatch.setattr(owner, attr, mutant)
+    if owner is OA and attr == "block_hash":
+        # the allocator captured the module function at construction time through its default
+        monkeypatch.setattr(OA.Allocator, "__init__", _init_with(OA.Allocator.__init__, mutant))
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, OA.AllocError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake: {name}"
+
+
+def _init_with(init, h):
+    def wrapped(self, *a, **kw):
+        if kw.get("hash_fn") is None:
+            kw["hash_fn"] = h
+        init(self, *a, **kw)
+    return wrapped
