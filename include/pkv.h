@@ -1,0 +1,221 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The KV cache is cut into fixed blocks of 256 tokens; a per-sequence block
+ * table maps a sequence's logical blocks onto physically scattered blocks
+ * (ocdem.com nano-vllm article, §2.1 PagedAttention; block size 256 as in
+ * "Nano-vLLM性能调优实战", §1.1 KV缓存块配置, and the intelliparadigm.com
+ * Nano-vLLM article, §2.1 动态分块内存管理).  The library provides:
+ *
+ *   - a host block manager (pkv_alloc_*) producing block tables, slot
+ *     mappings and prefix-hash reuse;
+ *   - pkv_kv_store: the store_kvcache scatter of new K/V rows by slot;
+ *   - pkv_paged_attn_decode: one query token per sequence, split-K over the
+ *     context with a log-sum-exp merge;
+ *   - pkv_paged_attn_prefill: varlen causal attention of new prompt tokens
+ *     over cached + new keys (flash_attn_with_kvcache's role in
+ *     "Nano-vLLM性能调优实战", §2.2 缓存复用策略).
+ *
+ * Conventions for every function:
+ *   - Return 0 (PKV_OK) on success, a negative pkv_status on failure; the
+ *     failure text is available from pkv_last_error() on the same thread.
+ *     Nothing throws, aborts or synchronises a stream.
+ *   - Device functions take device pointers owned by the caller and enqueue
+ *     work on `stream` (a hipStream_t; NULL = the default stream).  Buffers
+ *     must stay alive until the stream has passed the work.  The library
+ *     never allocates device memory.
+ *   - Arguments that can be checked on the host are checked before anything
+ *     is enqueued; a rejected call enqueues nothing.  Device data (slots, block
+ *     ids, lengths) is trusted: out-of-range values there are undefined.
+ *
+ * Cache layout (all dtypes): K and V are each
+ *     [num_blocks][num_kv_heads][256][head_dim]
+ * row-major, so the 256 x head_dim tile of one (block, KV head) is contiguous.
+ * Token slot s lives in block s / 256 at row s % 256.  Int8 caches carry one
+ * fp32 scale per (block, KV head): k_scale, v_scale are [num_blocks][num_kv_heads]
+ * and a stored code c means c * scale.
+ *
+ * Attention semantics (the pages give no formula; the plain reading):
+ *   out[h] = sum_j softmax_j(softmax_scale * q[h] . k_j) v_j, fp32 accumulation;
+ *   query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 256
+
+enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_INVALID = -1,      /* bad argument (null pointer, negative size, inconsistent shapes) */
+    PKV_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, dtype combination) */
+    PKV_ERR_NO_BLOCKS = -3,    /* block pool exhausted; allocator state unchanged */
+    PKV_ERR_UNKNOWN_SEQ = -4,  /* sequence id not admitted (or already freed) */
+    PKV_ERR_DUP_SEQ = -5,      /* sequence id already admitted */
+    PKV_ERR_SMALL_BUFFER = -6, /* caller buffer (table width, slot capacity, workspace) too small */
+    PKV_ERR_HIP = -7           /* a HIP runtime call or kernel launch failed */
+};
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 } pkv_dtype;
+
+typedef struct {
+    int32_t num_blocks;   /* physical blocks in the pool */
+    int32_t block_size;   /* must be 256 */
+    int32_t num_kv_heads; /* Hkv */
+    int32_t head_dim;     /* 64 or 128 */
+    int32_t kv_dtype;     /* pkv_dtype of the cache */
+} pkv_cache_desc;
+
+/* Text of the last failure on the calling thread ("" if none).  Owned by the library. */
+const char* pkv_last_error(void);
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Host block manager.
+ *
+ * Blocks come from a FIFO free pool (intelliparadigm.com Nano-vLLM article, §2.1
+ * 动态分块内存管理: ceil(len / 256) blocks, taken from the head of a free deque),
+ * are shared through reference counts ("1200行代码挑战vLLM", §2 内存管理策略), and
+ * full blocks of a prompt are reused through a hash of the prompt prefix
+ * ("1200行代码挑战vLLM", §性能优化 1. 前缀缓存).  Freed blocks keep their contents
+ * and hash until they are handed out again (lazy release; intelliparadigm.com
+ * article, §7.2 关键优化点).
+ *
+ * Exact rules (fixed so that results are reproducible bit for bit):
+ *   - The free deque starts as initial_order (a permutation of 0..num_blocks-1,
+ *     e.g. a seeded shuffle for random physical placement; NULL = 0,1,2,...).
+ *   - Full block i of a prompt (tokens 256i..256i+255) hashes as
+ *     h_i = FNV-1a-64( le64(h_{i-1}) || le32(token) x 256 ), h_{-1} = 0.
+ *   - add_seq: block i is reused ("hit") only if prefix caching is on, all
+ *     earlier blocks were hits, the table maps h_i to a block holding exactly
+ *     these tokens, and the prompt continues past the block ((i+1)*256 < n).
+ *     A hit takes a reference (and leaves the free deque if it sat there).
+ *     Every other block pops the head of the free deque, drops its old hash
+ *     entry, and -- if full -- is registered under h_i (last writer wins).
+ *   - append: a new block is popped when the position is a multiple of 256;
+ *     a block is hashed and registered when it becomes full.
+ *   - free_seq: references are dropped in reverse block order; a block whose
+ *     count reaches 0 goes to the tail of the free deque.
+ *   - add_seq, append and append_batch are atomic: on failure nothing changes.
+ *   - With prefix_cache = 0 nothing is hashed.
+ *
+ * A handle is not thread-safe: use one thread per handle.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct pkv_allocator pkv_allocator;
+
+/* Creates a manager over num_blocks blocks of block_size (must be 256) tokens.
+ * initial_order: host int32[num_blocks] permutation or NULL.  *out receives the handle. */
+int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order,
+                     int32_t prefix_cache, pkv_allocator** out);
+void pkv_alloc_destroy(pkv_allocator* a);
+
+/* Admits prompt `tokens[n]` (host) as sequence seq_id; *n_cached receives how many leading
+ * tokens (a multiple of 256) already have their KV in the cache through prefix hits. */
+int pkv_alloc_add_seq(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n,
+                      int32_t* n_cached);
+
+/* Appends one generated token to seq_id; *slot receives the cache slot of its K/V row. */
+int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t token, int32_t* slot);
+
+/* Appends tokens[i] to seq_ids[i] for i < n, in order, atomically; slots[i] receives each slot. */
+int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32_t* tokens,
+                           int32_t n, int32_t* slots);
+
+int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id);
+int pkv_alloc_num_free(const pkv_allocator* a, int32_t* out);
+
+/* Rows of int32[n][max_blocks] (host): each sequence's physical blocks, padded with -1.
+ * context_lens (host int32[n], may be NULL) receives each sequence's current length.
+ * PKV_ERR_SMALL_BUFFER if a sequence holds more than max_blocks blocks. */
+int pkv_alloc_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32_t n,
+                           int32_t max_blocks, int32_t* out, int32_t* context_lens);
+
+/* Metadata for prefilling sequences seq_ids[n] (host buffers): positions n_cached..len-1
+ * of each sequence are the new tokens.  cu_seqlens_q[n+1] = prefix sums of new-token
+ * counts, seqlens_k[n] = total lengths (cached prefix included), slot_mapping[cap] the
+ * slots of the new tokens in order; *n_slots = cu_seqlens_q[n]. */
+int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int32_t n,
+                            int32_t* cu_seqlens_q, int32_t* seqlens_k, int32_t* slot_mapping,
+                            int32_t cap, int32_t* n_slots);
+
+/* Test hook: when enable != 0 every block hashes to `value`, forcing collisions so that
+ * the token-comparison guard can be exercised. */
+int pkv_alloc_debug_constant_hash(pkv_allocator* a, int32_t enable, uint64_t value);
+
+/* ------------------------------------------------------------------------------------------
+ * store_kvcache ("Nano-vLLM性能调优实战", §2.2 缓存复用策略): for t < n with
+ * slot_mapping[t] >= 0, copy k_new[t][h][:] and v_new[t][h][:] (h < Hkv) into
+ * k_cache / v_cache at that slot.  An exact copy: the rows must already be in the
+ * cache dtype (f32, bf16 or int8 codes).  For int8 caches k_scale_new / v_scale_new
+ * ([n][Hkv] fp32, device) are written to k_scale / v_scale at [slot / 256][h]; for
+ * other dtypes all four scale pointers must be NULL.
+ * k_new, v_new: device [n][Hkv][head_dim]; slot_mapping: device int32[n]; n may be 0.
+ * ------------------------------------------------------------------------------------------ */
+int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
+                 const float* k_scale_new, const float* v_scale_new,
+                 const int32_t* slot_mapping, int32_t n, void* k_cache, void* v_cache,
+                 float* k_scale, float* v_scale, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Paged decode attention: one query token per sequence.
+ *
+ * The context of each sequence is cut into splits of blocks_per_split blocks; one
+ * workgroup handles one (sequence, KV head, split) and, when a sequence has more than
+ * one split, a second kernel merges the partial softmax states by their
+ * log-sum-exp (the max_splits knob of the intelliparadigm.com Nano-vLLM article,
+ * §8: more splits for throughput at some latency cost).
+ *
+ * pkv_decode_plan: the split count and split width the decode call will use for this
+ * shape.  max_splits = 0 picks automatically; > 0 caps the split count.
+ * pkv_decode_workspace_bytes: device workspace the decode call needs (0 when the
+ * plan has a single split).
+ * ------------------------------------------------------------------------------------------ */
+int pkv_decode_plan(int32_t B, int32_t num_kv_heads, int32_t max_context_len, int32_t max_splits,
+                    int32_t* splits, int32_t* blocks_per_split);
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t num_kv_heads,
+                                  int32_t max_context_len, int32_t max_splits);
+
+/* q: device [B][Hq][head_dim], f32 when the cache is f32, bf16 otherwise.
+ * k_cache, v_cache: device, layout above.  k_scale, v_scale: int8 caches only, else NULL.
+ * block_tables: device int32[B][max_blocks]; context_lens: device int32[B] -- the number
+ * of tokens to attend, including the one just stored; 0 gives a zero output.
+ * max_context_len: host upper bound of context_lens (sizes the split plan).
+ * out: device [B][Hq][head_dim] in the dtype of q.  workspace: device, at least
+ * pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0). */
+int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* context_lens, int32_t max_context_len, int32_t max_splits,
+                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation).
+ *
+ * q: device bf16 [total_q][Hq][head_dim], the new tokens of B sequences back to back;
+ * sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (device int32[B+1]).
+ * seqlens_k: device int32[B], all keys of sequence b (cached prefix included), read
+ * through block_tables (device int32[B][max_blocks]).  With causal != 0, new token i
+ * of sequence b sits at position seqlens_k[b] - n_q(b) + i and attends keys 0..that
+ * position (bottom-right alignment); otherwise it attends all seqlens_k[b] keys.
+ * The new tokens' K/V must already be stored (pkv_kv_store earlier on the stream).
+ * max_seqlen_q, max_seqlen_k: host upper bounds.  out: device bf16 [total_q][Hq][head_dim].
+ * ------------------------------------------------------------------------------------------ */
+int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                           const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                           int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks, float softmax_scale, int32_t causal, void* out,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

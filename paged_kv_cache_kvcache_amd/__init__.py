@@ -1,0 +1,261 @@
+"""Python binding of libpkv (ctypes): attention over a paged KV cache on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the path -- block management, the KV store, decode and
+prefill attention -- runs inside libpkv.so (host C++ and HIP kernels); PyTorch supplies device
+memory and the stream.  The names follow the C ABI in ``include/pkv.h`` without the ``pkv_``
+prefix.  Importing this module does not load the library; the first call does, and fails loudly
+when ``libpkv.so`` has not been built (``python -m paged_kv_cache_kvcache_amd.build``).
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+BLOCK = 256
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_NO_BLOCKS, ERR_UNKNOWN_SEQ, ERR_DUP_SEQ, ERR_SMALL_BUFFER, ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+STATUS_NAMES = {OK: "OK", ERR_INVALID: "INVALID", ERR_UNSUPPORTED: "UNSUPPORTED", ERR_NO_BLOCKS: "NO_BLOCKS",
+                ERR_UNKNOWN_SEQ: "UNKNOWN_SEQ", ERR_DUP_SEQ: "DUP_SEQ", ERR_SMALL_BUFFER: "SMALL_BUFFER",
+                ERR_HIP: "HIP"}
+F32, BF16, I8 = 0, 1, 2
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code, func, text):
+        self.code = code
+        self.kind = STATUS_NAMES.get(code, str(code))
+        super().__init__(f"{func}: {self.kind}: {text}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+
+_i32, _i64, _u64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,
+                                     ctypes.c_void_p, ctypes.c_size_t)
+_p32 = ctypes.POINTER(ctypes.c_int32)
+_p64 = ctypes.POINTER(ctypes.c_int64)
+_pdesc = ctypes.POINTER(CacheDesc)
+
+# name -> (restype, argtypes); mirrors include/pkv.h
+SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_alloc_create": (_i32, [_i32, _i32, _p32, _i32, ctypes.POINTER(_vp)]),
+    "pkv_alloc_destroy": (None, [_vp]),
+    "pkv_alloc_add_seq": (_i32, [_vp, _i64, _p32, _i32, _p32]),
+    "pkv_alloc_append": (_i32, [_vp, _i64, _i32, _p32]),
+    "pkv_alloc_append_batch": (_i32, [_vp, _p64, _p32, _i32, _p32]),
+    "pkv_alloc_free_seq": (_i32, [_vp, _i64]),
+    "pkv_alloc_num_free": (_i32, [_vp, _p32]),
+    "pkv_alloc_block_tables": (_i32, [_vp, _p64, _i32, _i32, _p32, _p32]),
+    "pkv_alloc_prefill_slots": (_i32, [_vp, _p64, _i32, _p32, _p32, _p32, _i32, _p32]),
+    "pkv_alloc_debug_constant_hash": (_i32, [_vp, _i32, _u64]),
+    "pkv_kv_store": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _p32, _p32]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                     _f32, _vp, _vp, _sz, _vp]),
+    "pkv_paged_attn_prefill": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
+                                      _f32, _i32, _vp, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libpkv.so (loaded after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_kvcache_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def last_error():
+    return lib().pkv_last_error().decode()
+
+
+def _check(rc, func):
+    if rc != OK:
+        raise PkvError(rc, func, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _host_i32(values):
+    import numpy as np
+    a = np.ascontiguousarray(values, dtype=np.int32)
+    return a, a.ctypes.data_as(_p32)
+
+
+def _host_i64(values):
+    import numpy as np
+    a = np.ascontiguousarray(values, dtype=np.int64)
+    return a, a.ctypes.data_as(_p64)
+
+
+def cache_desc(num_blocks, num_kv_heads, head_dim, kv_dtype):
+    return CacheDesc(int(num_blocks), BLOCK, int(num_kv_heads), int(head_dim), int(kv_dtype))
+
+
+def desc_of(k_cache):
+    """Descriptor of a cache tensor laid out [num_blocks][num_kv_heads][256][head_dim]."""
+    dt = {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}[k_cache.dtype]
+    nb, hkv, bs, d = k_cache.shape
+    if bs != BLOCK:
+        raise ValueError(f"cache block dimension is {bs}, expected {BLOCK}")
+    return cache_desc(nb, hkv, d, dt)
+
+
+# ------------------------------------------------------------------------------ block manager
+class Allocator:
+    """Host block manager (pkv_alloc_*): block tables, slot mappings, prefix reuse."""
+
+    def __init__(self, num_blocks, initial_order=None, prefix_cache=True):
+        self._h = ctypes.c_void_p()
+        order = None
+        if initial_order is not None:
+            arr, order = _host_i32(initial_order)
+            self._order = arr
+        _check(lib().pkv_alloc_create(int(num_blocks), BLOCK, order, int(bool(prefix_cache)), ctypes.byref(self._h)),
+               "pkv_alloc_create")
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and h.value and _lib is not None:
+            _lib.pkv_alloc_destroy(h)
+            self._h = ctypes.c_void_p()
+
+    def add_seq(self, seq_id, tokens):
+        arr, p = _host_i32(tokens)
+        out = ctypes.c_int32()
+        _check(lib().pkv_alloc_add_seq(self._h, int(seq_id), p, len(arr), ctypes.byref(out)), "pkv_alloc_add_seq")
+        return out.value
+
+    def append(self, seq_id, token):
+        out = ctypes.c_int32()
+        _check(lib().pkv_alloc_append(self._h, int(seq_id), int(token), ctypes.byref(out)), "pkv_alloc_append")
+        return out.value
+
+    def append_batch(self, seq_ids, tokens):
+        import numpy as np
+        ids, pi = _host_i64(seq_ids)
+        toks, pt = _host_i32(tokens)
+        slots = np.empty(len(ids), dtype=np.int32)
+        _check(lib().pkv_alloc_append_batch(self._h, pi, pt, len(ids), slots.ctypes.data_as(_p32)),
+               "pkv_alloc_append_batch")
+        return slots
+
+    def free_seq(self, seq_id):
+        _check(lib().pkv_alloc_free_seq(self._h, int(seq_id)), "pkv_alloc_free_seq")
+
+    def num_free(self):
+        out = ctypes.c_int32()
+        _check(lib().pkv_alloc_num_free(self._h, ctypes.byref(out)), "pkv_alloc_num_free")
+        return out.value
+
+    def block_tables(self, seq_ids, max_blocks, out=None, context_lens=None):
+        """int32 [n][max_blocks] (numpy, or fills ``out``), plus the sequences' lengths."""
+        import numpy as np
+        ids, pi = _host_i64(seq_ids)
+        n = len(ids)
+        tab = np.empty((n, max_blocks), dtype=np.int32) if out is None else out
+        lens = np.empty(n, dtype=np.int32) if context_lens is None else context_lens
+        _check(lib().pkv_alloc_block_tables(self._h, pi, n, int(max_blocks), tab.ctypes.data_as(_p32),
+                                            lens.ctypes.data_as(_p32)), "pkv_alloc_block_tables")
+        return tab, lens
+
+    def prefill_slots(self, seq_ids, cap):
+        import numpy as np
+        ids, pi = _host_i64(seq_ids)
+        n = len(ids)
+        cu = np.empty(n + 1, dtype=np.int32)
+        lk = np.empty(max(n, 1), dtype=np.int32)
+        slots = np.empty(max(int(cap), 1), dtype=np.int32)
+        ns = ctypes.c_int32()
+        _check(lib().pkv_alloc_prefill_slots(self._h, pi, n, cu.ctypes.data_as(_p32), lk.ctypes.data_as(_p32),
+                                             slots.ctypes.data_as(_p32), int(cap), ctypes.byref(ns)),
+               "pkv_alloc_prefill_slots")
+        return cu, lk[:n], slots[:ns.value]
+
+    def debug_constant_hash(self, enable, value=0):
+        _check(lib().pkv_alloc_debug_constant_hash(self._h, int(bool(enable)), int(value)),
+               "pkv_alloc_debug_constant_hash")
+
+
+# ------------------------------------------------------------------------------ device ops
+def kv_store(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale_new=None, v_scale_new=None,
+             k_scale=None, v_scale=None, stream=None):
+    """store_kvcache: scatter k_new/v_new [n][Hkv][D] into the caches at slot_mapping[n] (int32, -1 skips)."""
+    desc = desc_of(k_cache)
+    n = int(slot_mapping.shape[0])
+    _check(lib().pkv_kv_store(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_scale_new), _ptr(v_scale_new),
+                              _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                              _stream(stream)), "pkv_kv_store")
+
+
+def decode_plan(B, num_kv_heads, max_context_len, max_splits=0):
+    s, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pkv_decode_plan(int(B), int(num_kv_heads), int(max_context_len), int(max_splits),
+                                 ctypes.byref(s), ctypes.byref(b)), "pkv_decode_plan")
+    return s.value, b.value
+
+
+def decode_workspace_bytes(B, Hq, head_dim, num_kv_heads, max_context_len, max_splits=0):
+    return int(lib().pkv_decode_workspace_bytes(int(B), int(Hq), int(head_dim), int(num_kv_heads),
+                                                int(max_context_len), int(max_splits)))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, softmax_scale,
+                      out=None, workspace=None, max_splits=0, k_scale=None, v_scale=None, stream=None):
+    """Decode attention; q [B][Hq][D].  Allocates ``out`` / ``workspace`` with torch when not given."""
+    desc = desc_of(k_cache)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, D, desc.num_kv_heads, max_context_len, max_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode(ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
+                                       _ptr(context_lens), int(max_context_len), int(max_splits),
+                                       float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+           "pkv_paged_attn_decode")
+    return out
+
+
+def paged_attn_prefill(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache, block_tables,
+                       softmax_scale, causal=True, out=None, stream=None):
+    """Varlen prefill; q [total_q][Hq][D] bf16, cu_seqlens_q [B+1], seqlens_k [B] (device int32)."""
+    desc = desc_of(k_cache)
+    total_q, Hq, _ = q.shape
+    B = int(seqlens_k.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().pkv_paged_attn_prefill(ctypes.byref(desc), _ptr(q), int(Hq), _ptr(cu_seqlens_q), _ptr(seqlens_k),
+                                        B, int(total_q), int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]),
+                                        float(softmax_scale), int(bool(causal)), _ptr(out), _stream(stream)),
+           "pkv_paged_attn_prefill")
+    return out

@@ -1,0 +1,342 @@
+// Host block manager: the block tables, slot mappings and prefix reuse behind the paged KV cache.
+//
+// Blocks of 256 tokens come from a FIFO free pool (intelliparadigm.com Nano-vLLM article, §2.1
+// 动态分块内存管理), are shared by reference count ("1200行代码挑战vLLM", §2 内存管理策略), and full
+// prompt blocks are found again through a chained hash of the prompt prefix ("1200行代码挑战vLLM",
+// §性能优化 1. 前缀缓存).  Released blocks keep their hash and contents until reused (lazy release,
+// intelliparadigm.com article, §7.2 关键优化点).  The exact rules are listed in pkv.h.
+//
+// Data structures are chosen for O(1) steps: the free deque is an intrusive doubly linked list
+// over block ids (a hit on a released block unlinks it from the middle), the prefix table is a
+// hash map from the 64-bit chained hash to the block that last registered it.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+using pkv::fail;
+using pkv::kBlock;
+
+namespace {
+
+constexpr uint64_t kFnvOffset = 0xcbf29ce484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001b3ull;
+
+inline uint64_t fnv_byte(uint64_t h, uint8_t b) { return (h ^ b) * kFnvPrime; }
+
+// FNV-1a-64 over le64(prev) followed by le32 of each of the 256 tokens.
+uint64_t chained_block_hash(uint64_t prev, const int32_t* toks) {
+    uint64_t h = kFnvOffset;
+    for (int i = 0; i < 8; ++i) h = fnv_byte(h, uint8_t(prev >> (8 * i)));
+    for (int t = 0; t < kBlock; ++t) {
+        uint32_t u = uint32_t(toks[t]);
+        for (int i = 0; i < 4; ++i) h = fnv_byte(h, uint8_t(u >> (8 * i)));
+    }
+    return h;
+}
+
+struct Seq {
+    std::vector<int32_t> blocks;
+    std::vector<int32_t> tokens;
+    int32_t n_cached = 0;
+    uint64_t last_hash = 0;  // hash of the last full block (chain input for the next one)
+};
+
+}  // namespace
+
+struct pkv_allocator {
+    int32_t nblocks = 0;
+    bool prefix = true;
+    bool const_hash = false;
+    uint64_t const_hash_value = 0;
+
+    // free deque: intrusive list, -1 terminated
+    std::vector<int32_t> nxt, prv;
+    std::vector<uint8_t> in_free;
+    int32_t head = -1, tail = -1, nfree = 0;
+
+    std::vector<int32_t> ref;
+    std::vector<uint8_t> has_hash;
+    std::vector<uint64_t> bhash;
+    std::vector<std::vector<int32_t>> btok;  // tokens of a registered (hashed) block
+    std::unordered_map<uint64_t, int32_t> table;
+    std::unordered_map<int64_t, Seq> seqs;
+
+    uint64_t hash_block(uint64_t prev, const int32_t* toks) const {
+        return const_hash ? const_hash_value : chained_block_hash(prev, toks);
+    }
+
+    void push_back(int32_t b) {
+        nxt[b] = -1;
+        prv[b] = tail;
+        if (tail >= 0) nxt[tail] = b; else head = b;
+        tail = b;
+        in_free[b] = 1;
+        ++nfree;
+    }
+    void unlink(int32_t b) {
+        if (prv[b] >= 0) nxt[prv[b]] = nxt[b]; else head = nxt[b];
+        if (nxt[b] >= 0) prv[nxt[b]] = prv[b]; else tail = prv[b];
+        nxt[b] = prv[b] = -1;
+        in_free[b] = 0;
+        --nfree;
+    }
+    // Head of the free deque, wiped of its previous identity, with one reference.
+    int32_t pop_fresh() {
+        int32_t b = head;
+        unlink(b);
+        if (has_hash[b]) {
+            auto it = table.find(bhash[b]);
+            if (it != table.end() && it->second == b) table.erase(it);
+        }
+        has_hash[b] = 0;
+        bhash[b] = 0;
+        btok[b].clear();
+        ref[b] = 1;
+        return b;
+    }
+    void register_block(int32_t b, uint64_t h, const int32_t* toks) {
+        has_hash[b] = 1;
+        bhash[b] = h;
+        btok[b].assign(toks, toks + kBlock);
+        table[h] = b;
+    }
+};
+
+extern "C" {
+
+int pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order,
+                     int32_t prefix_cache, pkv_allocator** out) {
+    PKV_REQUIRE(out != nullptr, PKV_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    PKV_REQUIRE(block_size == kBlock, PKV_ERR_UNSUPPORTED, "block_size %d: only 256 is supported", block_size);
+    PKV_REQUIRE(num_blocks > 0 && num_blocks <= (INT32_MAX / kBlock), PKV_ERR_INVALID,
+                "num_blocks %d out of range", num_blocks);
+    pkv_allocator* a = new (std::nothrow) pkv_allocator();
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "out of host memory");
+    a->nblocks = num_blocks;
+    a->prefix = prefix_cache != 0;
+    a->nxt.assign(num_blocks, -1);
+    a->prv.assign(num_blocks, -1);
+    a->in_free.assign(num_blocks, 0);
+    a->ref.assign(num_blocks, 0);
+    a->has_hash.assign(num_blocks, 0);
+    a->bhash.assign(num_blocks, 0);
+    a->btok.resize(num_blocks);
+    std::vector<uint8_t> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+        int32_t b = initial_order ? initial_order[i] : i;
+        if (b < 0 || b >= num_blocks || seen[b]) {
+            delete a;
+            return fail(PKV_ERR_INVALID, "initial_order is not a permutation of 0..%d (entry %d = %d)",
+                        num_blocks - 1, i, b);
+        }
+        seen[b] = 1;
+        a->push_back(b);
+    }
+    *out = a;
+    return PKV_OK;
+}
+
+void pkv_alloc_destroy(pkv_allocator* a) { delete a; }
+
+int pkv_alloc_debug_constant_hash(pkv_allocator* a, int32_t enable, uint64_t value) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    a->const_hash = enable != 0;
+    a->const_hash_value = value;
+    return PKV_OK;
+}
+
+int pkv_alloc_add_seq(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t n,
+                      int32_t* n_cached) {
+    PKV_REQUIRE(a != nullptr && n_cached != nullptr, PKV_ERR_INVALID, "NULL argument");
+    PKV_REQUIRE(n >= 0 && (n == 0 || tokens != nullptr), PKV_ERR_INVALID, "bad prompt (n=%d)", n);
+    PKV_REQUIRE(a->seqs.find(seq_id) == a->seqs.end(), PKV_ERR_DUP_SEQ, "sequence %lld already admitted",
+                (long long)seq_id);
+    const int32_t nb = (n + kBlock - 1) / kBlock;
+
+    // Plan every block before touching any state, so that a shortage leaves nothing changed.
+    struct Step { int32_t hit; bool hashed; uint64_t h; };
+    std::vector<Step> plan(nb);
+    uint64_t prev = 0;
+    bool hit_ok = a->prefix;
+    int32_t misses = 0, hits_from_free = 0;
+    for (int32_t i = 0; i < nb; ++i) {
+        const int32_t* chunk = tokens + size_t(i) * kBlock;
+        const bool full = int64_t(i + 1) * kBlock <= n;
+        Step s{-1, false, 0};
+        if (full && a->prefix) {
+            s.hashed = true;
+            s.h = a->hash_block(prev, chunk);
+        }
+        if (hit_ok && s.hashed && int64_t(i + 1) * kBlock < n) {
+            auto it = a->table.find(s.h);
+            if (it != a->table.end()) {
+                int32_t cand = it->second;
+                const std::vector<int32_t>& st = a->btok[cand];
+                if (st.size() == size_t(kBlock) &&
+                    std::memcmp(st.data(), chunk, sizeof(int32_t) * kBlock) == 0)
+                    s.hit = cand;
+            }
+        }
+        if (s.hit < 0) {
+            hit_ok = false;
+            ++misses;
+        } else if (a->ref[s.hit] == 0) {
+            // count each released block once, even if (under a forced collision) it is hit twice
+            bool dup = false;
+            for (int32_t j = 0; j < i; ++j) dup = dup || plan[j].hit == s.hit;
+            if (!dup) ++hits_from_free;
+        }
+        plan[i] = s;
+        prev = s.hashed ? s.h : 0;
+    }
+    if (misses > a->nfree - hits_from_free)
+        return fail(PKV_ERR_NO_BLOCKS, "sequence %lld needs %d fresh blocks, %d free", (long long)seq_id,
+                    misses, a->nfree - hits_from_free);
+
+    Seq seq;
+    seq.blocks.reserve(nb);
+    for (int32_t i = 0; i < nb; ++i) {
+        const Step& s = plan[i];
+        if (s.hit >= 0) {
+            if (a->ref[s.hit] == 0) a->unlink(s.hit);
+            ++a->ref[s.hit];
+            seq.blocks.push_back(s.hit);
+            seq.n_cached += kBlock;
+        } else {
+            int32_t b = a->pop_fresh();
+            if (s.hashed) a->register_block(b, s.h, tokens + size_t(i) * kBlock);
+            seq.blocks.push_back(b);
+        }
+        if (s.hashed) seq.last_hash = s.h;
+    }
+    seq.tokens.assign(tokens, tokens + n);
+    *n_cached = seq.n_cached;
+    a->seqs.emplace(seq_id, std::move(seq));
+    return PKV_OK;
+}
+
+static int32_t append_one(pkv_allocator* a, Seq& s, int32_t token) {
+    const int32_t pos = int32_t(s.tokens.size());
+    if (pos % kBlock == 0) s.blocks.push_back(a->pop_fresh());
+    s.tokens.push_back(token);
+    const int32_t slot = s.blocks[pos / kBlock] * kBlock + pos % kBlock;
+    if (a->prefix && s.tokens.size() % kBlock == 0) {
+        const size_t i = s.tokens.size() / kBlock - 1;
+        const int32_t* chunk = s.tokens.data() + i * kBlock;
+        const uint64_t h = a->hash_block(s.last_hash, chunk);
+        a->register_block(s.blocks[i], h, chunk);
+        s.last_hash = h;
+    }
+    return slot;
+}
+
+int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t token, int32_t* slot) {
+    PKV_REQUIRE(a != nullptr && slot != nullptr, PKV_ERR_INVALID, "NULL argument");
+    auto it = a->seqs.find(seq_id);
+    PKV_REQUIRE(it != a->seqs.end(), PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+    PKV_REQUIRE(it->second.tokens.size() < size_t(INT32_MAX - 1), PKV_ERR_INVALID, "sequence too long");
+    if (it->second.tokens.size() % kBlock == 0 && a->nfree == 0)
+        return fail(PKV_ERR_NO_BLOCKS, "no free block for sequence %lld", (long long)seq_id);
+    *slot = append_one(a, it->second, token);
+    return PKV_OK;
+}
+
+int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32_t* tokens, int32_t n,
+                           int32_t* slots) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    PKV_REQUIRE(n >= 0, PKV_ERR_INVALID, "n = %d", n);
+    if (n == 0) return PKV_OK;
+    PKV_REQUIRE(seq_ids && tokens && slots, PKV_ERR_INVALID, "NULL argument");
+    // Validate and count the fresh blocks the whole batch needs (a sequence may repeat).
+    std::unordered_map<int64_t, size_t> len;
+    int32_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = a->seqs.find(seq_ids[i]);
+        if (it == a->seqs.end())
+            return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld (batch entry %d)", (long long)seq_ids[i], i);
+        auto ins = len.emplace(seq_ids[i], it->second.tokens.size());
+        size_t& l = ins.first->second;
+        if (l % kBlock == 0) ++need;
+        ++l;
+    }
+    if (need > a->nfree)
+        return fail(PKV_ERR_NO_BLOCKS, "batch needs %d fresh blocks, %d free", need, a->nfree);
+    for (int32_t i = 0; i < n; ++i) slots[i] = append_one(a, a->seqs.find(seq_ids[i])->second, tokens[i]);
+    return PKV_OK;
+}
+
+int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    auto it = a->seqs.find(seq_id);
+    PKV_REQUIRE(it != a->seqs.end(), PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+    const std::vector<int32_t>& bl = it->second.blocks;
+    for (auto r = bl.rbegin(); r != bl.rend(); ++r)
+        if (--a->ref[*r] == 0) a->push_back(*r);
+    a->seqs.erase(it);
+    return PKV_OK;
+}
+
+int pkv_alloc_num_free(const pkv_allocator* a, int32_t* out) {
+    PKV_REQUIRE(a != nullptr && out != nullptr, PKV_ERR_INVALID, "NULL argument");
+    *out = a->nfree;
+    return PKV_OK;
+}
+
+int pkv_alloc_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                           int32_t* out, int32_t* context_lens) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    PKV_REQUIRE(n >= 0 && max_blocks >= 0, PKV_ERR_INVALID, "n = %d, max_blocks = %d", n, max_blocks);
+    if (n == 0) return PKV_OK;
+    PKV_REQUIRE(seq_ids != nullptr && (out != nullptr || max_blocks == 0), PKV_ERR_INVALID, "NULL argument");
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = a->seqs.find(seq_ids[i]);
+        if (it == a->seqs.end())
+            return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+        if (it->second.blocks.size() > size_t(max_blocks))
+            return fail(PKV_ERR_SMALL_BUFFER, "sequence %lld holds %zu blocks > max_blocks %d",
+                        (long long)seq_ids[i], it->second.blocks.size(), max_blocks);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq& s = a->seqs.find(seq_ids[i])->second;
+        int32_t* row = out + size_t(i) * max_blocks;
+        const size_t nb = s.blocks.size();
+        std::copy(s.blocks.begin(), s.blocks.end(), row);
+        std::fill(row + nb, row + max_blocks, -1);
+        if (context_lens) context_lens[i] = int32_t(s.tokens.size());
+    }
+    return PKV_OK;
+}
+
+int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int32_t n, int32_t* cu_seqlens_q,
+                            int32_t* seqlens_k, int32_t* slot_mapping, int32_t cap, int32_t* n_slots) {
+    PKV_REQUIRE(a != nullptr && cu_seqlens_q != nullptr && n_slots != nullptr, PKV_ERR_INVALID, "NULL argument");
+    PKV_REQUIRE(n >= 0 && cap >= 0, PKV_ERR_INVALID, "n = %d, cap = %d", n, cap);
+    PKV_REQUIRE(n == 0 || (seq_ids != nullptr && seqlens_k != nullptr), PKV_ERR_INVALID, "NULL argument");
+    int64_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = a->seqs.find(seq_ids[i]);
+        if (it == a->seqs.end())
+            return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+        total += int64_t(it->second.tokens.size()) - it->second.n_cached;
+    }
+    if (total > cap) return fail(PKV_ERR_SMALL_BUFFER, "%lld new tokens > slot capacity %d", (long long)total, cap);
+    PKV_REQUIRE(total == 0 || slot_mapping != nullptr, PKV_ERR_INVALID, "slot_mapping is NULL");
+    int32_t k = 0;
+    cu_seqlens_q[0] = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq& s = a->seqs.find(seq_ids[i])->second;
+        const int32_t len = int32_t(s.tokens.size());
+        for (int32_t p = s.n_cached; p < len; ++p) slot_mapping[k++] = s.blocks[p / kBlock] * kBlock + p % kBlock;
+        cu_seqlens_q[i + 1] = k;
+        seqlens_k[i] = len;
+    }
+    *n_slots = k;
+    return PKV_OK;
+}
+
+}  // extern "C"

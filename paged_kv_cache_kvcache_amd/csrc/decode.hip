@@ -1,0 +1,555 @@
+// Paged decode attention for gfx950 (one query token per sequence).
+//
+// The pages name flash_attn_with_kvcache as the attention over the cache ("Nano-vLLM性能调优实战",
+// §2.2 缓存复用策略) and a max_splits knob that trades latency for throughput (intelliparadigm.com
+// Nano-vLLM article, closing paragraph after §8).  Everything below is this library's own design
+// for CDNA4; decode streams every KV byte once, so it is an HBM-bandwidth problem and uses no MFMA.
+//
+// Work decomposition
+//   One workgroup (4 wavefronts of 64 lanes) per (sequence, KV head, split).  A split is a run of
+//   blocks_per_split 256-token blocks.  Inside a block, wavefront w owns tokens 64w..64w+63 (a
+//   "tile"), so every wavefront walks the split's blocks with its own independent online-softmax
+//   state and no barrier until the end.
+//
+// Lane layout inside a wavefront (for all dtypes and head_dim 64/128)
+//   lane = 16 r + c.  Lane group r (16 lanes) reads rows 4i + r of the tile (i = 0..15), lane c
+//   holds elements c*E .. c*E+E-1 of each row, E = head_dim / 16.  Load i of the four groups thus
+//   covers four consecutive rows: one contiguous run of 4 * row_bytes per instruction.
+//   The G query heads that share the KV head live in registers (E elements per head per lane).
+//
+// Scores
+//   Each lane forms 16 partial dot products per head (one per row it read).  A 4-step
+//   transpose-reduction over the 16 lanes of a group (DPP row_mirror, row_half_mirror, quad
+//   permutes) halves the number of live values per step and leaves lane c holding the full score
+//   of row 4c + r: 15 exchanges per head instead of 64 for row-by-row butterflies.
+//
+// Softmax
+//   Log2 domain (scale * log2 e folded in, v_exp_f32).  Each 16-lane group keeps its own running
+//   max m (group-uniform), a per-lane partial denominator l and an accumulator acc[G][E] for its
+//   rows.  P * V broadcasts each row's probability from its owner lane with DPP row_newbcast.
+//   At the end the 16 (group, wavefront) states are merged through LDS; a multi-split sequence
+//   writes (m, l, acc) to the workspace and the reduce kernel merges the splits by log-sum-exp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 64;  // tokens per wavefront per block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -INFINITY;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------------- DPP helpers
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowMirror = 0x140;     // lane j <-> 15 - j within a row of 16
+constexpr int kRowHalfMirror = 0x141; // lane j <-> 7 - j within each half row
+constexpr int kRowNewBcast = 0x150;   // + n: broadcast lane n of each row (gfx90a and later)
+
+// Max over the 16 lanes of a row, result in every lane of the row.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<kQuadXor1>(x));
+    x = fmaxf(x, dpp<kQuadXor2>(x));
+    x = fmaxf(x, dpp<kRowHalfMirror>(x));
+    x = fmaxf(x, dpp<kRowMirror>(x));
+    return x;
+}
+
+// One transpose-reduction step: partners differ in bit BIT of the lane's row position; each keeps
+// the half of the values whose index bit matches its own and adds its partner's copy of that half.
+template <int CTRL, int HALF>
+__device__ __forceinline__ void treduce_step(float* x, bool upper) {
+#pragma unroll
+    for (int k = 0; k < HALF; ++k) {
+        const float send = upper ? x[k] : x[k + HALF];
+        const float keep = upper ? x[k + HALF] : x[k];
+        x[k] = keep + dpp<CTRL>(send);
+    }
+}
+
+// x[0..15] are per-lane partial sums of rows 0..15; returns the full sum of row c (c = lane % 16).
+__device__ __forceinline__ float transpose_reduce16(float* x, int c) {
+    treduce_step<kRowMirror, 8>(x, (c >> 3) & 1);
+    treduce_step<kRowHalfMirror, 4>(x, (c >> 2) & 1);
+    treduce_step<kQuadXor2, 2>(x, (c >> 1) & 1);
+    treduce_step<kQuadXor1, 1>(x, c & 1);
+    return x[0];
+}
+
+template <int N>
+__device__ __forceinline__ float bcast_row(float x) {
+    return dpp<kRowNewBcast + N>(x);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// ------------------------------------------------------------------------------ dtype traits
+// A lane's E-element piece of one row is W dwords.
+template <int DT, int D>
+struct Traits;
+
+template <int D>
+struct Traits<PKV_F32, D> {
+    static constexpr int E = D / 16;
+    static constexpr int W = E;
+    static constexpr int kRowBytes = D * 4;
+    using QReg = float[E];
+    __device__ static void load_q(QReg& q, const void* qp, size_t off) {
+        const float* p = static_cast<const float*>(qp) + off;
+#pragma unroll
+        for (int e = 0; e < E; ++e) q[e] = p[e];
+    }
+    __device__ static float dot(const QReg& q, const uint32_t* w) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = fmaf(q[e], __uint_as_float(w[e]), s);
+        return s;
+    }
+    __device__ static void unpack(const uint32_t* w, float* v) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = __uint_as_float(w[e]);
+    }
+};
+
+template <int D>
+struct Traits<PKV_BF16, D> {
+    static constexpr int E = D / 16;
+    static constexpr int W = E / 2;
+    static constexpr int kRowBytes = D * 2;
+    using QReg = uint32_t[W];  // packed bf16 pairs
+    __device__ static void load_q(QReg& q, const void* qp, size_t off) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(qp) + off);
+#pragma unroll
+        for (int k = 0; k < W; ++k) q[k] = p[k];
+    }
+    __device__ static float dot(const QReg& q, const uint32_t* w) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < W; ++k)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[k]),
+                                                __builtin_bit_cast(bf16x2_t, w[k]), s, false);
+        return s;
+    }
+    __device__ static void unpack(const uint32_t* w, float* v) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            v[2 * k] = bf16_lo(w[k]);
+            v[2 * k + 1] = bf16_hi(w[k]);
+        }
+    }
+};
+
+template <int D>
+struct Traits<PKV_I8, D> {
+    static constexpr int E = D / 16;
+    static constexpr int W = E / 4;
+    static constexpr int kRowBytes = D;
+    using QReg = float[E];  // bf16 query widened to fp32
+    __device__ static void load_q(QReg& q, const void* qp, size_t off) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(qp) + off);
+#pragma unroll
+        for (int k = 0; k < E / 2; ++k) {
+            q[2 * k] = bf16_lo(p[k]);
+            q[2 * k + 1] = bf16_hi(p[k]);
+        }
+    }
+    __device__ static float code(uint32_t w, int byte) {
+        return float(int32_t(w << (24 - 8 * byte)) >> 24);
+    }
+    __device__ static float dot(const QReg& q, const uint32_t* w) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = fmaf(q[e], code(w[e / 4], e % 4), s);
+        return s;
+    }
+    __device__ static void unpack(const uint32_t* w, float* v) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = code(w[e / 4], e % 4);
+    }
+};
+
+template <int W>
+__device__ __forceinline__ void load_piece(const char* p, uint32_t* w) {
+    if constexpr (W == 1) {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (W == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        w[0] = x.x; w[1] = x.y;
+    } else {
+#pragma unroll
+        for (int k = 0; k < W; k += 4) {
+            const uint4 x = reinterpret_cast<const uint4*>(p)[k / 4];
+            w[k] = x.x; w[k + 1] = x.y; w[k + 2] = x.z; w[k + 3] = x.w;
+        }
+    }
+}
+
+struct DecodeArgs {
+    const void* q;
+    const char* k_cache;
+    const char* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    void* out;
+    float* ws_acc;  // [B][Hq][S][D]
+    float* ws_ml;   // [B][Hq][S][2]  (max in log2 units, denominator)
+    int32_t max_blocks;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t splits;
+    int32_t blocks_per_split;
+    float scale_log2;  // softmax_scale * log2(e)
+};
+
+// --------------------------------------------------------------------------- split kernel
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+    using T = Traits<DT, D>;
+    constexpr int E = T::E, W = T::W, RB = T::kRowBytes, PB = W * 4;
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int ctx = a.context_lens[b];
+    const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
+    const int blk0 = s * a.blocks_per_split;
+    const int blk1 = min(nblk, blk0 + a.blocks_per_split);
+    if (a.splits > 1 && blk0 >= blk1) return;  // empty split: the reduce kernel skips it
+
+    // the wavefront index is uniform per wavefront: keep it (and the loop bounds) in scalar registers
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane >> 4, c = lane & 15;
+
+    typename T::QReg qr[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        T::load_q(qr[j], a.q, (size_t(b) * a.num_q_heads + g * G + j) * D + c * E);
+
+    float m[G], l[G], acc[G][E];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        m[j] = kNegInf;
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
+    }
+
+    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    const size_t lane_off = size_t(r) * RB + size_t(c) * PB;
+
+    for (int blk = blk0; blk < blk1; ++blk) {
+        const int t0 = blk * pkv::kBlock + w * kTile;
+        if (t0 >= ctx) break;
+        const int valid = min(kTile, ctx - t0);
+        const int64_t phys = bt[blk];
+        const size_t tile = ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB;
+        const char* kp = a.k_cache + tile + lane_off;
+        const char* vp = a.v_cache + tile + lane_off;
+
+        uint32_t kw[16][W], vw[16][W];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (4 * i + r < valid) {
+                load_piece<W>(kp + size_t(4 * i) * RB, kw[i]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < W; ++k) kw[i][k] = 0u;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (4 * i + r < valid) {
+                load_piece<W>(vp + size_t(4 * i) * RB, vw[i]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < W; ++k) vw[i][k] = 0u;
+            }
+        }
+
+        float ks = a.scale_log2, vs = 1.f;
+        if constexpr (DT == PKV_I8) {
+            ks *= a.k_scale[phys * a.num_kv_heads + g];
+            vs = a.v_scale[phys * a.num_kv_heads + g];
+        }
+        const bool row_ok = 4 * c + r < valid;
+
+        float p[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float part[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) part[i] = T::dot(qr[j], kw[i]);
+            // every lane must take part in the DPP exchanges: reduce first, mask afterwards
+            const float tot = transpose_reduce16(part, c);
+            const float sc = row_ok ? tot * ks : kNegInf;
+            const float mn = fmaxf(m[j], row_max16(sc));
+            const bool none = mn == kNegInf;
+            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
+            p[j] = none ? 0.f : __builtin_amdgcn_exp2f(sc - mn);
+            m[j] = mn;
+            l[j] = l[j] * alpha + p[j];
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[j][e] *= alpha;
+            p[j] *= vs;
+        }
+
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float v[E];
+            T::unpack(vw[i], v);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float pi;
+                switch (i) {  // DPP lane selects must be immediates
+                    case 0: pi = bcast_row<0>(p[j]); break;
+                    case 1: pi = bcast_row<1>(p[j]); break;
+                    case 2: pi = bcast_row<2>(p[j]); break;
+                    case 3: pi = bcast_row<3>(p[j]); break;
+                    case 4: pi = bcast_row<4>(p[j]); break;
+                    case 5: pi = bcast_row<5>(p[j]); break;
+                    case 6: pi = bcast_row<6>(p[j]); break;
+                    case 7: pi = bcast_row<7>(p[j]); break;
+                    case 8: pi = bcast_row<8>(p[j]); break;
+                    case 9: pi = bcast_row<9>(p[j]); break;
+                    case 10: pi = bcast_row<10>(p[j]); break;
+                    case 11: pi = bcast_row<11>(p[j]); break;
+                    case 12: pi = bcast_row<12>(p[j]); break;
+                    case 13: pi = bcast_row<13>(p[j]); break;
+                    case 14: pi = bcast_row<14>(p[j]); break;
+                    default: pi = bcast_row<15>(p[j]); break;
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[j][e] = fmaf(pi, v[e], acc[j][e]);
+            }
+        }
+    }
+
+    // ---- merge the four lane groups of this wavefront, then the four wavefronts through LDS
+    __shared__ float s_m[kWaves][G], s_l[kWaves][G];
+    __shared__ float s_acc[kWaves][G][D];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float M = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
+        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        const float f = m[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[j] - M);
+        const float L = wave_sum(l[j] * f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float x = acc[j][e] * f;
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            acc[j][e] = x;
+        }
+        if (lane == 0) {
+            s_m[w][j] = M;
+            s_l[w][j] = L;
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_acc[w][j][c * E + e] = acc[j][e];
+        }
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int j = idx / D, d = idx - j * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][j]);
+        float num = 0.f, den = 0.f;
+        if (M != kNegInf) {
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = s_m[ww][j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s_m[ww][j] - M);
+                num += f * s_acc[ww][j][d];
+                den += f * s_l[ww][j];
+            }
+        }
+        const int h = g * G + j;
+        if (a.splits == 1) {
+            const float o = den > 0.f ? num / den : 0.f;
+            const size_t oi = (size_t(b) * a.num_q_heads + h) * D + d;
+            if constexpr (DT == PKV_F32) static_cast<float*>(a.out)[oi] = o;
+            else static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
+        } else {
+            const size_t part = (size_t(b) * a.num_q_heads + h) * a.splits + s;
+            a.ws_acc[part * D + d] = num;
+            if (d == 0) {
+                a.ws_ml[2 * part] = M;
+                a.ws_ml[2 * part + 1] = den;
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------- split reduce
+// out[b][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the non-empty splits.
+template <int D, bool F32_OUT>
+__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int ctx = a.context_lens[b];
+    const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
+    const int active = min(a.splits, (nblk + a.blocks_per_split - 1) / a.blocks_per_split);
+    const size_t base = (size_t(b) * a.num_q_heads + h) * a.splits;
+    float M = kNegInf;
+    for (int s = 0; s < active; ++s) M = fmaxf(M, a.ws_ml[2 * (base + s)]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < active; ++s) {
+        const float f = __builtin_amdgcn_exp2f(a.ws_ml[2 * (base + s)] - M);
+        num += f * a.ws_acc[(base + s) * D + d];
+        den += f * a.ws_ml[2 * (base + s) + 1];
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    const size_t oi = (size_t(b) * a.num_q_heads + h) * D + d;
+    if constexpr (F32_OUT) static_cast<float*>(a.out)[oi] = o;
+    else static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
+}
+
+// ------------------------------------------------------------------------------ planning
+constexpr int kTargetWorkgroups = 2048;  // about 8 per CU on 256 CUs
+
+void plan(int B, int Hkv, int max_ctx, int max_splits, int* splits, int* bps) {
+    const int nblk = std::max(1, (max_ctx + pkv::kBlock - 1) / pkv::kBlock);
+    int S;
+    if (max_splits > 0) {
+        S = std::min(max_splits, nblk);
+    } else {
+        const long base = long(B) * Hkv;
+        S = int(std::min<long>(nblk, std::max<long>(1, (kTargetWorkgroups + base - 1) / base)));
+    }
+    *bps = (nblk + S - 1) / S;
+    *splits = (nblk + *bps - 1) / *bps;
+}
+
+template <int DT, int D, int G>
+hipError_t launch(const DecodeArgs& a, int B, hipStream_t st) {
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, G>), dim3(a.splits, a.num_kv_heads, B), dim3(kThreads), 0,
+                       st, a);
+    if (a.splits > 1)
+        hipLaunchKernelGGL((decode_reduce_kernel<D, DT == PKV_F32>), dim3(a.num_q_heads, B), dim3(D), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_g(const DecodeArgs& a, int B, int G, hipStream_t st) {
+    switch (G) {
+        case 1: return launch<DT, D, 1>(a, B, st);
+        case 2: return launch<DT, D, 2>(a, B, st);
+        case 4: return launch<DT, D, 4>(a, B, st);
+        case 8: return launch<DT, D, 8>(a, B, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT>
+hipError_t launch_d(const DecodeArgs& a, int B, int G, int D, hipStream_t st) {
+    return D == 64 ? launch_g<DT, 64>(a, B, G, st) : launch_g<DT, 128>(a, B, G, st);
+}
+
+}  // namespace
+
+extern "C" int pkv_decode_plan(int32_t B, int32_t num_kv_heads, int32_t max_context_len, int32_t max_splits,
+                               int32_t* splits, int32_t* blocks_per_split) {
+    PKV_REQUIRE(splits && blocks_per_split, PKV_ERR_INVALID, "NULL argument");
+    PKV_REQUIRE(B >= 0 && num_kv_heads > 0 && max_context_len >= 0 && max_splits >= 0, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hkv=%d, max_context_len=%d, max_splits=%d)", B, num_kv_heads,
+                max_context_len, max_splits);
+    plan(B, num_kv_heads, max_context_len, max_splits, splits, blocks_per_split);
+    return PKV_OK;
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t num_kv_heads,
+                                             int32_t max_context_len, int32_t max_splits) {
+    if (B <= 0 || Hq <= 0 || head_dim <= 0 || num_kv_heads <= 0 || max_context_len < 0 || max_splits < 0)
+        return 0;
+    int S, bps;
+    plan(B, num_kv_heads, max_context_len, max_splits, &S, &bps);
+    if (S <= 1) return 0;
+    return size_t(B) * Hq * S * (size_t(head_dim) + 2) * sizeof(float);
+}
+
+extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                     const void* k_cache, const void* v_cache, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                                     const int32_t* context_lens, int32_t max_context_len, int32_t max_splits,
+                                     float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    const int Hkv = desc->num_kv_heads, D = desc->head_dim;
+    PKV_REQUIRE(B >= 0 && Hq > 0 && max_blocks >= 0 && max_context_len >= 0 && max_splits >= 0,
+                PKV_ERR_INVALID, "bad shape (B=%d, Hq=%d, max_blocks=%d, max_context_len=%d, max_splits=%d)",
+                B, Hq, max_blocks, max_context_len, max_splits);
+    PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+    const int G = Hq / Hkv;
+    PKV_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, PKV_ERR_UNSUPPORTED,
+                "query group size %d (Hq/Hkv): supported 1, 2, 4, 8", G);
+    PKV_REQUIRE(int64_t(max_blocks) * pkv::kBlock >= max_context_len, PKV_ERR_INVALID,
+                "max_blocks %d cannot hold max_context_len %d", max_blocks, max_context_len);
+    PKV_REQUIRE(B <= 65535 && Hkv <= 65535, PKV_ERR_UNSUPPORTED, "B and Hkv must be at most 65535");
+    PKV_REQUIRE(std::isfinite(softmax_scale), PKV_ERR_INVALID, "softmax_scale is not finite");
+    const bool i8 = desc->kv_dtype == PKV_I8;
+    PKV_REQUIRE(i8 == (k_scale != nullptr) && i8 == (v_scale != nullptr), PKV_ERR_INVALID,
+                "k_scale / v_scale are required for int8 caches and rejected otherwise");
+    if (B == 0) return PKV_OK;
+    PKV_REQUIRE(q && k_cache && v_cache && block_tables && context_lens && out, PKV_ERR_INVALID, "NULL pointer");
+    const uintptr_t mis = uintptr_t(q) | uintptr_t(k_cache) | uintptr_t(v_cache) | uintptr_t(out);
+    PKV_REQUIRE((mis & 15) == 0, PKV_ERR_INVALID, "q, caches and out must be 16-byte aligned");
+
+    DecodeArgs a{};
+    a.q = q;
+    a.k_cache = static_cast<const char*>(k_cache);
+    a.v_cache = static_cast<const char*>(v_cache);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.max_blocks = max_blocks;
+    a.num_kv_heads = Hkv;
+    a.num_q_heads = Hq;
+    a.scale_log2 = softmax_scale * kLog2e;
+    plan(B, Hkv, max_context_len, max_splits, &a.splits, &a.blocks_per_split);
+    if (a.splits > 1) {
+        const size_t need = size_t(B) * Hq * a.splits * (size_t(D) + 2) * sizeof(float);
+        PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_SMALL_BUFFER,
+                    "decode needs %zu workspace bytes for %d splits, got %zu", need, a.splits, workspace_bytes);
+        PKV_REQUIRE((uintptr_t(workspace) & 15) == 0, PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+        a.ws_acc = static_cast<float*>(workspace);
+        a.ws_ml = a.ws_acc + size_t(B) * Hq * a.splits * D;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (desc->kv_dtype) {
+        case PKV_F32: e = launch_d<PKV_F32>(a, B, G, D, st); break;
+        case PKV_BF16: e = launch_d<PKV_BF16>(a, B, G, D, st); break;
+        default: e = launch_d<PKV_I8>(a, B, G, D, st); break;
+    }
+    PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+}

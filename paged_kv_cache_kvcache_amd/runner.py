@@ -1,0 +1,146 @@
+"""Drives the hot path on one GPU: admit prompts, store their KV, run decode steps and prefill chunks.
+
+This is the engine-side glue around the library, the way a scheduler would call it: the block
+manager hands out blocks and slots (host), the metadata goes to the device in one pinned copy, the
+store kernel writes the new K/V rows, then the attention kernel runs.  Every computation happens in
+libpkv; this module only moves arrays.
+"""
+
+import numpy as np
+import torch
+
+from . import (BF16, BLOCK, F32, I8, Allocator, decode_workspace_bytes, kv_store, paged_attn_decode,
+               paged_attn_prefill)
+
+TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
+
+
+def _to_dev(a, device, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+def bf16_tensor(bits_u16, device):
+    """Device bf16 tensor from bf16 bit patterns held in a uint16 numpy array."""
+    return _to_dev(np.asarray(bits_u16, dtype=np.uint16).view(np.int16), device, torch.bfloat16)
+
+
+class PagedKV:
+    """A paged KV cache pool plus its block manager."""
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, kv_dtype, free_order=None, prefix_cache=True,
+                 device="cuda", fill=None):
+        self.num_blocks, self.Hkv, self.D, self.dtype = int(num_blocks), int(num_kv_heads), int(head_dim), kv_dtype
+        self.device = torch.device(device)
+        self.alloc = Allocator(num_blocks, free_order, prefix_cache)
+        shape = (self.num_blocks, self.Hkv, BLOCK, self.D)
+        tdt = TORCH_DTYPE[kv_dtype]
+        self.k_cache = torch.empty(shape, dtype=tdt, device=self.device)
+        self.v_cache = torch.empty(shape, dtype=tdt, device=self.device)
+        if fill is not None:
+            self.k_cache.fill_(fill)
+            self.v_cache.fill_(fill)
+        self.k_scale = self.v_scale = None
+        if kv_dtype == I8:
+            self.k_scale = torch.zeros((self.num_blocks, self.Hkv), dtype=torch.float32, device=self.device)
+            self.v_scale = torch.zeros_like(self.k_scale)
+
+    def store(self, slots, k_rows, v_rows, k_scale_rows=None, v_scale_rows=None):
+        """Scatter device rows [n][Hkv][D] to device int32 slots[n]."""
+        kv_store(k_rows, v_rows, slots, self.k_cache, self.v_cache, k_scale_rows, v_scale_rows,
+                 self.k_scale, self.v_scale)
+
+
+class DecodeBatch:
+    """A batch of sequences in decode: history admitted and stored, then one token per step."""
+
+    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0):
+        self.kv = kv
+        self.Hq = int(Hq)
+        self.ids = np.asarray(seq_ids, dtype=np.int64)
+        self.B = len(self.ids)
+        self.max_blocks = max(1, -(-int(max_context_len) // BLOCK))
+        self.max_context_len = int(max_context_len)
+        self.max_splits = max_splits
+        dev = kv.device
+        # pinned staging for the per-step metadata: slots[B] | lens[B] | tables[B][max_blocks]
+        self._pin = torch.empty(2 * self.B + self.B * self.max_blocks, dtype=torch.int32).pin_memory()
+        self._meta = torch.empty_like(self._pin, device=dev)
+        self._copied = torch.cuda.Event()
+        self._copied.record()
+        self.slots = self._meta[:self.B]
+        self.context_lens = self._meta[self.B:2 * self.B]
+        self.block_tables = self._meta[2 * self.B:].view(self.B, self.max_blocks)
+        nbytes = decode_workspace_bytes(self.B, self.Hq, kv.D, kv.Hkv, self.max_context_len, max_splits)
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+    def upload_step_metadata(self, slots):
+        """Block tables and lengths of every sequence plus the new tokens' slots: one pinned H2D copy."""
+        self._copied.synchronize()  # the previous copy has left the staging buffer
+        pin = self._pin.numpy()
+        B, mb = self.B, self.max_blocks
+        pin[:B] = slots
+        tab = pin[2 * B:].reshape(B, mb)
+        self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=pin[B:2 * B])
+        self._meta.copy_(self._pin, non_blocking=True)
+        self._copied.record()
+
+    def step(self, tokens, q, k_new, v_new, softmax_scale, out=None, k_scale_new=None, v_scale_new=None):
+        """One decode step: append one token per sequence, store its K/V, attend.  Returns out [B][Hq][D]."""
+        slots = self.kv.alloc.append_batch(self.ids, tokens)
+        self.upload_step_metadata(slots)
+        self.kv.store(self.slots, k_new, v_new, k_scale_new, v_scale_new)
+        return self.attend(q, softmax_scale, out)
+
+    def attend(self, q, softmax_scale, out=None):
+        return paged_attn_decode(q, self.kv.k_cache, self.kv.v_cache, self.block_tables, self.context_lens,
+                                 self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
+                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale)
+
+
+def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None, v_scale_rows=None):
+    """Admit prompts and store the KV rows of their uncached tokens (as a prefill would).
+
+    k_rows[i], v_rows[i]: numpy [len_i][Hkv][D] per prompt (float32, bf16 bits as uint16, or int8);
+    scale rows [len_i][Hkv] float32 for int8 caches.  Returns the cached-prefix length per prompt.
+    """
+    ncached = [kv.alloc.add_seq(s, t) for s, t in zip(seq_ids, token_lists)]
+    total = sum(len(t) - c for t, c in zip(token_lists, ncached))
+    cu, lk, slots = kv.alloc.prefill_slots(seq_ids, total)
+    if total == 0:
+        return ncached
+    dev = kv.device
+    sel = [slice(c, None) for c in ncached]
+    def rows(arrs):
+        a = np.concatenate([r[s] for r, s in zip(arrs, sel)])
+        return bf16_tensor(a, dev) if kv.dtype == BF16 else _to_dev(a, dev)
+
+    ks = vs = None
+    if kv.dtype == I8:
+        ks = _to_dev(np.concatenate([r[s] for r, s in zip(k_scale_rows, sel)]), dev)
+        vs = _to_dev(np.concatenate([r[s] for r, s in zip(v_scale_rows, sel)]), dev)
+    kv.store(_to_dev(slots, dev), rows(k_rows), rows(v_rows), ks, vs)
+    return ncached
+
+
+def prefill_chunk(kv, seq_ids, q_new, k_new, v_new, softmax_scale, causal=True, out=None):
+    """One prefill chunk over already-admitted sequences: store the new tokens' K/V, then attend.
+
+    q_new [n_new][Hq][D], k_new/v_new [n_new][Hkv][D] (device bf16, in sequence order).
+    """
+    dev = kv.device
+    n_new = int(q_new.shape[0])
+    cu, lk, slots = kv.alloc.prefill_slots(seq_ids, n_new)
+    mb = max(1, -(-int(lk.max()) // BLOCK))
+    tab, _ = kv.alloc.block_tables(seq_ids, mb)
+    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel()]).astype(np.int32), dev)
+    B = len(seq_ids)
+    d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
+    d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
+    d_tab = meta[2 * B + 1 + n_new:].view(B, mb)
+    kv.store(d_slots, k_new, v_new)
+    n_q = np.diff(cu)
+    return paged_attn_prefill(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache, d_tab,
+                              softmax_scale, causal, out=out)

@@ -1,0 +1,127 @@
+"""Shared set-up for the GPU parity tests: one workload run through libpkv and through the oracle.
+
+The two sides meet only in the seeded inputs from ``workloads``: the GPU side runs the native
+block manager, the store kernel and the attention kernels; the oracle side runs its own block
+manager, its own store and its own attention.
+"""
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_kvcache_amd as P
+import workloads as W
+from oracle import allocator as OA
+from oracle import attention as OT
+from paged_kv_cache_kvcache_amd import runner as R
+
+DT = {"f32": P.F32, "bf16": P.BF16, "i8": P.I8}
+TOL = {"f32": (1e-5, None), "bf16": (2e-2, 2e-3), "i8": (5e-2, None)}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def dev_rows(a, device):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return R.bf16_tensor(a, device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host_out(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def kv_arrays(seq, dtype, sl=slice(None)):
+    """K rows, V rows and (int8) per-token scales of one sequence, as the cache stores them."""
+    if dtype == "i8":
+        return seq["kq"][sl], seq["vq"][sl], seq["k_tok_scale"][sl], seq["v_tok_scale"][sl]
+    return seq["k"][sl], seq["v"][sl], None, None
+
+
+def gpu_decode(wl, device, max_splits=0, fill=None, free_order=None):
+    """History admitted and stored, then one decode step (append + store + attend) on the GPU."""
+    cfg = wl["cfg"]
+    dtype = cfg["dtype"]
+    B, Hq, Hkv, D = len(wl["lens"]), cfg["Hq"], cfg["Hkv"], cfg["D"]
+    order = wl["free_order"] if free_order is None else free_order
+    kv = R.PagedKV(wl["num_blocks"], Hkv, D, DT[dtype], order, device=device, fill=fill)
+    ids = list(range(B))
+    parts = [kv_arrays(s, dtype, slice(0, -1)) for s in wl["seqs"]]
+    R.admit_and_store(kv, ids, [s["tokens"][:-1] for s in wl["seqs"]], [p[0] for p in parts],
+                      [p[1] for p in parts], [p[2] for p in parts], [p[3] for p in parts])
+    batch = R.DecodeBatch(kv, Hq, ids, max(wl["lens"]), max_splits)
+    last = [kv_arrays(s, dtype, slice(-1, None)) for s in wl["seqs"]]
+    k_new = dev_rows(np.concatenate([x[0] for x in last]), device)
+    v_new = dev_rows(np.concatenate([x[1] for x in last]), device)
+    ks = vs = None
+    if dtype == "i8":
+        ks = dev_rows(np.concatenate([x[2] for x in last]), device)
+        vs = dev_rows(np.concatenate([x[3] for x in last]), device)
+    q = dev_rows(np.stack([s["q"] for s in wl["seqs"]]), device)
+    tokens = [int(s["tokens"][-1]) for s in wl["seqs"]]
+    out = batch.step(tokens, q, k_new, v_new, 1.0 / math.sqrt(D), k_scale_new=ks, v_scale_new=vs)
+    torch.cuda.synchronize()
+    return out, kv, batch
+
+
+def oracle_decode(wl):
+    """The same step on the oracle: its allocator, its store, its attention (float64)."""
+    cfg = wl["cfg"]
+    dtype = cfg["dtype"]
+    B, Hkv, D = len(wl["lens"]), cfg["Hkv"], cfg["D"]
+    a = OA.Allocator(wl["num_blocks"], wl["free_order"])
+    ids = list(range(B))
+    for b, s in enumerate(wl["seqs"]):
+        a.add_seq(b, s["tokens"][:-1])
+    cu, lk, slots = a.prefill_slots(ids)
+    new_slots = [a.append(b, int(s["tokens"][-1])) for b, s in enumerate(wl["seqs"])]
+    shape = (wl["num_blocks"], Hkv, 256, D)
+    if dtype == "i8":
+        kc, vc = np.zeros(shape, np.int8), np.zeros(shape, np.int8)
+        ksc = np.zeros((wl["num_blocks"], Hkv), np.float32)
+        vsc = np.zeros_like(ksc)
+    else:
+        kc, vc = np.zeros(shape, np.float32), np.zeros(shape, np.float32)
+        ksc = vsc = None
+    rows = [kv_arrays(s, dtype) for s in wl["seqs"]]
+
+    def cat(i, sl):  # i: 0 K rows, 1 V rows, 2 K scales, 3 V scales
+        xs = [r[i][sl] for r in rows]
+        if i < 2 and dtype != "i8":
+            xs = [to_f64(x) for x in xs]
+        return np.concatenate(xs)
+
+    hist = slice(0, -1)
+    new = slice(-1, None)
+    if dtype == "i8":
+        kc, vc, ksc, vsc = OT.kv_store(kc, vc, cat(0, hist), cat(1, hist), slots, ksc, vsc, cat(2, hist), cat(3, hist))
+        kc, vc, ksc, vsc = OT.kv_store(kc, vc, cat(0, new), cat(1, new), new_slots, ksc, vsc, cat(2, new), cat(3, new))
+    else:
+        kc, vc = OT.kv_store(kc, vc, cat(0, hist), cat(1, hist), slots)
+        kc, vc = OT.kv_store(kc, vc, cat(0, new), cat(1, new), new_slots)
+    mb = max(1, -(-max(wl["lens"]) // 256))
+    tables = a.block_tables(ids, mb)
+    q = np.stack([to_f64(s["q"]) for s in wl["seqs"]])
+    return OT.decode(q, kc, vc, tables, wl["lens"], 1.0 / math.sqrt(D), ksc, vsc)
+
+
+def check_tol(got, ref, dtype, what=""):
+    max_abs, mean_abs = TOL[dtype]
+    err = np.abs(got - ref)
+    say(f"  {what}: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (bar {max_abs}, {mean_abs})")
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err.max() <= max_abs, f"{what}: max-abs {err.max():.3e} > {max_abs}"
+    if mean_abs is not None:
+        assert err.mean() <= mean_abs, f"{what}: mean-abs {err.mean():.3e} > {mean_abs}"

@@ -1,0 +1,115 @@
+"""The C ABI library (CPU only): it loads, exports what include/pkv.h declares, and rejects bad
+arguments on the host before anything is enqueued.  No test here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loaded first, so libpkv binds to torch's HIP runtime)
+
+import paged_kv_cache_kvcache_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    lib = P.lib()
+    declared = _header_functions()
+    assert len(declared) >= 17
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in pkv.h but not exported"
+    assert sorted(P.SIGNATURES) == declared, "binding signatures drift from pkv.h"
+    assert P.lib().pkv_version().decode().startswith("pkv")
+
+
+def test_library_has_gfx950_code_object():
+    data = open(P.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected on the host
+
+
+def _desc(**kw):
+    d = dict(num_blocks=8, num_kv_heads=2, head_dim=64, kv_dtype=P.F32)
+    d.update(kw)
+    return P.cache_desc(**d)
+
+
+def _store(desc, n=1, scales=(None, None, None, None), ptr=FAKE):
+    return P.lib().pkv_kv_store(ctypes.byref(desc), ptr, ptr, *scales[:2], ptr, n, ptr, ptr, *scales[2:], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), P.ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), P.ERR_UNSUPPORTED),
+    (dict(num_kv_heads=0), P.ERR_INVALID),
+    (dict(num_blocks=0), P.ERR_INVALID),
+])
+def test_kv_store_rejects_bad_descriptors(kw, code):
+    assert _store(_desc(**kw)) == code
+    assert P.last_error()
+
+
+def test_kv_store_rejects_block_size_other_than_256():
+    d = _desc()
+    d.block_size = 128
+    assert _store(d) == P.ERR_UNSUPPORTED
+
+
+def test_kv_store_scale_pointer_rules():
+    assert _store(_desc(kv_dtype=P.I8)) == P.ERR_INVALID  # int8 needs scales
+    assert _store(_desc(), scales=(FAKE, FAKE, FAKE, FAKE)) == P.ERR_INVALID  # f32 rejects them
+    assert _store(_desc(), n=-1) == P.ERR_INVALID
+    assert _store(_desc(), ptr=ctypes.c_void_p(8)) == P.ERR_INVALID  # misaligned
+    assert _store(_desc(), n=0) == P.OK  # empty store enqueues nothing
+
+
+def _decode(desc, B=2, Hq=4, max_blocks=3, max_ctx=600, splits=0, ks=None, vs=None, ws=None, ws_bytes=0,
+            scale=0.125):
+    return P.lib().pkv_paged_attn_decode(ctypes.byref(desc), FAKE, B, Hq, FAKE, FAKE, ks, vs, FAKE, max_blocks,
+                                         FAKE, max_ctx, splits, scale, FAKE, ws, ws_bytes, None)
+
+
+def test_decode_rejects_bad_arguments():
+    d = _desc()
+    assert _decode(d, Hq=3) == P.ERR_INVALID                       # Hq % Hkv
+    assert _decode(d, Hq=2 * 16) == P.ERR_UNSUPPORTED               # group 16
+    assert _decode(d, max_blocks=2, max_ctx=600) == P.ERR_INVALID   # table too narrow
+    assert _decode(d, scale=float("nan")) == P.ERR_INVALID
+    assert _decode(d, ks=FAKE, vs=FAKE) == P.ERR_INVALID            # scales on a float cache
+    assert _decode(_desc(kv_dtype=P.I8)) == P.ERR_INVALID           # int8 without scales
+    assert _decode(d, B=0) == P.OK
+
+
+def test_decode_needs_its_workspace():
+    d = _desc()
+    need = P.decode_workspace_bytes(2, 4, 64, 2, 600, 3)
+    assert need == 2 * 4 * 3 * (64 + 2) * 4
+    assert _decode(d, splits=3) == P.ERR_SMALL_BUFFER
+    assert _decode(d, splits=3, ws=FAKE, ws_bytes=need - 4) == P.ERR_SMALL_BUFFER
+
+
+def test_decode_plan():
+    assert P.decode_plan(4, 2, 600, 1) == (1, 3)
+    assert P.decode_plan(4, 2, 600, 2) == (2, 2)
+    assert P.decode_plan(4, 2, 600, 9) == (3, 1)       # at most one split per block
+    assert P.decode_plan(4, 2, 0, 0) == (1, 1)
+    s, bps = P.decode_plan(64, 8, 8192, 0)             # few workgroups: split the long contexts
+    assert s > 1 and s * bps >= 32 and (s - 1) * bps < 32
+    assert P.decode_plan(256, 8, 2048, 0)[0] == 1       # 2048 workgroups already
+    assert P.decode_workspace_bytes(256, 16, 128, 8, 2048, 0) == 0
+
+
+def test_prefill_rejects_bad_descriptor():
+    d = _desc(head_dim=80)
+    rc = P.lib().pkv_paged_attn_prefill(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE, 1,
+                                        0.1, 1, FAKE, None)
+    assert rc == P.ERR_UNSUPPORTED
