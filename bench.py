@@ -1,0 +1,235 @@
+"""Throughput of the paged-KV hot path on one MI355X, as one JSON line.
+
+Default workload: the Qwen3-0.6B-shaped decode step -- batch 256, contexts U[100, 2048], 16 query /
+8 KV heads, head_dim 128, bf16 KV, one layer.  One *step* is everything a decode iteration does on
+the path: the block manager appends one token per sequence (host C++), block tables, lengths and
+slots go to the device in one pinned copy, kv_store writes the new K/V rows, and the decode kernels
+attend over the whole paged context.  Contexts therefore grow by one token per step, as in a real
+decode loop.  All inputs are seeded synthetic data and are resident in HBM before timing starts.
+
+``--config prefill_prefix`` times the chunked varlen prefill workload instead (32 prompts with a
+shared 512-token prefix per group of 8, chunks of at most 4096 new tokens): one step is the
+whole workload -- every chunk's store and prefill attention.
+
+Reported beside the throughput:
+* ``roofline`` -- the dominant kernel's algorithmic traffic (decode: KV bytes of the valid tokens;
+  prefill: causal flops) divided by its average duration, timed with HIP events on the launch
+  stream, against MI355X's published peak (8 TB/s HBM3E; 2.5 PFLOP/s dense bf16);
+* ``cpu_baseline`` -- the fp64 oracle timed on the host on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--seed S]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6  # dense MFMA, 256 CUs at 2.4 GHz
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="qwen3_decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------ decode
+def bench_decode(args, cfg):
+    import torch
+    import workloads as W
+    from paged_kv_cache_kvcache_amd import BF16, F32, I8, decode_plan
+    from paged_kv_cache_kvcache_amd import runner as R
+
+    dev = torch.device("cuda:0")
+    dtype = cfg["dtype"]
+    kvdt = {"f32": F32, "bf16": BF16, "i8": I8}[dtype]
+    B, Hq, Hkv, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    nsteps = args.warmup + args.steps
+    t0 = time.time()
+    wl = W.decode_workload(cfg, args.seed)
+    lens = wl["lens"]
+    # the pool also holds the tokens the timed steps append
+    nb = max(wl["num_blocks"], W.pool_blocks(cfg, [L + nsteps for L in lens]))
+    order = W.free_order(cfg, args.seed, nb)
+    log(f"[bench] generated {cfg['name']} (B={B}, sum ctx={sum(lens)}) in {time.time() - t0:.1f}s")
+
+    kv = R.PagedKV(nb, Hkv, D, kvdt, order, device=dev)
+    ids = list(range(B))
+    if dtype == "i8":
+        parts = [(s["kq"], s["vq"], s["k_tok_scale"], s["v_tok_scale"]) for s in wl["seqs"]]
+    else:
+        parts = [(s["k"], s["v"], None, None) for s in wl["seqs"]]
+    # history = every token but the last; the workload's own new token is the first timed append
+    R.admit_and_store(kv, ids, [s["tokens"][:-1] for s in wl["seqs"]], [p[0][:-1] for p in parts],
+                      [p[1][:-1] for p in parts],
+                      [None if p[2] is None else p[2][:-1] for p in parts],
+                      [None if p[3] is None else p[3][:-1] for p in parts])
+    max_ctx = max(lens) + nsteps
+    batch = R.DecodeBatch(kv, Hq, ids, max_ctx, args.max_splits)
+    splits, bps = decode_plan(B, Hkv, max_ctx, args.max_splits)
+
+    # per-step inputs, resident on the device before timing
+    steps = []
+    blk_scale = {}
+    cur = list(lens)
+    for s in range(nsteps):
+        if s == 0:
+            tokens = np.array([x["tokens"][-1] for x in wl["seqs"]], dtype=np.int32)
+            q = np.stack([x["q"] for x in wl["seqs"]])
+            k = np.stack([p[0][-1] for p in parts])
+            v = np.stack([p[1][-1] for p in parts])
+            ks = vs = None
+            if dtype == "i8":
+                ks = np.stack([p[2][-1] for p in parts])
+                vs = np.stack([p[3][-1] for p in parts])
+                for b, x in enumerate(wl["seqs"]):
+                    blk_scale[b] = (x["k_blk_scale"][-1].copy(), x["v_blk_scale"][-1].copy())
+        else:
+            inp = W.decode_step_inputs(cfg, args.seed, s, B)
+            tokens, q, k, v = inp["tokens"], inp["q"], inp["k"], inp["v"]
+            ks = vs = None
+            if dtype == "i8":
+                bk = np.stack([np.full(Hkv, np.nan, np.float32) if (cur[b] - 1) % 256 == 0 else blk_scale[b][0]
+                               for b in range(B)])
+                bv = np.stack([np.full(Hkv, np.nan, np.float32) if (cur[b] - 1) % 256 == 0 else blk_scale[b][1]
+                               for b in range(B)])
+                k, ks = W.int8_encode_token(W.bf16_bits_to_f32(k), bk)
+                v, vs = W.int8_encode_token(W.bf16_bits_to_f32(v), bv)
+                for b in range(B):
+                    blk_scale[b] = (ks[b].copy(), vs[b].copy())
+        dv = lambda a: None if a is None else (R.bf16_tensor(a, dev) if a.dtype == np.uint16 else
+                                               torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+        steps.append(dict(tokens=tokens, q=dv(q), k=dv(k), v=dv(v), ks=dv(ks), vs=dv(vs), ctx=list(cur)))
+        cur = [c + 1 for c in cur]
+    out = torch.empty((B, Hq, D), dtype=torch.float32 if dtype == "f32" else torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    esize = {"f32": 4, "bf16": 2, "i8": 1}[dtype]
+
+    def kv_bytes(ctx):
+        b = sum(ctx) * Hkv * D * esize * 2
+        if dtype == "i8":
+            b += sum(-(-c // 256) for c in ctx) * Hkv * 2 * 4
+        return b
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def run(i, timed_idx=None):
+        st = steps[i]
+        slots = kv.alloc.append_batch(batch.ids, st["tokens"])
+        batch.upload_step_metadata(slots)
+        kv.store(batch.slots, st["k"], st["v"], st["ks"], st["vs"])
+        if timed_idx is not None:
+            ev[timed_idx][0].record(stream)
+        batch.attend(st["q"], scale, out)
+        if timed_idx is not None:
+            ev[timed_idx][1].record(stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        run(args.warmup + j, j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    bytes_per_launch = sum(kv_bytes(steps[args.warmup + j]["ctx"]) for j in range(args.steps)) / args.steps
+    achieved = bytes_per_launch / avg_kern_s / 1e9
+    log(f"[bench] splits={splits} blocks/split={bps}; decode kernel avg {avg_kern_s * 1e6:.1f} us, "
+        f"{achieved:.0f} GB/s; step {elapsed / args.steps * 1e3:.3f} ms")
+
+    res = dict(
+        metric="paged decode tokens/s + KV HBM GB/s (% of peak); prefill TFLOP/s",
+        value=B * args.steps / elapsed, unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=elapsed / args.steps * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype=dtype, data="synthetic",
+        config=dict(workload=cfg["name"], batch=B, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]" if isinstance(
+            cfg["ctx"], tuple) else str(cfg["ctx"]), q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256,
+            splits=splits, blocks_per_split=bps, seed=args.seed),
+        decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
+        kv_gbs=achieved,
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                      traffic=None, kernel="decode (split kernel + LSE reduce when splits > 1)",
+                      bytes_per_launch=bytes_per_launch),
+    )
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_sample or 8)
+    return res
+
+
+def _timed_sample(run, total, first=8, budget_s=10.0):
+    """Time ``run(n)`` on growing prefixes of the workload until one run takes ``budget_s`` or covers it all."""
+    n = min(first, total)
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= total:
+            return n, dt
+        n = min(total, max(2 * n, int(n * 1.2 * budget_s / max(dt, 1e-3))))
+
+
+def cpu_baseline_decode(wl, first=8):
+    """The oracle's whole decode step (its block manager, store and attention) on the first n sequences."""
+    from threadpoolctl import threadpool_limits
+    import workloads as W
+    from oracle.steps import decode_step
+
+    def run(n):
+        sub = dict(wl)
+        sub["lens"] = wl["lens"][:n]
+        sub["seqs"] = wl["seqs"][:n]
+        sub["num_blocks"] = W.pool_blocks(wl["cfg"], sub["lens"])
+        sub["free_order"] = W.free_order(wl["cfg"], wl["seed"], sub["num_blocks"])
+        decode_step(sub)
+
+    with threadpool_limits(1):
+        n, dt = _timed_sample(run, len(wl["lens"]), first)
+    return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {n} of {len(wl['lens'])} sequences ({sum(wl['lens'][:n])} context tokens), one decode "
+                       f"step: oracle block manager + store + fp64 attention, {dt:.1f}s on one thread")
+
+
+# ------------------------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = W.config(args.config)
+    if cfg["kind"] == "decode":
+        res = bench_decode(args, cfg)
+    else:
+        from bench_prefill import bench_prefill  # noqa
+        res = bench_prefill(args, cfg)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,7 +53,7 @@ CONFIGS = {
                         dtype="i8", value_scale=1.0, pool=None),
 }
 
-_P_LEN, _P_SEQ, _P_GROUP, _P_POOL = 0, 1, 2, 3
+_P_LEN, _P_SEQ, _P_GROUP, _P_POOL, _P_STEP = 0, 1, 2, 3, 4
 
 
 def _rng(seed, cfg, purpose, index=0):
@@ -166,6 +166,32 @@ def decode_workload(cfg, seed, threads=16):
     with ThreadPoolExecutor(max_workers=threads) as ex:
         seqs = list(ex.map(lambda a: decode_sequence(cfg, seed, a[0], a[1]), enumerate(lens)))
     return dict(cfg=cfg, seed=seed, lens=lens, num_blocks=nb, free_order=free_order(cfg, seed, nb), seqs=seqs)
+
+
+def decode_step_inputs(cfg, seed, step, B):
+    """New-token inputs of decode step ``step`` (after the workload's own step) for all B sequences.
+
+    Returns tokens ``[B]``, q ``[B][Hq][D]``, k, v ``[B][Hkv][D]`` drawn like the workload's values.
+    (int8 workloads: k, v are the bf16 source; see :func:`int8_encode_token`.)
+    """
+    rng = _rng(seed, cfg, _P_STEP, step)
+    Hq, Hkv, D, dt, vs = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["dtype"], cfg["value_scale"]
+    return dict(tokens=rng.integers(0, VOCAB, size=B, dtype=np.int32), q=_normal(rng, (B, Hq, D), vs, dt),
+                k=_normal(rng, (B, Hkv, D), vs, dt), v=_normal(rng, (B, Hkv, D), vs, dt))
+
+
+def int8_encode_token(x_f32, block_scale):
+    """int8 codes of decode tokens ``[B][Hkv][D]``: a token that opens a new block (block_scale row
+    is NaN) sets the block's scale from its own absmax; otherwise it reuses the block's scale and
+    its codes are clamped to +-127.  Returns (codes, scale ``[B][Hkv]``)."""
+    x = x_f32.astype(np.float64)
+    own = (np.abs(x).max(axis=2) / 127.0).astype(np.float32)
+    s = np.where(np.isnan(block_scale), own, block_scale).astype(np.float32)
+    s64 = s.astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    c = np.clip(np.rint(x / safe[:, :, None]), -127, 127)
+    c[s64 == 0] = 0
+    return c.astype(np.int8), s
 
 
 # -- prefill workload -------------------------------------------------------------
