@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain 1 GiB device copy (to scale hardware byte counters) and exit")
     return ap.parse_args()
 
 
@@ -209,6 +211,112 @@ def cpu_baseline_decode(wl, first=8):
                        f"step: oracle block manager + store + fp64 attention, {dt:.1f}s on one thread")
 
 
+# ------------------------------------------------------------------------------------ prefill
+def bench_prefill(args, cfg):
+    import torch
+    import workloads as W
+    from paged_kv_cache_kvcache_amd import BF16, kv_store, paged_attn_prefill
+    from paged_kv_cache_kvcache_amd import runner as R
+
+    dev = torch.device("cuda:0")
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    wl = W.prefill_workload(cfg, args.seed)
+    prompts = wl["prompts"]
+    kv = R.PagedKV(wl["num_blocks"], Hkv, D, BF16, wl["free_order"], device=dev)
+    t0 = time.perf_counter()
+    ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+    n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
+    chunks = W.pack_chunks(n_new, cfg["chunk"])
+    metas = []
+    for ch in chunks:
+        cu, lk, slots = kv.alloc.prefill_slots(ch, sum(n_new[i] for i in ch))
+        mb = max(1, -(-int(lk.max()) // 256))
+        tab, _ = kv.alloc.block_tables(ch, mb)
+        metas.append((cu, lk, slots, tab, mb))
+    host_s = time.perf_counter() - t0
+    # device-resident inputs of every chunk
+    dchunks, flops = [], 0
+    for ch, (cu, lk, slots, tab, mb) in zip(chunks, metas):
+        dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), dev)
+        q, k, v = dv("q"), dv("k"), dv("v")
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        dchunks.append(dict(q=q, k=k, v=v, cu=to(cu), lk=to(lk), slots=to(slots), tab=to(tab).view(len(ch), mb),
+                            max_q=int(np.diff(cu).max()), max_k=int(lk.max()), out=torch.empty_like(q)))
+        for b in range(len(ch)):
+            nq, L = int(cu[b + 1] - cu[b]), int(lk[b])
+            flops += 4 * D * Hq * sum(L - nq + i + 1 for i in range(nq))
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    nch = len(dchunks)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nch)]
+          for _ in range(args.steps)]
+
+    def run(timed=None):
+        for c, d in enumerate(dchunks):
+            kv_store(d["k"], d["v"], d["slots"], kv.k_cache, kv.v_cache)
+            if timed is not None:
+                ev[timed][c][0].record(stream)
+            paged_attn_prefill(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache, d["tab"],
+                               scale, True, out=d["out"])
+            if timed is not None:
+                ev[timed][c][1].record(stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        run(j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = sum(a.elapsed_time(b) for row in ev for a, b in row) / args.steps / 1e3
+    tflops = flops / kern_s / 1e12
+    total_new = sum(n_new)
+    log(f"[bench] prefill {nch} chunks, {total_new} new tokens, {flops / 1e9:.2f} GFLOP; prefill kernels "
+        f"{kern_s * 1e6:.1f} us/step -> {tflops:.1f} TFLOP/s; step {elapsed / args.steps * 1e3:.3f} ms")
+    res = dict(
+        metric="paged decode tokens/s + KV HBM GB/s (% of peak); prefill TFLOP/s",
+        value=total_new * args.steps / elapsed, unit="prefill tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=elapsed / args.steps * 1e3, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=cfg["name"], prompts=cfg["B"], prompt_len=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]",
+                    shared_prefix=cfg["shared"], group=cfg["group"], chunk_tokens=cfg["chunk"], q_heads=Hq,
+                    kv_heads=Hkv, head_dim=D, block_size=256, chunks=nch, new_tokens=total_new,
+                    cached_tokens=sum(ncached), seed=args.seed),
+        prefill_kernel_us=kern_s * 1e6, prefill_tflops=tflops, host_admit_us=host_s * 1e6,
+        roofline=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=tflops / BF16_PEAK_TFLOPS, traffic=None, kernel="prefill (all chunks of one step)",
+                      flops_per_step=flops),
+    )
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_sample or 4)
+    return res
+
+
+def cpu_baseline_prefill(wl, first=4):
+    """The oracle's chunked prefill (its block manager, store, fp64 attention) on the first n prompts."""
+    from threadpoolctl import threadpool_limits
+    import workloads as W
+    from oracle.steps import prefill_run
+    cfg = wl["cfg"]
+
+    def run(n):
+        sub = dict(wl)
+        sub["lens"] = wl["lens"][:n]
+        sub["prompts"] = wl["prompts"][:n]
+        sub["num_blocks"] = W.pool_blocks(cfg, sub["lens"])
+        sub["free_order"] = W.free_order(cfg, wl["seed"], sub["num_blocks"])
+        run.out = prefill_run(sub)
+
+    with threadpool_limits(1):
+        n, dt = _timed_sample(run, len(wl["lens"]), first)
+    _, ncached, _ = run.out
+    new = sum(L - c for L, c in zip(wl["lens"][:n], ncached))
+    return dict(value=new / dt, unit="prefill tokens/s", cores=1, kind="oracle",
+                sample=f"first {n} of {len(wl['lens'])} prompts ({new} new tokens): oracle block manager + store + "
+                       f"fp64 causal attention, {dt:.1f}s on one thread")
+
+
 # ------------------------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -222,11 +330,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calib:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n, "launches": 5}), flush=True)
+        return
     cfg = W.config(args.config)
     if cfg["kind"] == "decode":
         res = bench_decode(args, cfg)
     else:
-        from bench_prefill import bench_prefill  # noqa
         res = bench_prefill(args, cfg)
     print(json.dumps(res), flush=True)
 

@@ -205,7 +205,8 @@ int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, 
  * of sequence b sits at position seqlens_k[b] - n_q(b) + i and attends keys 0..that
  * position (bottom-right alignment); otherwise it attends all seqlens_k[b] keys.
  * The new tokens' K/V must already be stored (pkv_kv_store earlier on the stream).
- * max_seqlen_q, max_seqlen_k: host upper bounds.  out: device bf16 [total_q][Hq][head_dim].
+ * max_seqlen_q, max_seqlen_k: host upper bounds.  softmax_scale must be positive.
+ * out: device bf16 [total_q][Hq][head_dim].
  * ------------------------------------------------------------------------------------------ */
 int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q, int32_t Hq,
                            const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,

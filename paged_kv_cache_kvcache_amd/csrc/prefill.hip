@@ -7,18 +7,22 @@
 // article, §2.1).  The kernel below is this library's own design for CDNA4.
 //
 // Work decomposition
-//   One workgroup (4 wavefronts) per (sequence, query tile, KV head).  The G = Hq/Hkv query heads
-//   that read one KV head are stacked into 128 MFMA rows: a query tile holds QT = 128/G new tokens
-//   of all G heads, so every K/V tile staged in LDS serves all of them.  Wavefront w owns rows
-//   32w..32w+31 (row rho -> head rho / QT, token rho % QT).  Tiles are visited last-first within a
-//   sequence so the longest causal rows start first.
+//   One workgroup per (sequence, query tile, KV head).  The G = Hq/Hkv query heads that read one
+//   KV head are stacked into 128 MFMA rows: a query tile holds QT = 128/G new tokens of all G
+//   heads, so every K/V tile staged in LDS serves all of them.  A group of four wavefronts walks
+//   the key tiles; wavefront w owns rows 32w..32w+31 (row rho -> head rho / QT, token rho % QT).
+//   Optionally (template NS = 2) a second group splits the key range (tiles s, s+2, ...) with its
+//   own LDS stages and the partial softmax states are merged through LDS; on MI355X two
+//   independent one-group workgroups per CU measured faster, so NS = 1 is dispatched.  Work items
+//   are ordered so that the tiles with the longest causal rows (each sequence's last) start first.
 //
 // Per 64-key tile (double-buffered in LDS, next tile's global loads in flight during compute):
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T kept in registers.
 //                   The accumulator layout puts one query per lane column, 16 keys per lane, and
 //                   the other 16 keys of that query in lane ^ 32: the softmax max/sum of a query
 //                   needs a single cross-lane swap.
-//   online softmax  log2 domain, causal mask by absolute position (bottom-right aligned).
+//   online softmax  log2 domain, one FMA folds the scale into the exponent, causal mask by
+//                   absolute position (bottom-right aligned) on diagonal tiles only, lazy rescale.
 //   O^T += V^T P^T  A = V^T from LDS, B = P^T converted to bf16 straight from the S accumulators.
 //                   V is stored transposed in LDS with the keys of each 16-key group permuted
 //                   (bits 2 and 3 of the key index swapped) so that the 8 keys a lane needs for the
@@ -27,6 +31,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -35,11 +40,12 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
+constexpr int kGroupThreads = 256;         // 4 wavefronts, 32 query rows each
 constexpr int kRows = 128;  // MFMA query rows per workgroup (tokens x heads)
 constexpr int kKT = 64;     // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
+constexpr f32x16_t kZero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
 struct PrefillArgs {
     const uint16_t* q;
@@ -68,33 +74,57 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Position of key i (0..63) of a tile in the transposed V rows: bits 2 and 3 swapped.
 __device__ __forceinline__ int vpos(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+// Byte offset of position `pos` (8-byte aligned) in transposed V row d.  Rows are 128 bytes; the
+// 16-byte chunk index is xor-ed with (d ^ d/8) & 7 so that both the transposing writes (16 lanes
+// on rows 8 apart) and the MFMA operand reads (lanes on 32 consecutive rows, one chunk) spread over
+// all banks.
+__device__ __forceinline__ int vt_off(int d, int pos) {
+    const int sw = (d ^ (d >> 3)) & 7;
+    return d * 128 + ((((pos >> 3) ^ sw) << 4) | ((pos & 4) << 1));
+}
+
+// NS = number of wavefront groups that split the key range inside a workgroup (1 or 2).
+template <int D, int G, int NS>
+__global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(PrefillArgs a) {
+    constexpr int kGroups = NS;
     constexpr int QT = kRows / G;       // new tokens per workgroup
     constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;          // 32-row tiles of O^T
     constexpr int KP = D * 2 + 16;      // LDS pitch of a K row (bytes)
-    constexpr int VP = kKT * 2 + 16;    // LDS pitch of a transposed V row (bytes)
+    constexpr int VP = kKT * 2;         // LDS pitch of a transposed V row (bytes), chunks swizzled
     constexpr int KBYTES = kKT * KP;
     constexpr int BUF = KBYTES + D * VP;
     constexpr int CPR = D / 8;          // 16-byte pieces per K/V row
-    constexpr int KLOADS = kKT * CPR / kThreads;  // K pieces per thread
-    __shared__ __attribute__((aligned(16))) char lds[2][BUF];
+    constexpr int KLOADS = kKT * CPR / kGroupThreads;  // K pieces per thread
+    constexpr int XCH = kGroupThreads * (16 * DT + 2) * 4;  // bytes of one group's merge state
+    static_assert(NS == 1 || NS == 2, "one or two key-range groups");
+    static_assert(XCH <= 2 * BUF, "merge state must fit in a group's stages");
+    __shared__ __attribute__((aligned(16))) char lds[kGroups][2][BUF];
 
-    // ---- which (sequence, query tile) this workgroup owns
-    const int g = blockIdx.y;
-    const int x = blockIdx.x;
-    int b = -1, tile = 0, nq = 0, start = 0;
-    for (int s = 0; s < a.B; ++s) {
-        const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
-        const int T = (n + QT - 1) / QT;
-        if (x < start + T) {
-            b = s;
-            tile = T - 1 - (x - start);
-            nq = n;
-            break;
+    // ---- which (sequence, query tile, KV head) this workgroup owns.  Work items are ordered by
+    // distance from the end of their sequence (every sequence's last tile first, then every
+    // second-to-last tile, ...), so the tiles with the longest causal rows start first; the KV
+    // head varies fastest.
+    const int g = blockIdx.x % a.num_kv_heads;
+    int item = blockIdx.x / a.num_kv_heads;
+    int b = -1, tile = 0, nq = 0;
+    for (int r = 0; b < 0; ++r) {
+        int live = 0;
+        for (int s = 0; s < a.B; ++s) {
+            const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
+            const int T = (n + QT - 1) / QT;
+            if (T > r) {
+                if (item == 0) {
+                    b = s;
+                    tile = T - 1 - r;
+                    nq = n;
+                    break;
+                }
+                --item;
+                ++live;
+            }
         }
-        start += T;
+        if (b < 0 && live == 0) break;  // past the last work item
     }
     if (b < 0) return;
 
@@ -106,18 +136,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int kv_len = a.causal ? min(Lk, pos0 + nqt) : Lk;
     const int ntiles = (kv_len + kKT - 1) / kKT;
 
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x & (kGroupThreads - 1);  // thread within its group
+    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / kGroupThreads);
+    const int w = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
     const int lane = tid & 63, col = lane & 31, h = lane >> 5;
     const int rho = 32 * w + col;
     const int j = rho / QT, t = rho % QT;
     const bool col_ok = t < nqt;
     const int P = a.causal ? min(pos0 + t, kv_len - 1) : kv_len - 1;  // last key this column sees
-    // last key any column of this wavefront sees (for skipping fully masked tiles)
-    int pw = P;
+    // last key any column of this wavefront sees (tiles past it are skipped) and the last key every
+    // column sees (tiles up to it need no mask)
+    int pw = P, pm = P;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) pw = max(pw, __shfl_xor(pw, o, 64));
+    for (int o = 32; o >= 1; o >>= 1) {
+        pw = max(pw, __shfl_xor(pw, o, 64));
+        pm = min(pm, __shfl_xor(pm, o, 64));
+    }
     const int pw_max = __builtin_amdgcn_readfirstlane(pw);
+    const int pw_min = __builtin_amdgcn_readfirstlane(pm);
 
     // ---- Q^T operand: column col = query row, 8 consecutive d per k-step
     bf16x8_t qb[KS];
@@ -146,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const uint4* vg = reinterpret_cast<const uint4*>(a.v_cache + row0 * D * 2);
 #pragma unroll
         for (int r = 0; r < KLOADS; ++r) {
-            const int p = tid + kThreads * r;
+            const int p = tid + kGroupThreads * r;
             const int row = p / CPR;
             kreg[r] = (key0 + row < kv_len) ? kg[p] : make_uint4(0, 0, 0, 0);
         }
@@ -160,11 +196,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     };
     // ---- register -> LDS (K row-major, V transposed with permuted keys)
     auto lstore = [&](int buf) {
-        char* Ks = lds[buf];
-        char* Vt = lds[buf] + KBYTES;
+        char* Ks = lds[grp][buf];
+        char* Vt = lds[grp][buf] + KBYTES;
 #pragma unroll
         for (int r = 0; r < KLOADS; ++r) {
-            const int p = tid + kThreads * r;
+            const int p = tid + kGroupThreads * r;
             *reinterpret_cast<uint4*>(Ks + (p / CPR) * KP + (p % CPR) * 16) = kreg[r];
         }
         if (v_thread) {
@@ -181,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                     uint2 pr;
                     pr.x = __builtin_amdgcn_perm(w1[m], w0[m], sel);
                     pr.y = __builtin_amdgcn_perm(w3[m], w2[m], sel);
-                    *reinterpret_cast<uint2*>(Vt + (8 * vc + 2 * m + s) * VP + pos * 2) = pr;
+                    *reinterpret_cast<uint2*>(Vt + vt_off(8 * vc + 2 * m + s, pos)) = pr;
                 }
             }
         }
@@ -194,58 +230,76 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    if (ntiles > 0) gload(0);
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        lstore(buf);
+    // group grp walks tiles grp, grp + kGroups, ...; one workgroup barrier per step
+    const int steps = (ntiles + kGroups - 1) / kGroups;
+    if (grp < ntiles) gload(grp);
+    // One step: stage this group's tile, launch the next tile's loads, barrier, compute.  The step is
+    // instantiated for each LDS stage so that every LDS address offset is an immediate.
+    auto step = [&](int st, auto stage) {
+        constexpr int buf = decltype(stage)::value;
+        const int kt = st * kGroups + grp;
+        if (kt < ntiles) lstore(buf);
+        // the next tile's loads go out before the barrier, so the barrier wait also hides them
+        if (kt + kGroups < ntiles) gload(kt + kGroups);
         __syncthreads();
-        if (kt + 1 < ntiles) gload(kt + 1);
-        if (kt * kKT > pw_max) continue;  // every key of this tile is masked for this wavefront
+        if (kt >= ntiles || kt * kKT > pw_max) return;  // no tile, or every key masked for this wavefront
 
-        const char* Ks = lds[buf];
-        const char* Vt = lds[buf] + KBYTES;
+        const char* Ks = lds[grp][buf];
+        const char* Vt = lds[grp][buf] + KBYTES;
         // S^T = K Q^T for keys 32mt..32mt+31
+        // two independent accumulator chains (keys 0-31 and 32-63), interleaved k-step by k-step
         f32x16_t s[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8_t ka[2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[mt][i] = 0.f;
+            for (int mt = 0; mt < 2; ++mt)
+                ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + (32 * mt + col) * KP + (16 * ks + 8 * h) * 2);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t ka =
-                    *reinterpret_cast<const bf16x8_t*>(Ks + (32 * mt + col) * KP + (16 * ks + 8 * h) * 2);
-                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s[mt], 0, 0, 0);
-            }
+            for (int mt = 0; mt < 2; ++mt)  // the first k-step starts from an inline zero accumulator
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mt], qb[ks], ks == 0 ? kZero16 : s[mt], 0, 0, 0);
         }
-        // scale, mask, tile max
+        // mask (diagonal tiles only) and tile max, in raw score units (the scale is positive)
         float tmax = kNegInf;
+        if (kt * kKT + kKT - 1 > pw_min) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = kt * kKT + 32 * mt + 8 * (i / 4) + 4 * h + (i % 4);
-                const float v = key <= P ? s[mt][i] * a.scale_log2 : kNegInf;
-                s[mt][i] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m_run, tmax);  // finite: key 0 is visible to every column
-        const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-        m_run = mn;
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kt * kKT + 32 * mt + 8 * (i / 4) + 4 * h + (i % 4);
+                    s[mt][i] = key <= P ? s[mt][i] : kNegInf;
+                    tmax = fmaxf(tmax, s[mt][i]);
+                }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mt][i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
+        // Lazy rescaling: the reference max only moves when some column's max grew by more than
+        // 2^8, so most tiles skip rescaling O; probabilities then stay below 2^8, well inside bf16.
+        if (__any(tmax > m_run + 8.f)) {
+            const float mn = fmaxf(m_run, tmax);  // finite: key 0 is visible to every column
+            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+            m_run = mn;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        }
+        const float neg_m = -m_run;
         float psum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(s[mt][i] - mn);
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][i], a.scale_log2, neg_m));
                 s[mt][i] = p;
                 psum += p;
             }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        l_run += psum;
         // O^T += V^T P^T
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -260,11 +314,43 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-                        Vt + (32 * dt + col) * VP + (32 * mt + 16 * kk + 8 * h) * 2);
+                        Vt + vt_off(32 * dt + col, 32 * mt + 16 * kk + 8 * h));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
                 }
             }
         }
+    
+    };
+    for (int st = 0; st < steps; st += 2) {
+        step(st, std::integral_constant<int, 0>{});
+        if (st + 1 < steps) step(st + 1, std::integral_constant<int, 1>{});
+    }
+
+    // ---- merge the second group's state into the first through LDS (stages are free now)
+    if constexpr (NS == 2) {
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(lds[0][0]) + w * (16 * DT + 2) * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xch[(16 * dt + i) * 64] = o[dt][i];
+        xch[(16 * DT) * 64] = m_run;
+        xch[(16 * DT + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    {
+        const float m1 = xch[(16 * DT) * 64], l1 = xch[(16 * DT + 1) * 64];
+        const float mx = fmaxf(m_run, m1);  // group 0 always saw tile 0, so mx is finite
+        const float f0 = __builtin_amdgcn_exp2f(m_run - mx);
+        const float f1 = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+        l_run = l_run * f0 + l1 * f1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] = o[dt][i] * f0 + xch[(16 * dt + i) * 64] * f1;
+    }
     }
 
     // ---- normalise and write this column's row: d = 32dt + 8(i/4) + 4h + i%4
@@ -283,11 +369,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
 }
 
+// One group of four wavefronts per workgroup, two workgroups per CU: measured faster on MI355X than
+// two key-range groups in one workgroup per CU (kept for experiments: prefill_kernel<D, G, 2>).
+constexpr int kPrefillGroups = 1;
+
 template <int D, int G>
 hipError_t launch(const PrefillArgs& a, int total_q, hipStream_t st) {
     constexpr int QT = kRows / G;
-    const long tiles = (long(total_q) + QT - 1) / QT + a.B;
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(unsigned(tiles), a.num_kv_heads), dim3(kThreads), 0, st, a);
+    const long items = ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
+    if (items > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_kernel<D, G, kPrefillGroups>), dim3(unsigned(items)),
+                       dim3(kPrefillGroups * kGroupThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -326,7 +418,8 @@ extern "C" int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q,
     PKV_REQUIRE(max_seqlen_q <= max_seqlen_k || !causal, PKV_ERR_INVALID,
                 "causal prefill needs max_seqlen_q (%d) <= max_seqlen_k (%d)", max_seqlen_q, max_seqlen_k);
     PKV_REQUIRE(Hkv <= 65535, PKV_ERR_UNSUPPORTED, "Hkv must be at most 65535");
-    PKV_REQUIRE(std::isfinite(softmax_scale), PKV_ERR_INVALID, "softmax_scale is not finite");
+    PKV_REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, PKV_ERR_INVALID,
+                "softmax_scale must be finite and positive");
     if (B == 0 || total_q == 0) return PKV_OK;
     PKV_REQUIRE(q && cu_seqlens_q && seqlens_k && k_cache && v_cache && block_tables && out, PKV_ERR_INVALID,
                 "NULL pointer");
