@@ -45,12 +45,83 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (to scale hardware byte counters) and exit")
+    ap.add_argument("--summarize", metavar="NAME",
+                    help="write profiles/NAME.txt from rocprofv3 CSV output (see --prof-dir) and exit")
+    ap.add_argument("--prof-dir", default="gpurun_out/prof")
+    ap.add_argument("--prof-cmd", default="", help="the command lines that produced the CSVs (recorded)")
     return ap.parse_args()
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
+
+
+# ------------------------------------------------------------------------------------ profiles
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {"decode_split_kernel": "decode.hip", "prefill_kernel": "prefill.hip", "kv_store_kernel": "kv_store.hip"}
+
+
+def source_hash(kernel):
+    """Short hash of the HIP source a kernel is built from (ties a stored counter reading to a kernel version)."""
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", KERNEL_SOURCES[kernel])
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def summarize(name, prof_dir, cmd):
+    """Summarise rocprofv3 CSVs: kernel stats, and FETCH_SIZE / WRITE_SIZE per dispatch scaled by the
+    same counters' reading for a plain copy of known size."""
+    import csv
+    import glob
+    out = [f"# {name}", f"# produced by: {cmd}", ""]
+    for f in sorted(glob.glob(os.path.join(prof_dir, "*kernel_stats.csv"))):
+        out.append(f"## kernel stats ({os.path.basename(f)})")
+        out.append("kernel | calls | avg us | min us | max us | share %")
+        for r in csv.DictReader(open(f)):
+            out.append(f"{r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}")
+        out.append("")
+    counters = {}
+    for f in sorted(glob.glob(os.path.join(prof_dir, "*counter_collection.csv"))):
+        for r in csv.DictReader(open(f)):
+            key = (os.path.basename(f).split("_")[0], r["Kernel_Name"], r["Counter_Name"])
+            counters.setdefault(key, []).append(float(r["Counter_Value"]))
+    if counters:
+        out.append("## hardware counters (per dispatch, KiB for *_SIZE)")
+        scale = {}
+        for (run, kern, ctr), v in sorted(counters.items()):
+            avg = sum(v) / len(v)
+            out.append(f"{run} | {kern[:80]} | {ctr} | n={len(v)} | avg={avg:.6g} | min={min(v):.6g} | max={max(v):.6g}")
+            if run == "copy" and "copyBuffer" in kern:
+                scale[ctr] = (1 << 30) / (avg * 1024)
+        out.append("")
+        if scale:
+            out.append("copy calibration (bytes of a 1 GiB copy / counter bytes): " +
+                       ", ".join(f"{k} x{v:.4f}" for k, v in sorted(scale.items())))
+        for kern in ("decode_split_kernel", "prefill_kernel"):  # the dominant kernels
+            f = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "FETCH_SIZE"]
+            w = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "WRITE_SIZE"]
+            if f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+                fb = f[0] * 1024 * scale["FETCH_SIZE"]
+                wb = w[0] * 1024 * scale["WRITE_SIZE"]
+                out.append(f"TRAFFIC {kern} source={source_hash(kern)} fetch_bytes={fb:.6g} write_bytes={wb:.6g} "
+                           f"total_bytes={fb + wb:.6g}")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    print(path)
+
+
+def stored_traffic(kernel):
+    """HBM bytes per dispatch from a committed counter summary, if taken on the current kernel source."""
+    import glob
+    h = source_hash(kernel)
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        for line in open(f):
+            if line.startswith(f"TRAFFIC {kernel} source={h} "):
+                return float(line.split("total_bytes=")[1].split()[0])
+    return None
 
 # ------------------------------------------------------------------------------------ decode
 def bench_decode(args, cfg):
@@ -170,7 +241,9 @@ def bench_decode(args, cfg):
         decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
         kv_gbs=achieved,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                      traffic=None, kernel="decode (split kernel + LSE reduce when splits > 1)",
+                      traffic=stored_traffic("decode_split_kernel") if cfg["name"] == "qwen3_decode" and splits == 1
+                      and args.seed == 0 else None,
+                      kernel="decode (split kernel + LSE reduce when splits > 1)",
                       bytes_per_launch=bytes_per_launch),
     )
     if not args.no_cpu_baseline:
@@ -320,6 +393,9 @@ def cpu_baseline_prefill(wl, first=4):
 # ------------------------------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.prof_dir, args.prof_cmd)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

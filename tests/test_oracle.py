@@ -247,15 +247,25 @@ def _sdpa(q, k, v, scale, mask=None):
         attn_mask=None if mask is None else torch.from_numpy(mask)[None], scale=scale)[0].numpy()
 
 
+def _golden_hand():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "hand_attention.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, *xs = line.split()
+            vals[name] = [math.sqrt(2.0) * math.log(3.0) if x == "sqrt2ln3" else float(x) for x in xs]
+    return vals
+
+
 def test_hand_worked_example():
-    r2 = math.sqrt(2.0)
+    g = _golden_hand()
     kc = np.zeros((1, 1, 256, 2))
     vc = np.zeros((1, 1, 256, 2))
-    kc[0, 0, 1] = [r2 * math.log(3.0), 0.0]
-    vc[0, 0, 0] = [4.0, 0.0]
-    vc[0, 0, 1] = [0.0, 4.0]
-    out = OT.decode(np.array([[[1.0, 0.0]]]), kc, vc, [[0]], [2], 1.0 / r2)
-    assert np.allclose(out[0, 0], [1.0, 3.0], atol=1e-14)
+    kc[0, 0, 0], kc[0, 0, 1] = g["k0"], g["k1"]
+    vc[0, 0, 0], vc[0, 0, 1] = g["v0"], g["v1"]
+    out = OT.decode(np.array([[g["q"]]]), kc, vc, [[0]], [2], 1.0 / math.sqrt(2.0))
+    assert np.allclose(out[0, 0], g["o"], atol=1e-14)
+    # the probabilities themselves: o = p0 v0 + p1 v1 with v0, v1 on separate axes
+    assert np.allclose(out[0, 0] / 4.0, [g["p"][0], g["p"][1]], atol=1e-14)
 
 
 def test_context_one_returns_the_new_value_exactly():
