@@ -154,3 +154,43 @@ def test_decode_zero_context_gives_zero(gpu):
         torch.cuda.synchronize()
         assert torch.all(out[0] == 0)
         assert torch.all(torch.isfinite(out[1]))
+
+
+# --------------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("name", ["qwen3_decode", "long_decode", "int8_decode"])
+def test_decode_full_size_sampled(gpu, name):
+    """Full-size workload in the launch configuration the bench times (automatic split plan,
+    max_context_len covering its 23 default steps); eight sampled sequences are checked against
+    the oracle one by one, and their stored cache rows bit for bit through the oracle's tables."""
+    from oracle import allocator as OA
+    from oracle import steps as OS
+    cfg = W.config(name)
+    wl = W.decode_workload(cfg, 0)
+    say(f"full-size {name}: B={len(wl['lens'])} sum ctx={sum(wl['lens'])}")
+    out, kv, batch = gpu_decode(wl, gpu, max_context_len=max(wl["lens"]) + 23)
+    got = host_out(out)
+    sample = np.random.default_rng(7).choice(len(wl["lens"]), size=8, replace=False)
+    ref = np.stack([OS.decode_one_sequence(cfg, wl["seqs"][b], wl["lens"][b]) for b in sample])
+    check_tol(got[sample], ref, cfg["dtype"], f"{name} full size, 8 sampled sequences")
+    # the cache rows of the sampled sequences, located through the oracle's own block manager
+    a = OA.Allocator(wl["num_blocks"], wl["free_order"])
+    for b, s in enumerate(wl["seqs"]):
+        a.add_seq(b, s["tokens"][:-1])
+    for b, s in enumerate(wl["seqs"]):
+        a.append(b, int(s["tokens"][-1]))
+    key = "kq" if cfg["dtype"] == "i8" else "k"
+    vkey = "vq" if cfg["dtype"] == "i8" else "v"
+    kc = kv.k_cache.view(torch.int8 if cfg["dtype"] == "i8" else torch.int16)
+    vc = kv.v_cache.view(torch.int8 if cfg["dtype"] == "i8" else torch.int16)
+    for b in sample[:3]:
+        L = wl["lens"][b]
+        row = a.block_tables([b], -(-L // 256))[0]
+        idx = torch.tensor([row[j // 256] for j in range(L)], device=gpu)
+        off = torch.tensor([j % 256 for j in range(L)], device=gpu)
+        gk = kc[idx, :, off].cpu().numpy()
+        gv = vc[idx, :, off].cpu().numpy()
+        ek, ev = wl["seqs"][b][key], wl["seqs"][b][vkey]
+        assert np.array_equal(gk.view(ek.dtype), ek) and np.array_equal(gv.view(ev.dtype), ev)
+        if cfg["dtype"] == "i8":
+            ks = kv.k_scale[idx[::256].long()].cpu().numpy()
+            assert np.array_equal(ks, wl["seqs"][b]["k_blk_scale"])
