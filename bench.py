@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--se
 """
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -215,6 +216,10 @@ def bench_decode(args, cfg):
         if timed_idx is not None:
             ev[timed_idx][1].record(stream)
 
+    # Python's cyclic GC can pause the host for tens of ms inside a step; like timeit (and serving
+    # loops), collect once and keep it off while timing
+    gc.collect()
+    gc.disable()
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
@@ -223,6 +228,7 @@ def bench_decode(args, cfg):
         run(args.warmup + j, j)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
     bytes_per_launch = sum(kv_bytes(steps[args.warmup + j]["ctx"]) for j in range(args.steps)) / args.steps
@@ -334,6 +340,8 @@ def bench_prefill(args, cfg):
             if timed is not None:
                 ev[timed][c][1].record(stream)
 
+    gc.collect()
+    gc.disable()
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -342,6 +350,7 @@ def bench_prefill(args, cfg):
         run(j)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     kern_s = sum(a.elapsed_time(b) for row in ev for a, b in row) / args.steps / 1e3
     tflops = flops / kern_s / 1e12
     total_new = sum(n_new)

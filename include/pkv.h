@@ -185,15 +185,18 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32
  * k_cache, v_cache: device, layout above.  k_scale, v_scale: int8 caches only, else NULL.
  * block_tables: device int32[B][max_blocks]; context_lens: device int32[B] -- the number
  * of tokens to attend, including the one just stored; 0 gives a zero output.
+ * seq_order: NULL, or device int32[B], a permutation of 0..B-1 giving the order in which the
+ * sequences' workgroups are launched (longest context first shortens the tail of the launch);
+ * the output stays indexed by sequence.
  * max_context_len: host upper bound of context_lens (sizes the split plan).
  * out: device [B][Hq][head_dim] in the dtype of q.  workspace: device, at least
  * pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0). */
 int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
                           const void* k_cache, const void* v_cache, const float* k_scale,
                           const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
-                          const int32_t* context_lens, int32_t max_context_len, int32_t max_splits,
-                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                          const int32_t* context_lens, const int32_t* seq_order,
+                          int32_t max_context_len, int32_t max_splits, float softmax_scale,
+                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation).

@@ -59,8 +59,8 @@ SIGNATURES = {
     "pkv_kv_store": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pkv_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _p32, _p32]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
-    "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
-                                     _f32, _vp, _vp, _sz, _vp]),
+    "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                     _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attn_prefill": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                       _f32, _i32, _vp, _vp]),
 }
@@ -227,8 +227,10 @@ def decode_workspace_bytes(B, Hq, head_dim, num_kv_heads, max_context_len, max_s
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, softmax_scale,
-                      out=None, workspace=None, max_splits=0, k_scale=None, v_scale=None, stream=None):
-    """Decode attention; q [B][Hq][D].  Allocates ``out`` / ``workspace`` with torch when not given."""
+                      out=None, workspace=None, max_splits=0, k_scale=None, v_scale=None, seq_order=None,
+                      stream=None):
+    """Decode attention; q [B][Hq][D].  Allocates ``out`` / ``workspace`` with torch when not given.
+    ``seq_order`` (device int32 [B], optional): launch order of the sequences, e.g. longest first."""
     desc = desc_of(k_cache)
     B, Hq, D = q.shape
     if out is None:
@@ -239,7 +241,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pkv_paged_attn_decode(ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
-                                       _ptr(context_lens), int(max_context_len), int(max_splits),
+                                       _ptr(context_lens), _ptr(seq_order), int(max_context_len), int(max_splits),
                                        float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "pkv_paged_attn_decode")
     return out

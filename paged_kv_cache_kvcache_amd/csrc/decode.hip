@@ -6,7 +6,8 @@
 // for CDNA4; decode streams every KV byte once, so it is an HBM-bandwidth problem and uses no MFMA.
 //
 // Work decomposition
-//   One workgroup (4 wavefronts of 64 lanes) per (sequence, KV head, split).  A split is a run of
+//   One workgroup (4 wavefronts of 64 lanes) per (sequence, KV head, split), launched in the
+//   caller's sequence order (longest contexts first keeps the tail short).  A split is a run of
 //   blocks_per_split 256-token blocks.  Inside a block, wavefront w owns tokens 64w..64w+63 (a
 //   "tile"), so every wavefront walks the split's blocks with its own independent online-softmax
 //   state and no barrier until the end.
@@ -217,6 +218,7 @@ struct DecodeArgs {
     const float* v_scale;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    const int32_t* seq_order;  // optional launch order of the sequences (a permutation of 0..B-1)
     void* out;
     float* ws_acc;  // [B][Hq][S][D]
     float* ws_ml;   // [B][Hq][S][2]  (max in log2 units, denominator)
@@ -234,7 +236,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     using T = Traits<DT, D>;
     constexpr int E = T::E, W = T::W, RB = T::kRowBytes, PB = W * 4;
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int b = a.seq_order != nullptr ? a.seq_order[blockIdx.z] : int(blockIdx.z);
     const int ctx = a.context_lens[b];
     const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
     const int blk0 = s * a.blocks_per_split;
@@ -262,34 +265,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
     const size_t lane_off = size_t(r) * RB + size_t(c) * PB;
 
-    for (int blk = blk0; blk < blk1; ++blk) {
-        const int t0 = blk * pkv::kBlock + w * kTile;
-        if (t0 >= ctx) break;
-        const int valid = min(kTile, ctx - t0);
-        const int64_t phys = bt[blk];
-        const size_t tile = ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB;
-        const char* kp = a.k_cache + tile + lane_off;
-        const char* vp = a.v_cache + tile + lane_off;
+    // Blocks whose quarter w holds valid tokens: blk0 .. blk_end-1 (only the last may be partial).
+    const int blk_end = min(blk1, max(blk0, (ctx - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
+    auto tile_ptr = [&](const char* cache, int64_t phys) {
+        return cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
+    };
+    auto load_tile = [&](uint32_t (&dst)[16][W], const char* src, int valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (4 * i + r < valid) {
+                load_piece<W>(src + size_t(4 * i) * RB, dst[i]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < W; ++k) dst[i][k] = 0u;
+            }
+        }
+    };
 
-        uint32_t kw[16][W], vw[16][W];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (4 * i + r < valid) {
-                load_piece<W>(kp + size_t(4 * i) * RB, kw[i]);
-            } else {
-#pragma unroll
-                for (int k = 0; k < W; ++k) kw[i][k] = 0u;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (4 * i + r < valid) {
-                load_piece<W>(vp + size_t(4 * i) * RB, vw[i]);
-            } else {
-#pragma unroll
-                for (int k = 0; k < W; ++k) vw[i][k] = 0u;
-            }
-        }
+    uint32_t kw[16][W], vw[16][W];
+    for (int blk = blk0; blk < blk_end; ++blk) {
+        const int64_t phys = bt[blk];
+        const int valid = min(kTile, ctx - (blk * pkv::kBlock + w * kTile));
+        load_tile(kw, tile_ptr(a.k_cache, phys), valid);
+        load_tile(vw, tile_ptr(a.v_cache, phys), valid);
 
         float ks = a.scale_log2, vs = 1.f;
         if constexpr (DT == PKV_I8) {
@@ -496,9 +494,9 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head
 extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
                                      const void* k_cache, const void* v_cache, const float* k_scale,
                                      const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
-                                     const int32_t* context_lens, int32_t max_context_len, int32_t max_splits,
-                                     float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+                                     const int32_t* context_lens, const int32_t* seq_order,
+                                     int32_t max_context_len, int32_t max_splits, float softmax_scale, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     const int Hkv = desc->num_kv_heads, D = desc->head_dim;
@@ -529,6 +527,7 @@ extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, 
     a.v_scale = v_scale;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    a.seq_order = seq_order;
     a.out = out;
     a.max_blocks = max_blocks;
     a.num_kv_heads = Hkv;

@@ -65,14 +65,15 @@ class DecodeBatch:
         self.max_context_len = int(max_context_len)
         self.max_splits = max_splits
         dev = kv.device
-        # pinned staging for the per-step metadata: slots[B] | lens[B] | tables[B][max_blocks]
-        self._pin = torch.empty(2 * self.B + self.B * self.max_blocks, dtype=torch.int32).pin_memory()
+        # pinned staging for the per-step metadata: slots[B] | lens[B] | order[B] | tables[B][max_blocks]
+        self._pin = torch.empty(3 * self.B + self.B * self.max_blocks, dtype=torch.int32).pin_memory()
         self._meta = torch.empty_like(self._pin, device=dev)
         self._copied = torch.cuda.Event()
         self._copied.record()
         self.slots = self._meta[:self.B]
         self.context_lens = self._meta[self.B:2 * self.B]
-        self.block_tables = self._meta[2 * self.B:].view(self.B, self.max_blocks)
+        self.seq_order = self._meta[2 * self.B:3 * self.B]
+        self.block_tables = self._meta[3 * self.B:].view(self.B, self.max_blocks)
         nbytes = decode_workspace_bytes(self.B, self.Hq, kv.D, kv.Hkv, self.max_context_len, max_splits)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
@@ -82,8 +83,10 @@ class DecodeBatch:
         pin = self._pin.numpy()
         B, mb = self.B, self.max_blocks
         pin[:B] = slots
-        tab = pin[2 * B:].reshape(B, mb)
-        self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=pin[B:2 * B])
+        tab = pin[3 * B:].reshape(B, mb)
+        lens = pin[B:2 * B]
+        self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=lens)
+        pin[2 * B:3 * B] = np.argsort(-lens, kind="stable")  # longest contexts launch first
         self._meta.copy_(self._pin, non_blocking=True)
         self._copied.record()
 
@@ -97,7 +100,8 @@ class DecodeBatch:
     def attend(self, q, softmax_scale, out=None):
         return paged_attn_decode(q, self.kv.k_cache, self.kv.v_cache, self.block_tables, self.context_lens,
                                  self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
-                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale)
+                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale,
+                                 seq_order=self.seq_order)
 
 
 def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None, v_scale_rows=None):

@@ -75,7 +75,7 @@ def test_kv_store_scale_pointer_rules():
 def _decode(desc, B=2, Hq=4, max_blocks=3, max_ctx=600, splits=0, ks=None, vs=None, ws=None, ws_bytes=0,
             scale=0.125):
     return P.lib().pkv_paged_attn_decode(ctypes.byref(desc), FAKE, B, Hq, FAKE, FAKE, ks, vs, FAKE, max_blocks,
-                                         FAKE, max_ctx, splits, scale, FAKE, ws, ws_bytes, None)
+                                         FAKE, None, max_ctx, splits, scale, FAKE, ws, ws_bytes, None)
 
 
 def test_decode_rejects_bad_arguments():
