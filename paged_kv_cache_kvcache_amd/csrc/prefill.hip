@@ -7,26 +7,25 @@
 // article, §2.1).  The kernel below is this library's own design for CDNA4.
 //
 // Work decomposition
-//   One workgroup per (sequence, query tile, KV head).  The G = Hq/Hkv query heads that read one
-//   KV head are stacked into 128 MFMA rows: a query tile holds QT = 128/G new tokens of all G
-//   heads, so every K/V tile staged in LDS serves all of them.  A group of four wavefronts walks
-//   the key tiles; wavefront w owns rows 32w..32w+31 (row rho -> head rho / QT, token rho % QT).
-//   Optionally (template NS = 2) a second group splits the key range (tiles s, s+2, ...) with its
-//   own LDS stages and the partial softmax states are merged through LDS; on MI355X two
-//   independent one-group workgroups per CU measured faster, so NS = 1 is dispatched.  Work items
-//   are ordered so that the tiles with the longest causal rows (each sequence's last) start first.
+//   One workgroup (four wavefronts) per (sequence, query tile, KV head).  The G = Hq/Hkv query heads
+//   that read one KV head are stacked into 128 MFMA rows: a query tile holds QT = 128/G new tokens
+//   of all G heads, so every K/V tile staged in LDS serves all of them.  Wavefront w owns rows
+//   32w..32w+31 (row rho -> head rho / QT, token rho % QT).  Work items are ordered so that the tiles
+//   with the longest causal rows (each sequence's last) start first.
 //
-// Per 64-key tile (double-buffered in LDS, next tile's global loads in flight during compute):
+// Per 64-key tile (two LDS stages; the next tile's DMA is in flight during compute):
+//   staging         K and V rows go from HBM straight into LDS (global_load_lds_dwordx4, no
+//                   registers), row-major with XOR-swizzled 16-byte chunks.
 //   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T kept in registers.
 //                   The accumulator layout puts one query per lane column, 16 keys per lane, and
 //                   the other 16 keys of that query in lane ^ 32: the softmax max/sum of a query
 //                   needs a single cross-lane swap.
 //   online softmax  log2 domain, one FMA folds the scale into the exponent, causal mask by
 //                   absolute position (bottom-right aligned) on diagonal tiles only, lazy rescale.
-//   O^T += V^T P^T  A = V^T from LDS, B = P^T converted to bf16 straight from the S accumulators.
-//                   V is stored transposed in LDS with the keys of each 16-key group permuted
-//                   (bits 2 and 3 of the key index swapped) so that the 8 keys a lane needs for the
-//                   MFMA operand are contiguous and match the keys its S values belong to.
+//   O^T += V^T P^T  A = V^T read from the row-major V tile with LDS transpose reads
+//                   (ds_read_b64_tr_b16), B = P^T converted to bf16 straight from the S
+//                   accumulators; the transpose reads fetch V for exactly the keys each lane's P
+//                   values belong to.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,7 +39,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kGroupThreads = 256;         // 4 wavefronts, 32 query rows each
+constexpr int kThreads = 256;   // 4 wavefronts, 32 query rows each
 constexpr int kRows = 128;  // MFMA query rows per workgroup (tokens x heads)
 constexpr int kKT = 64;     // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -71,35 +70,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Position of key i (0..63) of a tile in the transposed V rows: bits 2 and 3 swapped.
-__device__ __forceinline__ int vpos(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// 16-byte chunk position of chunk c in LDS row `row` of a K or V tile: c ^ swz(row).  Eight
+// consecutive rows get eight distinct low chunk bits (K operand reads: 8 lanes on 8 rows, one chunk)
+// and four consecutive rows shift an aligned chunk pair to four distinct pairs (V transpose reads:
+// 4 rows x 32 bytes per 16 lanes), so both read patterns are free of bank conflicts.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-// Byte offset of position `pos` (8-byte aligned) in transposed V row d.  Rows are 128 bytes; the
-// 16-byte chunk index is xor-ed with (d ^ d/8) & 7 so that both the transposing writes (16 lanes
-// on rows 8 apart) and the MFMA operand reads (lanes on 32 consecutive rows, one chunk) spread over
-// all banks.
-__device__ __forceinline__ int vt_off(int d, int pos) {
-    const int sw = (d ^ (d >> 3)) & 7;
-    return d * 128 + ((((pos >> 3) ^ sw) << 4) | ((pos & 4) << 1));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ i16x4_t read_tr(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)((lds_char*)(const_cast<char*>(p))));
 }
 
-// NS = number of wavefront groups that split the key range inside a workgroup (1 or 2).
-template <int D, int G, int NS>
-__global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(PrefillArgs a) {
-    constexpr int kGroups = NS;
+__device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src, (lds_char*)lds_dst, 16,
+                                     0, 0);
+}
+
+// every DMA this wavefront issued has landed in LDS (vmcnt(0); expcnt and lgkmcnt left alone)
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int QT = kRows / G;       // new tokens per workgroup
     constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;          // 32-row tiles of O^T
-    constexpr int KP = D * 2 + 16;      // LDS pitch of a K row (bytes)
-    constexpr int VP = kKT * 2;         // LDS pitch of a transposed V row (bytes), chunks swizzled
-    constexpr int KBYTES = kKT * KP;
-    constexpr int BUF = KBYTES + D * VP;
-    constexpr int CPR = D / 8;          // 16-byte pieces per K/V row
-    constexpr int KLOADS = kKT * CPR / kGroupThreads;  // K pieces per thread
-    constexpr int XCH = kGroupThreads * (16 * DT + 2) * 4;  // bytes of one group's merge state
-    static_assert(NS == 1 || NS == 2, "one or two key-range groups");
-    static_assert(XCH <= 2 * BUF, "merge state must fit in a group's stages");
-    __shared__ __attribute__((aligned(16))) char lds[kGroups][2][BUF];
+    constexpr int RB = D * 2;           // bytes per K/V row in LDS (chunks swizzled, no padding)
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int TB = kKT * RB;        // bytes of one K (or V) tile
+    constexpr int NLD = TB / (kThreads * 16);  // DMA instructions per wavefront per tile, K and V each
+    static_assert(NLD >= 1 && NLD * kThreads * 16 == TB, "a tile is a whole number of wavefront DMAs");
+    __shared__ __attribute__((aligned(1024))) char lds[2][2 * TB];  // two stages of (K tile, V tile)
 
     // ---- which (sequence, query tile, KV head) this workgroup owns.  Work items are ordered by
     // distance from the end of their sequence (every sequence's last tile first, then every
@@ -136,10 +139,8 @@ __global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(Pre
     const int kv_len = a.causal ? min(Lk, pos0 + nqt) : Lk;
     const int ntiles = (kv_len + kKT - 1) / kKT;
 
-    const int tid = threadIdx.x & (kGroupThreads - 1);  // thread within its group
-    const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / kGroupThreads);
-    const int w = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);
-    const int lane = tid & 63, col = lane & 31, h = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
     const int rho = 32 * w + col;
     const int j = rho / QT, t = rho % QT;
     const bool col_ok = t < nqt;
@@ -170,58 +171,51 @@ __global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(Pre
     const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
     const size_t head_off = size_t(g) * pkv::kBlock;
 
-    // ---- global -> register staging of one K/V tile
-    uint4 kreg[KLOADS], vreg[4];
-    const bool v_thread = tid < 16 * CPR;   // threads that move a 4-key x 8-d piece of V
-    const int vkg = tid / CPR, vc = tid % CPR;
-    auto gload = [&](int kt) {
+    // ---- global -> LDS DMA of one K/V tile.  Instruction r of wavefront w fills LDS bytes
+    // [(NLD w + r) KiB, +1 KiB) of the tile, lane l the 16 bytes at +16 l: row L / CPR, position
+    // L % CPR, which holds chunk (L % CPR) ^ swz(row) of that key row.  Rows past the sequence end
+    // are read from its last key (finite data; their scores are masked, their probabilities zero).
+    int drow[NLD], dcol[NLD];
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+        const int L = (NLD * w + r) * 64 + lane;
+        drow[r] = L / CPR;
+        dcol[r] = ((L % CPR) ^ swz(L / CPR)) * 16;
+    }
+    auto dma = [&](int kt, char* stage) {
         const int key0 = kt * kKT;
         const int64_t phys = bt[key0 / pkv::kBlock];
         const size_t row0 = (size_t(phys) * a.num_kv_heads) * pkv::kBlock + head_off + key0 % pkv::kBlock;
-        const uint4* kg = reinterpret_cast<const uint4*>(a.k_cache + row0 * D * 2);
-        const uint4* vg = reinterpret_cast<const uint4*>(a.v_cache + row0 * D * 2);
+        const char* kg = a.k_cache + row0 * RB;
+        const char* vg = a.v_cache + row0 * RB;
+        const int last = kv_len - 1 - key0;
 #pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int p = tid + kGroupThreads * r;
-            const int row = p / CPR;
-            kreg[r] = (key0 + row < kv_len) ? kg[p] : make_uint4(0, 0, 0, 0);
-        }
-        if (v_thread) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int row = 4 * vkg + k;
-                vreg[k] = (key0 + row < kv_len) ? vg[row * CPR + vc] : make_uint4(0, 0, 0, 0);
-            }
+        for (int r = 0; r < NLD; ++r) {
+            const size_t off = size_t(min(drow[r], last)) * RB + dcol[r];
+            dma16(kg + off, stage + (NLD * w + r) * 1024);
+            dma16(vg + off, stage + TB + (NLD * w + r) * 1024);
         }
     };
-    // ---- register -> LDS (K row-major, V transposed with permuted keys)
-    auto lstore = [&](int buf) {
-        char* Ks = lds[grp][buf];
-        char* Vt = lds[grp][buf] + KBYTES;
+
+    // ---- per-lane LDS read offsets.  K operand (S^T = K Q^T): lane reads key row 32mt + col,
+    // chunk 2ks + h; swz(row) depends on col only, and ks >= 4 adds 8 chunks (128 bytes).
+    int koff[4];
 #pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int p = tid + kGroupThreads * r;
-            *reinterpret_cast<uint4*>(Ks + (p / CPR) * KP + (p % CPR) * 16) = kreg[r];
+    for (int x = 0; x < 4; ++x) koff[x] = col * RB + (((2 * x + h) ^ swz(col)) << 4);
+    // V^T operand (O^T += V^T P^T) by transpose reads: in each 16-lane group, lane i of the result
+    // takes element i % 4 of the 8 bytes addressed by lane 4e + i / 4, for e = 0..3.  Lane l
+    // addresses key row 4h + (l & 15) / 4 (+ a multiple of 8) and the four d from
+    // 32dt + 16((l >> 4) & 1) + 4(l & 3), so result lane l holds d = 32dt + (l & 31) for four
+    // consecutive keys.  Within a 32-d tile the chunk is 4(dt & 1) + 2((l >> 4) & 1) + ((l >> 1) & 1).
+    int voff[2];
+    {
+        const int vr = 4 * h + ((lane & 15) >> 2);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int c = 4 * x + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+            voff[x] = vr * RB + ((c ^ swz(vr)) << 4) + 8 * (lane & 1);
         }
-        if (v_thread) {
-            const int pos = vpos(4 * vkg);
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const uint32_t sel = s ? 0x07060302u : 0x05040100u;
-                    uint2 pr;
-                    pr.x = __builtin_amdgcn_perm(w1[m], w0[m], sel);
-                    pr.y = __builtin_amdgcn_perm(w3[m], w2[m], sel);
-                    *reinterpret_cast<uint2*>(Vt + vt_off(8 * vc + 2 * m + s, pos)) = pr;
-                }
-            }
-        }
-    };
+    }
 
     f32x16_t o[DT];
 #pragma unroll
@@ -230,31 +224,27 @@ __global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(Pre
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    // group grp walks tiles grp, grp + kGroups, ...; one workgroup barrier per step
-    const int steps = (ntiles + kGroups - 1) / kGroups;
-    if (grp < ntiles) gload(grp);
-    // One step: stage this group's tile, launch the next tile's loads, barrier, compute.  The step is
+    if (ntiles > 0) dma(0, lds[0]);
+    // One step per key tile: wait for its DMA, barrier (the other stage is then free: every
+    // wavefront finished the previous tile), launch the next tile's DMA, compute.  The step is
     // instantiated for each LDS stage so that every LDS address offset is an immediate.
-    auto step = [&](int st, auto stage) {
+    auto step = [&](int kt, auto stage) {
         constexpr int buf = decltype(stage)::value;
-        const int kt = st * kGroups + grp;
-        if (kt < ntiles) lstore(buf);
-        // the next tile's loads go out before the barrier, so the barrier wait also hides them
-        if (kt + kGroups < ntiles) gload(kt + kGroups);
+        wait_dma();
         __syncthreads();
-        if (kt >= ntiles || kt * kKT > pw_max) return;  // no tile, or every key masked for this wavefront
+        if (kt + 1 < ntiles) dma(kt + 1, lds[buf ^ 1]);
+        if (kt * kKT > pw_max) return;  // every key of this tile is masked for this wavefront
 
-        const char* Ks = lds[grp][buf];
-        const char* Vt = lds[grp][buf] + KBYTES;
-        // S^T = K Q^T for keys 32mt..32mt+31
-        // two independent accumulator chains (keys 0-31 and 32-63), interleaved k-step by k-step
+        const char* Ks = lds[buf];
+        const char* Vs = lds[buf] + TB;
+        // S^T = K Q^T for keys 32mt..32mt+31: two independent accumulator chains, interleaved
         f32x16_t s[2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bf16x8_t ka[2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + (32 * mt + col) * KP + (16 * ks + 8 * h) * 2);
+                ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks & 3] + 32 * mt * RB + 128 * (ks >> 2));
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)  // the first k-step starts from an inline zero accumulator
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mt], qb[ks], ks == 0 ? kZero16 : s[mt], 0, 0, 0);
@@ -300,7 +290,9 @@ __global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(Pre
                 psum += p;
             }
         l_run += psum;
-        // O^T += V^T P^T
+        // O^T += V^T P^T over keys 32mt + 16kk + [0, 16).  This lane's P values are keys
+        // 16kk + 4h + {0..3} (elements 8kk..8kk+3 of s[mt]) and 16kk + 8 + 4h + {0..3} (8kk+4..8kk+7);
+        // the two transpose reads fetch V of exactly those keys, in that order.
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -313,44 +305,18 @@ __global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(Pre
                 const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw4);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-                        Vt + vt_off(32 * dt + col, 32 * mt + 16 * kk + 8 * h));
+                    const char* vp = Vs + voff[dt & 1] + (32 * mt + 16 * kk) * RB + 128 * (dt >> 1);
+                    const i16x4_t lo = read_tr(vp);
+                    const i16x4_t hi = read_tr(vp + 8 * RB);
+                    const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
                 }
             }
         }
-    
     };
-    for (int st = 0; st < steps; st += 2) {
-        step(st, std::integral_constant<int, 0>{});
-        if (st + 1 < steps) step(st + 1, std::integral_constant<int, 1>{});
-    }
-
-    // ---- merge the second group's state into the first through LDS (stages are free now)
-    if constexpr (NS == 2) {
-    __syncthreads();
-    float* xch = reinterpret_cast<float*>(lds[0][0]) + w * (16 * DT + 2) * 64 + lane;
-    if (grp == 1) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xch[(16 * dt + i) * 64] = o[dt][i];
-        xch[(16 * DT) * 64] = m_run;
-        xch[(16 * DT + 1) * 64] = l_run;
-    }
-    __syncthreads();
-    if (grp != 0) return;
-    {
-        const float m1 = xch[(16 * DT) * 64], l1 = xch[(16 * DT + 1) * 64];
-        const float mx = fmaxf(m_run, m1);  // group 0 always saw tile 0, so mx is finite
-        const float f0 = __builtin_amdgcn_exp2f(m_run - mx);
-        const float f1 = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
-        l_run = l_run * f0 + l1 * f1;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[dt][i] = o[dt][i] * f0 + xch[(16 * dt + i) * 64] * f1;
-    }
+    for (int kt = 0; kt < ntiles; kt += 2) {
+        step(kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- normalise and write this column's row: d = 32dt + 8(i/4) + 4h + i%4
@@ -369,17 +335,12 @@ __global__ __launch_bounds__(NS * kGroupThreads, 3 - NS) void prefill_kernel(Pre
         }
 }
 
-// One group of four wavefronts per workgroup, two workgroups per CU: measured faster on MI355X than
-// two key-range groups in one workgroup per CU (kept for experiments: prefill_kernel<D, G, 2>).
-constexpr int kPrefillGroups = 1;
-
 template <int D, int G>
 hipError_t launch(const PrefillArgs& a, int total_q, hipStream_t st) {
     constexpr int QT = kRows / G;
     const long items = ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
     if (items > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D, G, kPrefillGroups>), dim3(unsigned(items)),
-                       dim3(kPrefillGroups * kGroupThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(unsigned(items)), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
