@@ -70,11 +70,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 16-byte chunk position of chunk c in LDS row `row` of a K or V tile: c ^ swz(row).  Eight
-// consecutive rows get eight distinct low chunk bits (K operand reads: 8 lanes on 8 rows, one chunk)
-// and four consecutive rows shift an aligned chunk pair to four distinct pairs (V transpose reads:
-// 4 rows x 32 bytes per 16 lanes), so both read patterns are free of bank conflicts.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// LDS holds 64 banks of 4 bytes: a 16-byte chunk position p of a row sits on bank group
+// (row * RB / 16 + p) % 16.  Chunk c of a K or V row is stored at position c ^ swz(row), with one
+// swizzle per tile so that each operand read pattern is free of bank conflicts:
+//   K (ds_read_b128, 16 lanes per cycle on 16 consecutive rows, one chunk): the 16 rows must land
+//     on 16 distinct bank groups;
+//   V (ds_read_b64_tr_b16, 32 lanes per cycle on 4 consecutive rows x 4 consecutive chunks): the
+//     16 (row, chunk) pairs must land on 16 distinct bank groups.
+// The V swizzle depends only on row bits that are constant across the rows one lane reads.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -102,7 +109,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     constexpr int TB = kKT * RB;        // bytes of one K (or V) tile
     constexpr int NLD = TB / (kThreads * 16);  // DMA instructions per wavefront per tile, K and V each
     static_assert(NLD >= 1 && NLD * kThreads * 16 == TB, "a tile is a whole number of wavefront DMAs");
-    __shared__ __attribute__((aligned(1024))) char lds[2][2 * TB];  // two stages of (K tile, V tile)
+    // Two stages of (K tile, V tile), as two distinct arrays: the compiler then sees that reads of
+    // one stage cannot alias the DMA in flight into the other and adds no wait for it.
+    __shared__ __attribute__((aligned(1024))) char lds0[2 * TB];
+    __shared__ __attribute__((aligned(1024))) char lds1[2 * TB];
+    char* const lds[2] = {lds0, lds1};
 
     // ---- which (sequence, query tile, KV head) this workgroup owns.  Work items are ordered by
     // distance from the end of their sequence (every sequence's last tile first, then every
@@ -173,14 +184,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
     // ---- global -> LDS DMA of one K/V tile.  Instruction r of wavefront w fills LDS bytes
     // [(NLD w + r) KiB, +1 KiB) of the tile, lane l the 16 bytes at +16 l: row L / CPR, position
-    // L % CPR, which holds chunk (L % CPR) ^ swz(row) of that key row.  Rows past the sequence end
+    // L % CPR, which holds chunk (L % CPR) ^ swz_k(row) (K) or ^ swz_v(row) (V) of that key row.  Rows past the sequence end
     // are read from its last key (finite data; their scores are masked, their probabilities zero).
-    int drow[NLD], dcol[NLD];
+    int drow[NLD], kcol[NLD], vcol[NLD];
 #pragma unroll
     for (int r = 0; r < NLD; ++r) {
         const int L = (NLD * w + r) * 64 + lane;
         drow[r] = L / CPR;
-        dcol[r] = ((L % CPR) ^ swz(L / CPR)) * 16;
+        kcol[r] = ((L % CPR) ^ swz_k<D>(L / CPR)) * 16;
+        vcol[r] = ((L % CPR) ^ swz_v<D>(L / CPR)) * 16;
     }
     auto dma = [&](int kt, char* stage) {
         const int key0 = kt * kKT;
@@ -191,29 +203,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int last = kv_len - 1 - key0;
 #pragma unroll
         for (int r = 0; r < NLD; ++r) {
-            const size_t off = size_t(min(drow[r], last)) * RB + dcol[r];
-            dma16(kg + off, stage + (NLD * w + r) * 1024);
-            dma16(vg + off, stage + TB + (NLD * w + r) * 1024);
+            const size_t row = size_t(min(drow[r], last)) * RB;
+            dma16(kg + row + kcol[r], stage + (NLD * w + r) * 1024);
+            dma16(vg + row + vcol[r], stage + TB + (NLD * w + r) * 1024);
         }
     };
 
     // ---- per-lane LDS read offsets.  K operand (S^T = K Q^T): lane reads key row 32mt + col,
-    // chunk 2ks + h; swz(row) depends on col only, and ks >= 4 adds 8 chunks (128 bytes).
-    int koff[4];
+    // chunk 2ks + h; the swizzle of that row depends on col only.
+    int koff[KS];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) koff[x] = col * RB + (((2 * x + h) ^ swz(col)) << 4);
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = col * RB + (((2 * ks + h) ^ swz_k<D>(col)) << 4);
     // V^T operand (O^T += V^T P^T) by transpose reads: in each 16-lane group, lane i of the result
     // takes element i % 4 of the 8 bytes addressed by lane 4e + i / 4, for e = 0..3.  Lane l
     // addresses key row 4h + (l & 15) / 4 (+ a multiple of 8) and the four d from
     // 32dt + 16((l >> 4) & 1) + 4(l & 3), so result lane l holds d = 32dt + (l & 31) for four
-    // consecutive keys.  Within a 32-d tile the chunk is 4(dt & 1) + 2((l >> 4) & 1) + ((l >> 1) & 1).
-    int voff[2];
+    // consecutive keys.  The chunk of those four d is 4dt + 2((l >> 4) & 1) + ((l >> 1) & 1).
+    int voff[DT];
     {
         const int vr = 4 * h + ((lane & 15) >> 2);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int c = 4 * x + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
-            voff[x] = vr * RB + ((c ^ swz(vr)) << 4) + 8 * (lane & 1);
+        for (int dt = 0; dt < DT; ++dt) {
+            const int c = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+            voff[dt] = vr * RB + ((c ^ swz_v<D>(vr)) << 4) + 8 * (lane & 1);
         }
     }
 
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
             bf16x8_t ka[2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks & 3] + 32 * mt * RB + 128 * (ks >> 2));
+                ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks] + 32 * mt * RB);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)  // the first k-step starts from an inline zero accumulator
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mt], qb[ks], ks == 0 ? kZero16 : s[mt], 0, 0, 0);
@@ -305,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                 const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw4);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    const char* vp = Vs + voff[dt & 1] + (32 * mt + 16 * kk) * RB + 128 * (dt >> 1);
+                    const char* vp = Vs + voff[dt] + (32 * mt + 16 * kk) * RB;
                     const i16x4_t lo = read_tr(vp);
                     const i16x4_t hi = read_tr(vp + 8 * RB);
                     const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
