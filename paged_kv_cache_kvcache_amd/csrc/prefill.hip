@@ -38,13 +38,14 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // 4 wavefronts, 32 query rows each
 constexpr int kRows = 128;  // MFMA query rows per workgroup (tokens x heads)
 constexpr int kKT = 64;     // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
-constexpr f32x16_t kZero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+constexpr bf16x2_t kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
 struct PrefillArgs {
     const uint16_t* q;
@@ -167,7 +168,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int pw_max = __builtin_amdgcn_readfirstlane(pw);
     const int pw_min = __builtin_amdgcn_readfirstlane(pm);
 
-    // ---- Q^T operand: column col = query row, 8 consecutive d per k-step
+    // ---- Q^T operand: column col = query row, 8 consecutive d per k-step.  Q is multiplied by
+    // softmax_scale * log2(e) (fp32, rounded once to bf16), so S comes out in log2 units.
     bf16x8_t qb[KS];
     {
         const int tq = min(t, nqt - 1);
@@ -175,6 +177,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 v = col_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+            uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                u[e] = pack_bf16x2(__uint_as_float(u[e] << 16) * a.scale_log2,
+                                   __uint_as_float(u[e] & 0xffff0000u) * a.scale_log2);
             qb[ks] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
@@ -186,7 +193,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // [(NLD w + r) KiB, +1 KiB) of the tile, lane l the 16 bytes at +16 l: row L / CPR, position
     // L % CPR, which holds chunk (L % CPR) ^ swz_k(row) (K) or ^ swz_v(row) (V) of that key row.  Rows past the sequence end
     // are read from its last key (finite data; their scores are masked, their probabilities zero).
-    int drow[NLD], kcol[NLD], vcol[NLD];
+    int drow[NLD];
+    uint32_t kcol[NLD], vcol[NLD];
 #pragma unroll
     for (int r = 0; r < NLD; ++r) {
         const int L = (NLD * w + r) * 64 + lane;
@@ -203,9 +211,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int last = kv_len - 1 - key0;
 #pragma unroll
         for (int r = 0; r < NLD; ++r) {
-            const size_t row = size_t(min(drow[r], last)) * RB;
-            dma16(kg + row + kcol[r], stage + (NLD * w + r) * 1024);
-            dma16(vg + row + vcol[r], stage + TB + (NLD * w + r) * 1024);
+            const uint32_t row = uint32_t(min(drow[r], last) * RB);  // 32-bit offsets from a uniform base
+            dma16(kg + (row + kcol[r]), stage + (NLD * w + r) * 1024);
+            dma16(vg + (row + vcol[r]), stage + TB + (NLD * w + r) * 1024);
         }
     };
 
@@ -249,19 +257,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
         const char* Ks = lds[buf];
         const char* Vs = lds[buf] + TB;
-        // S^T = K Q^T for keys 32mt..32mt+31: two independent accumulator chains, interleaved
+        // S^T = K Q^T - base for keys 32mt..32mt+31 (log2 units, relative to this column's running
+        // max; the first k-step starts from the accumulator -base), two interleaved chains
+        const float base = m_run == kNegInf ? 0.f : m_run;
         f32x16_t s[2];
+        {
+            f32x16_t c0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8_t ka[2];
+            for (int i = 0; i < 16; ++i) c0[i] = -base;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks] + 32 * mt * RB);
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8_t ka[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)  // the first k-step starts from an inline zero accumulator
-                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mt], qb[ks], ks == 0 ? kZero16 : s[mt], 0, 0, 0);
+                for (int mt = 0; mt < 2; ++mt)
+                    ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks] + 32 * mt * RB);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mt], qb[ks], ks == 0 ? c0 : s[mt], 0, 0, 0);
+            }
         }
-        // mask (diagonal tiles only) and tile max, in raw score units (the scale is positive)
+        // mask (diagonal tiles only) and tile max
         float tmax = kNegInf;
         if (kt * kKT + kKT - 1 > pw_min) {
 #pragma unroll
@@ -278,30 +293,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mt][i]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.scale_log2;
-        // Lazy rescaling: the reference max only moves when some column's max grew by more than
-        // 2^8, so most tiles skip rescaling O; probabilities then stay below 2^8, well inside bf16.
-        if (__any(tmax > m_run + 8.f)) {
-            const float mn = fmaxf(m_run, tmax);  // finite: key 0 is visible to every column
-            const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // Lazy rescaling: the running max only moves on a column's first tile or when its max grew
+        // by more than 2^8, so most tiles skip rescaling O and take p = exp2(s) directly;
+        // probabilities then stay below 2^8, well inside bf16.
+        if (__any(tmax > 8.f || m_run == kNegInf)) {
+            const float mn = fmaxf(m_run, base + tmax);
+            const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
+            const float shift = mn == kNegInf ? 0.f : mn - base;
             m_run = mn;
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[mt][i] -= shift;
         }
-        const float neg_m = -m_run;
-        float psum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[mt][i], a.scale_log2, neg_m));
-                s[mt][i] = p;
-                psum += p;
-            }
-        l_run += psum;
+            for (int i = 0; i < 16; ++i) s[mt][i] = __builtin_amdgcn_exp2f(s[mt][i]);
         // O^T += V^T P^T over keys 32mt + 16kk + [0, 16).  This lane's P values are keys
         // 16kk + 4h + {0..3} (elements 8kk..8kk+3 of s[mt]) and 16kk + 8 + 4h + {0..3} (8kk+4..8kk+7);
         // the two transpose reads fetch V of exactly those keys, in that order.
@@ -315,6 +329,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                 pw4.z = pack_bf16x2(s[mt][8 * kk + 4], s[mt][8 * kk + 5]);
                 pw4.w = pack_bf16x2(s[mt][8 * kk + 6], s[mt][8 * kk + 7]);
                 const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw4);
+                // the row sum takes the same bf16 probabilities that multiply V
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw4.x), kOnes2, l_run, false);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw4.y), kOnes2, l_run, false);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw4.z), kOnes2, l_run, false);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw4.w), kOnes2, l_run, false);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const char* vp = Vs + voff[dt] + (32 * mt + 16 * kk) * RB;
