@@ -262,20 +262,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const float base = m_run == kNegInf ? 0.f : m_run;
         f32x16_t s[2];
         {
+            // all K operand reads first, so their LDS latency overlaps instead of stalling each MFMA
+            bf16x8_t ka[KS][2];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    ka[ks][mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks] + 32 * mt * RB);
+            __builtin_amdgcn_sched_barrier(0);
             f32x16_t c0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) c0[i] = -base;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                bf16x8_t ka[2];
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
-                    ka[mt] = *reinterpret_cast<const bf16x8_t*>(Ks + koff[ks] + 32 * mt * RB);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[mt], qb[ks], ks == 0 ? c0 : s[mt], 0, 0, 0);
-            }
+                    s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks][mt], qb[ks], ks == 0 ? c0 : s[mt], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // V^T operands of this tile: issued before the softmax, which hides their latency.  va
+        // [mt][kk][dt] covers keys 32mt + 16kk + {4h..4h+3, 8+4h..8+4h+3}, d = 32dt + (lane & 31).
+        bf16x8_t va[2][2][DT];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const char* vp = Vs + voff[dt] + (32 * mt + 16 * kk) * RB;
+                    const i16x4_t lo = read_tr(vp);
+                    const i16x4_t hi = read_tr(vp + 8 * RB);
+                    va[mt][kk][dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+        __builtin_amdgcn_sched_barrier(0);
         // mask (diagonal tiles only) and tile max
         float tmax = kNegInf;
         if (kt * kKT + kKT - 1 > pw_min) {
@@ -317,8 +336,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[mt][i] = __builtin_amdgcn_exp2f(s[mt][i]);
         // O^T += V^T P^T over keys 32mt + 16kk + [0, 16).  This lane's P values are keys
-        // 16kk + 4h + {0..3} (elements 8kk..8kk+3 of s[mt]) and 16kk + 8 + 4h + {0..3} (8kk+4..8kk+7);
-        // the two transpose reads fetch V of exactly those keys, in that order.
+        // 16kk + 4h + {0..3} (elements 8kk..8kk+3 of s[mt]) and 16kk + 8 + 4h + {0..3} (8kk+4..8kk+7):
+        // the keys, in that order, of the V operand va[mt][kk].
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -335,13 +354,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw4.z), kOnes2, l_run, false);
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw4.w), kOnes2, l_run, false);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const char* vp = Vs + voff[dt] + (32 * mt + 16 * kk) * RB;
-                    const i16x4_t lo = read_tr(vp);
-                    const i16x4_t hi = read_tr(vp + 8 * RB);
-                    const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < DT; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[mt][kk][dt], pb, o[dt], 0, 0, 0);
             }
         }
     };
