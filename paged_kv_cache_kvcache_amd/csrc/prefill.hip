@@ -7,11 +7,13 @@
 // article, §2.1).  The kernel below is this library's own design for CDNA4.
 //
 // Work decomposition
-//   One workgroup (four wavefronts) per (sequence, query tile, KV head).  The G = Hq/Hkv query heads
-//   that read one KV head are stacked into 128 MFMA rows: a query tile holds QT = 128/G new tokens
-//   of all G heads, so every K/V tile staged in LDS serves all of them.  Wavefront w owns rows
-//   32w..32w+31 (row rho -> head rho / QT, token rho % QT).  Work items are ordered so that the tiles
-//   with the longest causal rows (each sequence's last) start first.
+//   One workgroup (NW = 4 or 8 wavefronts) per (sequence, query tile, KV head).  The G = Hq/Hkv
+//   query heads that read one KV head are stacked into 32 NW MFMA rows: a query tile holds
+//   QT = 32 NW / G new tokens of all G heads, so every K/V tile staged in LDS serves all of them.
+//   Wavefront w owns rows 32w..32w+31 (row rho -> head rho / QT, token rho % QT).  Work items are
+//   ordered so that the tiles with the longest causal rows (each sequence's last) start first.
+//   Large launches take eight wavefronts (half the K/V staging per row), small ones four (twice
+//   the workgroups, a shorter tail).
 //
 // Per 64-key tile (two LDS stages; the next tile's DMA is in flight during compute):
 //   staging         K and V rows go from HBM straight into LDS (global_load_lds_dwordx4, no
@@ -40,8 +42,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;   // 4 wavefronts, 32 query rows each
-constexpr int kRows = 128;  // MFMA query rows per workgroup (tokens x heads)
+constexpr int kWaveRows = 32;  // MFMA query rows (tokens x heads) per wavefront
 constexpr int kKT = 64;     // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -INFINITY;
@@ -100,8 +101,11 @@ __device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
 // every DMA this wavefront issued has landed in LDS (vmcnt(0); expcnt and lgkmcnt left alone)
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
+// NW = wavefronts per workgroup (4 or 8): all of them share each staged K/V tile.
+template <int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
+    constexpr int kThreads = 64 * NW;
+    constexpr int kRows = kWaveRows * NW;  // MFMA query rows per workgroup
     constexpr int QT = kRows / G;       // new tokens per workgroup
     constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
     constexpr int DT = D / 32;          // 32-row tiles of O^T
@@ -380,24 +384,46 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         }
 }
 
-template <int D, int G>
-hipError_t launch(const PrefillArgs& a, int total_q, hipStream_t st) {
-    constexpr int QT = kRows / G;
-    const long items = ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
-    if (items > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(unsigned(items)), dim3(kThreads), 0, st, a);
+template <int D, int G, int NW>
+hipError_t launch_nw(const PrefillArgs& a, long items, hipStream_t st) {
+    hipLaunchKernelGGL((prefill_kernel<D, G, NW>), dim3(unsigned(items)), dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
 
+// Eight-wavefront workgroups halve the K/V staging per query row; four-wavefront ones give twice as
+// many workgroups, which shortens the tail of a small launch (its longest causal rows).  Eight are
+// used once a launch has at least two workgroups per CU of them.
+template <int D, int G>
+hipError_t launch(const PrefillArgs& a, int total_q, int num_cus, hipStream_t st) {
+    constexpr int QT8 = 8 * kWaveRows / G, QT4 = 4 * kWaveRows / G;
+    const long items8 = ((long(total_q) + QT8 - 1) / QT8 + a.B) * a.num_kv_heads;
+    const long items4 = ((long(total_q) + QT4 - 1) / QT4 + a.B) * a.num_kv_heads;
+    if (items4 > INT32_MAX) return hipErrorInvalidValue;
+    return items8 >= 2L * num_cus ? launch_nw<D, G, 8>(a, items8, st) : launch_nw<D, G, 4>(a, items4, st);
+}
+
 template <int D>
-hipError_t launch_g(const PrefillArgs& a, int total_q, int G, hipStream_t st) {
+hipError_t launch_g(const PrefillArgs& a, int total_q, int G, int num_cus, hipStream_t st) {
     switch (G) {
-        case 1: return launch<D, 1>(a, total_q, st);
-        case 2: return launch<D, 2>(a, total_q, st);
-        case 4: return launch<D, 4>(a, total_q, st);
-        case 8: return launch<D, 8>(a, total_q, st);
+        case 1: return launch<D, 1>(a, total_q, num_cus, st);
+        case 2: return launch<D, 2>(a, total_q, num_cus, st);
+        case 4: return launch<D, 4>(a, total_q, num_cus, st);
+        case 8: return launch<D, 8>(a, total_q, num_cus, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+// compute units of the current device (queried once per device)
+int current_num_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
 }  // namespace
@@ -446,7 +472,8 @@ extern "C" int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q,
     a.causal = causal != 0;
     a.scale_log2 = softmax_scale * kLog2e;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, st) : launch_g<128>(a, total_q, G, st);
+    const int cus = current_num_cus();
+    const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, st) : launch_g<128>(a, total_q, G, cus, st);
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }

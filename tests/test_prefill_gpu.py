@@ -41,6 +41,20 @@ def test_prefill_short_and_single_token_prompts():
     check_tol(got, ref, "bf16", "prefill short prompts")
 
 
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_prefill_wide_workgroups(D, causal):
+    """One chunk of ~8K new tokens with ragged tails: enough query tiles that the kernel runs with
+    eight-wavefront workgroups (at least two per CU of them)."""
+    import torch
+    lens = [1000, 1100, 900, 1050, 1023, 977, 1100, 1040]
+    cfg = W.config("prefill_prefix", B=8, ctx=lens, D=D, group=1, shared=0, chunk=9000)
+    qt8 = 8 * 32 // (cfg["Hq"] // cfg["Hkv"])
+    items8 = (-(-sum(lens) // qt8) + cfg["B"]) * cfg["Hkv"]
+    assert items8 >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    got, ref, _ = _run(cfg, causal=causal)
+    check_tol(got, ref, "bf16", f"prefill wide workgroups D={D} causal={causal}")
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_prefill_full_workload(seed):
     """The full 32-prompt workload: chunks of at most 4096 new tokens, groups of 8 sharing 512 tokens."""
