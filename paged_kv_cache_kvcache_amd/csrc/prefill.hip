@@ -172,6 +172,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     const int pw_max = __builtin_amdgcn_readfirstlane(pw);
     const int pw_min = __builtin_amdgcn_readfirstlane(pm);
 
+    // ---- this sequence's block table, 64 entries at a time: lane i holds entry 64 win + i, and a
+    // tile reads its physical block with readlane (no memory access per tile).  The first window
+    // is requested here, ahead of the Q loads, so the two latencies overlap.
+    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    int bt_win = 0;
+    int btv = lane < a.max_blocks ? bt[lane] : 0;
+    auto phys_block = [&](int blk) {  // blk is uniform
+        const int win = blk >> 6;
+        if (win != bt_win) {  // a new window every 16384 keys
+            bt_win = win;
+            const int e = 64 * win + lane;
+            btv = e < a.max_blocks ? bt[e] : 0;
+        }
+        return __builtin_amdgcn_readlane(btv, blk & 63);
+    };
+
     // ---- Q^T operand: column col = query row, 8 consecutive d per k-step.  Q is multiplied by
     // softmax_scale * log2(e) (fp32, rounded once to bf16), so S comes out in log2 units.
     bf16x8_t qb[KS];
@@ -190,7 +206,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         }
     }
 
-    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
     const size_t head_off = size_t(g) * pkv::kBlock;
 
     // ---- global -> LDS DMA of one K/V tile.  Instruction r of wavefront w fills LDS bytes
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     }
     auto dma = [&](int kt, char* stage) {
         const int key0 = kt * kKT;
-        const int64_t phys = bt[key0 / pkv::kBlock];
+        const int64_t phys = phys_block(key0 / pkv::kBlock);
         const size_t row0 = (size_t(phys) * a.num_kv_heads) * pkv::kBlock + head_off + key0 % pkv::kBlock;
         const char* kg = a.k_cache + row0 * RB;
         const char* vg = a.v_cache + row0 * RB;
