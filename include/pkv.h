@@ -172,7 +172,9 @@ int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const void* v_ne
  * §8: more splits for throughput at some latency cost).
  *
  * pkv_decode_plan: the split count and split width the decode call will use for this
- * shape.  max_splits = 0 picks automatically; > 0 caps the split count.
+ * shape.  max_splits = 0 picks automatically (split only until there are two workgroups per
+ * CU of the current device; 256 CUs are assumed when no device is visible); > 0 caps the
+ * split count.
  * pkv_decode_workspace_bytes: device workspace the decode call needs (0 when the
  * plan has a single split).
  * ------------------------------------------------------------------------------------------ */

@@ -445,7 +445,19 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------ planning
-constexpr int kTargetWorkgroups = 2048;  // about 8 per CU on 256 CUs
+// Automatic plan: split only until the launch has two workgroups per CU.  Measured on MI355X, a
+// launch that already fills the chip twice over (e.g. 64 long sequences x 8 KV heads) runs fastest
+// unsplit: splits add partial-state traffic and a second launch, and the longest-first order
+// already balances the tail.
+int num_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();  // no device here: plan for MI355X's 256 CUs
+        return 256;
+    }
+    return n;
+}
 
 void plan(int B, int Hkv, int max_ctx, int max_splits, int* splits, int* bps) {
     const int nblk = std::max(1, (max_ctx + pkv::kBlock - 1) / pkv::kBlock);
@@ -453,8 +465,9 @@ void plan(int B, int Hkv, int max_ctx, int max_splits, int* splits, int* bps) {
     if (max_splits > 0) {
         S = std::min(max_splits, nblk);
     } else {
-        const long base = long(B) * Hkv;
-        S = int(std::min<long>(nblk, std::max<long>(1, (kTargetWorkgroups + base - 1) / base)));
+        const long base = std::max(1L, long(B) * Hkv);
+        const long target = 2L * num_cus();
+        S = int(std::min<long>(nblk, std::max<long>(1, (target + base - 1) / base)));
     }
     *bps = (nblk + S - 1) / S;
     *splits = (nblk + *bps - 1) / *bps;

@@ -102,9 +102,10 @@ def test_decode_plan():
     assert P.decode_plan(4, 2, 600, 2) == (2, 2)
     assert P.decode_plan(4, 2, 600, 9) == (3, 1)       # at most one split per block
     assert P.decode_plan(4, 2, 0, 0) == (1, 1)
-    s, bps = P.decode_plan(64, 8, 8192, 0)             # few workgroups: split the long contexts
-    assert s > 1 and s * bps >= 32 and (s - 1) * bps < 32
-    assert P.decode_plan(256, 8, 2048, 0)[0] == 1       # 2048 workgroups already
+    s, bps = P.decode_plan(16, 8, 8192, 0)             # 128 workgroups: split the long contexts
+    assert s == 4 and s * bps >= 32 and (s - 1) * bps < 32   # up to 2 per CU of 256 CUs
+    assert P.decode_plan(64, 8, 8192, 0)[0] == 1        # 512 workgroups already fill 256 CUs twice
+    assert P.decode_plan(256, 8, 2048, 0)[0] == 1
     assert P.decode_workspace_bytes(256, 16, 128, 8, 2048, 0) == 0
 
 
