@@ -188,24 +188,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         return __builtin_amdgcn_readlane(btv, blk & 63);
     };
 
-    // ---- Q^T operand: column col = query row, 8 consecutive d per k-step.  Q is multiplied by
-    // softmax_scale * log2(e) (fp32, rounded once to bf16), so S comes out in log2 units.
-    bf16x8_t qb[KS];
-    {
-        const int tq = min(t, nqt - 1);
-        const uint16_t* qp = a.q + (size_t(qrow0 + q0 + tq) * a.num_q_heads + g * G + j) * D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 v = col_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-            uint32_t* u = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                u[e] = pack_bf16x2(__uint_as_float(u[e] << 16) * a.scale_log2,
-                                   __uint_as_float(u[e] & 0xffff0000u) * a.scale_log2);
-            qb[ks] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-
     const size_t head_off = size_t(g) * pkv::kBlock;
 
     // ---- global -> LDS DMA of one K/V tile.  Instruction r of wavefront w fills LDS bytes
@@ -264,6 +246,26 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     float m_run = kNegInf, l_run = 0.f;
 
     if (ntiles > 0) dma(0, lds[0]);
+
+    // ---- Q^T operand: column col = query row, 8 consecutive d per k-step.  Q is multiplied by
+    // softmax_scale * log2(e) (fp32, rounded once to bf16), so S comes out in log2 units.  Loaded
+    // once the first tile's DMA is in flight, so the two latencies overlap.
+    bf16x8_t qb[KS];
+    {
+        const int tq = min(t, nqt - 1);
+        const uint16_t* qp = a.q + (size_t(qrow0 + q0 + tq) * a.num_q_heads + g * G + j) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 v = col_ok ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+            uint32_t* u = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                u[e] = pack_bf16x2(__uint_as_float(u[e] << 16) * a.scale_log2,
+                                   __uint_as_float(u[e] & 0xffff0000u) * a.scale_log2);
+            qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    }
+
     // One step per key tile: wait for its DMA, barrier (the other stage is then free: every
     // wavefront finished the previous tile), launch the next tile's DMA, compute.  The step is
     // instantiated for each LDS stage so that every LDS address offset is an immediate.
