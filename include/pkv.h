@@ -200,6 +200,26 @@ int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, 
                           int32_t max_context_len, int32_t max_splits, float softmax_scale,
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_decode_store_attend: one decode step's store and attention in one launch -- the
+ * engine's store_kvcache write of each step's new token followed by attention over the cache
+ * ("Nano-vLLM性能调优实战", §2.2 缓存复用策略), fused.
+ * k_new, v_new: device [B][num_kv_heads][head_dim] in the cache dtype, row b the new token
+ * of sequence b; k_scale_new, v_scale_new: int8 caches only, device float[B][num_kv_heads],
+ * written as the scale of the token's (block, head) as pkv_kv_store does; slot_mapping:
+ * device int32[B], the new token's slot, which must be the slot of position
+ * context_lens[b] - 1 of sequence b in block_tables (-1: nothing stored for b).  The store
+ * happens before any read of that block, by the one workgroup that reads it.  All other
+ * arguments and rules are those of pkv_paged_attn_decode; k_cache, v_cache, k_scale and
+ * v_scale are written.  The result equals pkv_kv_store followed by pkv_paged_attn_decode. */
+int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                            const void* k_new, const void* v_new, const float* k_scale_new,
+                            const float* v_scale_new, const int32_t* slot_mapping, void* k_cache,
+                            void* v_cache, float* k_scale, float* v_scale,
+                            const int32_t* block_tables, int32_t max_blocks,
+                            const int32_t* context_lens, const int32_t* seq_order,
+                            int32_t max_context_len, int32_t max_splits, float softmax_scale,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation).
  *

@@ -61,6 +61,8 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _f32, _vp, _vp, _sz, _vp]),
+    "pkv_decode_store_attend": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i32, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attn_prefill": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                       _f32, _i32, _vp, _vp]),
 }
@@ -244,6 +246,29 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
                                        _ptr(context_lens), _ptr(seq_order), int(max_context_len), int(max_splits),
                                        float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "pkv_paged_attn_decode")
+    return out
+
+
+def decode_store_attend(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                        softmax_scale, out=None, workspace=None, max_splits=0, k_scale=None, v_scale=None,
+                        k_scale_new=None, v_scale_new=None, seq_order=None, stream=None):
+    """One decode step's store of each sequence's new token (k_new/v_new [B][Hkv][D] in the cache
+    dtype, slot_mapping [B]) and its attention, in one launch; otherwise as :func:`paged_attn_decode`."""
+    desc = desc_of(k_cache)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, D, desc.num_kv_heads, max_context_len, max_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_decode_store_attend(ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_new), _ptr(v_new),
+                                         _ptr(k_scale_new), _ptr(v_scale_new), _ptr(slot_mapping), _ptr(k_cache),
+                                         _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                         int(block_tables.shape[1]), _ptr(context_lens), _ptr(seq_order),
+                                         int(max_context_len), int(max_splits), float(softmax_scale), _ptr(out),
+                                         _ptr(workspace), ws_bytes, _stream(stream)),
+           "pkv_decode_store_attend")
     return out
 
 

@@ -225,6 +225,16 @@ struct DecodeArgs {
     void* out;
     float* ws_acc;  // [B][Hq][S][D]
     float* ws_ml;   // [B][Hq][S][2]  (max in log2 units, denominator)
+    // optional store of each sequence's new token before attending (pkv_decode_store_attend)
+    const int32_t* new_slots;  // [B], -1: nothing to store
+    const char* k_new;         // [B][Hkv][D] in the cache dtype
+    const char* v_new;
+    const float* k_scale_new;  // int8: [B][Hkv]
+    const float* v_scale_new;
+    char* k_store;             // writable views of the caches and (int8) scales
+    char* v_store;
+    float* k_scale_store;
+    float* v_scale_store;
     int32_t max_blocks;
     int32_t num_kv_heads;
     int32_t num_q_heads;
@@ -246,6 +256,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int blk0 = s * a.blocks_per_split;
     const int blk1 = min(nblk, blk0 + a.blocks_per_split);
     if (a.splits > 1 && blk0 >= blk1) return;  // empty split: the reduce kernel skips it
+
+    // ---- the new token of this sequence (position ctx - 1), stored by the workgroup whose split
+    // holds its block before any wavefront reads that block; no other workgroup reads it
+    if (a.new_slots != nullptr) {
+        const int bn = (ctx - 1) / pkv::kBlock;
+        const int slot = ctx > 0 && bn >= blk0 && bn < blk1 ? a.new_slots[b] : -1;
+        if (slot >= 0) {
+            const int64_t pblk = slot / pkv::kBlock, off = slot % pkv::kBlock;
+            const size_t dst = ((size_t(pblk) * a.num_kv_heads + g) * pkv::kBlock + off) * RB;
+            const size_t src = (size_t(b) * a.num_kv_heads + g) * RB;
+            constexpr int NP = RB / 16;  // 16-byte pieces per row
+            for (int p = threadIdx.x; p < 2 * NP; p += kThreads) {
+                const bool is_v = p >= NP;
+                const int pp = is_v ? p - NP : p;
+                const uint4 val = reinterpret_cast<const uint4*>((is_v ? a.v_new : a.k_new) + src)[pp];
+                reinterpret_cast<uint4*>((is_v ? a.v_store : a.k_store) + dst)[pp] = val;
+            }
+            if constexpr (DT == PKV_I8) {
+                if (threadIdx.x == 0) {
+                    a.k_scale_store[pblk * a.num_kv_heads + g] = a.k_scale_new[size_t(b) * a.num_kv_heads + g];
+                    a.v_scale_store[pblk * a.num_kv_heads + g] = a.v_scale_new[size_t(b) * a.num_kv_heads + g];
+                }
+            }
+        }
+        __syncthreads();  // the stores are complete before any wavefront loads the block
+    }
 
     // the wavefront index is uniform per wavefront: keep it (and the loop bounds) in scalar registers
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -520,12 +556,25 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head
     return size_t(B) * Hq * S * (size_t(head_dim) + 2) * sizeof(float);
 }
 
-extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
-                                     const void* k_cache, const void* v_cache, const float* k_scale,
-                                     const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
-                                     const int32_t* context_lens, const int32_t* seq_order,
-                                     int32_t max_context_len, int32_t max_splits, float softmax_scale, void* out,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+struct NewTokens {
+    const void* k_new = nullptr;
+    const void* v_new = nullptr;
+    const float* k_scale_new = nullptr;
+    const float* v_scale_new = nullptr;
+    const int32_t* slot_mapping = nullptr;
+    void* k_cache = nullptr;
+    void* v_cache = nullptr;
+    float* k_scale = nullptr;
+    float* v_scale = nullptr;
+};
+
+int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq, const void* k_cache,
+                const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                int32_t max_blocks, const int32_t* context_lens, const int32_t* seq_order, int32_t max_context_len,
+                int32_t max_splits, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                const NewTokens* nt, void* stream) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     const int Hkv = desc->num_kv_heads, D = desc->head_dim;
@@ -543,10 +592,18 @@ extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, 
     const bool i8 = desc->kv_dtype == PKV_I8;
     PKV_REQUIRE(i8 == (k_scale != nullptr) && i8 == (v_scale != nullptr), PKV_ERR_INVALID,
                 "k_scale / v_scale are required for int8 caches and rejected otherwise");
+    if (nt != nullptr) {
+        PKV_REQUIRE(i8 == (nt->k_scale_new != nullptr) && i8 == (nt->v_scale_new != nullptr), PKV_ERR_INVALID,
+                    "k_scale_new / v_scale_new are required for int8 caches and rejected otherwise");
+    }
     if (B == 0) return PKV_OK;
     PKV_REQUIRE(q && k_cache && v_cache && block_tables && context_lens && out, PKV_ERR_INVALID, "NULL pointer");
-    const uintptr_t mis = uintptr_t(q) | uintptr_t(k_cache) | uintptr_t(v_cache) | uintptr_t(out);
-    PKV_REQUIRE((mis & 15) == 0, PKV_ERR_INVALID, "q, caches and out must be 16-byte aligned");
+    uintptr_t mis = uintptr_t(q) | uintptr_t(k_cache) | uintptr_t(v_cache) | uintptr_t(out);
+    if (nt != nullptr) {
+        PKV_REQUIRE(nt->k_new && nt->v_new && nt->slot_mapping, PKV_ERR_INVALID, "NULL new-token pointer");
+        mis |= uintptr_t(nt->k_new) | uintptr_t(nt->v_new);
+    }
+    PKV_REQUIRE((mis & 15) == 0, PKV_ERR_INVALID, "q, caches, new rows and out must be 16-byte aligned");
 
     DecodeArgs a{};
     a.q = q;
@@ -562,6 +619,17 @@ extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, 
     a.num_kv_heads = Hkv;
     a.num_q_heads = Hq;
     a.scale_log2 = softmax_scale * kLog2e;
+    if (nt != nullptr) {
+        a.new_slots = nt->slot_mapping;
+        a.k_new = static_cast<const char*>(nt->k_new);
+        a.v_new = static_cast<const char*>(nt->v_new);
+        a.k_scale_new = nt->k_scale_new;
+        a.v_scale_new = nt->v_scale_new;
+        a.k_store = static_cast<char*>(nt->k_cache);
+        a.v_store = static_cast<char*>(nt->v_cache);
+        a.k_scale_store = nt->k_scale;
+        a.v_scale_store = nt->v_scale;
+    }
     plan(B, Hkv, max_context_len, max_splits, &a.splits, &a.blocks_per_split);
     if (a.splits > 1) {
         const size_t need = size_t(B) * Hq * a.splits * (size_t(D) + 2) * sizeof(float);
@@ -580,4 +648,39 @@ extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, 
     }
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                     const void* k_cache, const void* v_cache, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                                     const int32_t* context_lens, const int32_t* seq_order,
+                                     int32_t max_context_len, int32_t max_splits, float softmax_scale, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
+                       seq_order, max_context_len, max_splits, softmax_scale, out, workspace, workspace_bytes,
+                       nullptr, stream);
+}
+
+extern "C" int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                       const void* k_new, const void* v_new, const float* k_scale_new,
+                                       const float* v_scale_new, const int32_t* slot_mapping, void* k_cache,
+                                       void* v_cache, float* k_scale, float* v_scale, const int32_t* block_tables,
+                                       int32_t max_blocks, const int32_t* context_lens, const int32_t* seq_order,
+                                       int32_t max_context_len, int32_t max_splits, float softmax_scale, void* out,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    NewTokens nt;
+    nt.k_new = k_new;
+    nt.v_new = v_new;
+    nt.k_scale_new = k_scale_new;
+    nt.v_scale_new = v_scale_new;
+    nt.slot_mapping = slot_mapping;
+    nt.k_cache = k_cache;
+    nt.v_cache = v_cache;
+    nt.k_scale = k_scale;
+    nt.v_scale = v_scale;
+    return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
+                       seq_order, max_context_len, max_splits, softmax_scale, out, workspace, workspace_bytes, &nt,
+                       stream);
 }

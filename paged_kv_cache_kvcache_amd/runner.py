@@ -9,8 +9,8 @@ libpkv; this module only moves arrays.
 import numpy as np
 import torch
 
-from . import (BF16, BLOCK, F32, I8, Allocator, decode_workspace_bytes, kv_store, paged_attn_decode,
-               paged_attn_prefill)
+from . import (BF16, BLOCK, F32, I8, Allocator, decode_store_attend, decode_workspace_bytes, kv_store,
+               paged_attn_decode, paged_attn_prefill)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 
@@ -54,9 +54,10 @@ class PagedKV:
 
 
 class DecodeBatch:
-    """A batch of sequences in decode: history admitted and stored, then one token per step."""
+    """A batch of sequences in decode: history admitted and stored, then one token per step
+    (``fused``: the step's store and attention in one launch, pkv_decode_store_attend)."""
 
-    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0):
+    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False):
         self.kv = kv
         self.Hq = int(Hq)
         self.ids = np.asarray(seq_ids, dtype=np.int64)
@@ -64,6 +65,7 @@ class DecodeBatch:
         self.max_blocks = max(1, -(-int(max_context_len) // BLOCK))
         self.max_context_len = int(max_context_len)
         self.max_splits = max_splits
+        self.fused = fused
         dev = kv.device
         # pinned staging for the per-step metadata: slots[B] | lens[B] | order[B] | tables[B][max_blocks]
         self._pin = torch.empty(3 * self.B + self.B * self.max_blocks, dtype=torch.int32).pin_memory()
@@ -94,14 +96,25 @@ class DecodeBatch:
         """One decode step: append one token per sequence, store its K/V, attend.  Returns out [B][Hq][D]."""
         slots = self.kv.alloc.append_batch(self.ids, tokens)
         self.upload_step_metadata(slots)
+        if self.fused:
+            return self.store_attend(q, k_new, v_new, softmax_scale, out, k_scale_new, v_scale_new)
         self.kv.store(self.slots, k_new, v_new, k_scale_new, v_scale_new)
         return self.attend(q, softmax_scale, out)
 
+    def store_attend(self, q, k_new, v_new, softmax_scale, out=None, k_scale_new=None, v_scale_new=None):
+        """The step's store of the new tokens and its attention, in one launch."""
+        kv = self.kv
+        return decode_store_attend(q, k_new, v_new, self.slots, kv.k_cache, kv.v_cache, self.block_tables,
+                                  self.context_lens, self.max_context_len, softmax_scale, out=out,
+                                  workspace=self.workspace, max_splits=self.max_splits, k_scale=kv.k_scale,
+                                  v_scale=kv.v_scale, k_scale_new=k_scale_new, v_scale_new=v_scale_new,
+                                  seq_order=self.seq_order)
+
     def attend(self, q, softmax_scale, out=None):
         return paged_attn_decode(q, self.kv.k_cache, self.kv.v_cache, self.block_tables, self.context_lens,
-                                 self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
-                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale,
-                                 seq_order=self.seq_order)
+                                self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
+                                max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale,
+                                seq_order=self.seq_order)
 
 
 def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None, v_scale_rows=None):

@@ -89,6 +89,20 @@ def test_decode_rejects_bad_arguments():
     assert _decode(d, B=0) == P.OK
 
 
+def test_fused_store_decode_rejects_bad_arguments():
+    d = _desc()
+    i8 = _desc(kv_dtype=P.I8)
+
+    def call(desc, k_new=FAKE, slots=FAKE, ksn=None, vsn=None, ks=None, vs=None):
+        return P.lib().pkv_decode_store_attend(ctypes.byref(desc), FAKE, 2, 4, k_new, FAKE, ksn, vsn, slots, FAKE,
+                                               FAKE, ks, vs, FAKE, 3, FAKE, None, 600, 0, 0.125, FAKE, None, 0, None)
+    assert call(d, k_new=None) == P.ERR_INVALID                  # new rows required
+    assert call(d, slots=None) == P.ERR_INVALID                  # slots required
+    assert call(d, k_new=ctypes.c_void_p((1 << 20) + 4)) == P.ERR_INVALID  # misaligned rows
+    assert call(d, ksn=FAKE, vsn=FAKE) == P.ERR_INVALID          # scales on a float cache
+    assert call(i8, ks=FAKE, vs=FAKE) == P.ERR_INVALID           # int8 without the new tokens' scales
+
+
 def test_decode_needs_its_workspace():
     d = _desc()
     need = P.decode_workspace_bytes(2, 4, 64, 2, 600, 3)

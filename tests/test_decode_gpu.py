@@ -115,6 +115,23 @@ def test_decode_matches_oracle(gpu, name, max_splits):
     check_tol(host_out(out), _oracle(name, 0, wl), cfg["dtype"], f"{name}/splits={max_splits}")
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("max_splits", [0, 3])
+def test_fused_store_equals_store_then_attend(gpu, name, max_splits):
+    """pkv_decode_store_attend leaves the same cache (rows and int8 scales) and the same output,
+    bit for bit, as pkv_kv_store followed by pkv_paged_attn_decode."""
+    cfg = _cfg(name)
+    wl = W.decode_workload(cfg, 0)
+    fill = float("nan") if cfg["dtype"] != "i8" else -128  # rows nobody writes compare equal too
+    a, kva, _ = gpu_decode(wl, gpu, max_splits=max_splits, fill=fill, fused=True)
+    b, kvb, _ = gpu_decode(wl, gpu, max_splits=max_splits, fill=fill, fused=False)
+    bits = lambda t: t.contiguous().view(torch.uint8)
+    assert torch.equal(bits(a), bits(b))
+    assert torch.equal(bits(kva.k_cache), bits(kvb.k_cache)) and torch.equal(bits(kva.v_cache), bits(kvb.v_cache))
+    if cfg["dtype"] == "i8":
+        assert torch.equal(bits(kva.k_scale), bits(kvb.k_scale)) and torch.equal(bits(kva.v_scale), bits(kvb.v_scale))
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_decode_other_seeds(gpu, seed):
     cfg = _cfg("qwen3_decode")
