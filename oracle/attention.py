@@ -70,6 +70,61 @@ def kv_store(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale=None, v_scale
     return k_cache, v_cache
 
 
+def _int8_codes(x, scale):
+    """clamp(rint(x / scale), -127, 127) with the quotient in float64, ties to even; scale 0 -> 0."""
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.int8)
+    return np.clip(np.rint(x / float(scale)), -127, 127).astype(np.int8)
+
+
+def kv_store_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slot_mapping):
+    """Quantising store_kvcache into int8 caches (INT8 KV is an engine option: intelliparadigm.com
+    Nano-vLLM article, §2.2 混合精度计算流水线; the pages give no encoding, so the rule below is a
+    reading).
+
+    One fp32 scale per (physical block, KV head).  The new rows of one call that land in the same
+    block form a run of consecutive slots (this is what the allocator hands out for a prompt's
+    tokens and for a decode append).  For a run starting at offset o0 of block b, per KV head and
+    separately for K and V:
+
+    * candidate = absmax of the run's new values / 127, the quotient in float64 rounded to float32;
+    * old = the block's scale if o0 > 0 (rows 0..o0-1 hold earlier codes), else 0 (a fresh block);
+    * new = max(old, candidate); if new > old the earlier rows are re-quantised,
+      code -> rint(code * old / new) (float64, ties to even);
+    * the run's rows become clamp(rint(x / new), -127, 127) (float64 quotient, ties to even), all
+      zero when new == 0, and the block's scale becomes new.
+
+    Rows with slot < 0 are skipped.  Inputs are the float values (bf16-representable or float32);
+    returns new (k_cache, v_cache, k_scale, v_scale).
+    """
+    kc, vc = k_cache.copy(), v_cache.copy()
+    ks, vs = k_scale.copy(), v_scale.copy()
+    slots = [int(x) for x in slot_mapping]
+    n = len(slots)
+    t = 0
+    while t < n:
+        if slots[t] < 0:
+            t += 1
+            continue
+        blk, o0 = divmod(slots[t], BLOCK)
+        t1 = t + 1
+        while t1 < n and slots[t1] == slots[t] + (t1 - t) and o0 + (t1 - t) < BLOCK:
+            t1 += 1
+        for cache, scale, new in ((kc, ks, k_new), (vc, vs, v_new)):
+            for g in range(cache.shape[1]):
+                x = np.asarray(new[t:t1, g], dtype=np.float64)
+                cand = np.float32(np.abs(x).max() / 127.0)
+                old = np.float32(scale[blk, g]) if o0 > 0 else np.float32(0.0)
+                s_new = max(old, cand)
+                if o0 > 0 and s_new > old:
+                    c = cache[blk, g, :o0].astype(np.float64)
+                    cache[blk, g, :o0] = np.clip(np.rint(c * float(old) / float(s_new)), -127, 127).astype(np.int8)
+                cache[blk, g, o0:o0 + (t1 - t)] = _int8_codes(x, s_new)
+                scale[blk, g] = s_new
+        t = t1
+    return kc, vc, ks, vs
+
+
 def gather(cache, table_row, length, head, scale=None):
     """Rows 0..length-1 of one sequence for one KV head, as float64 ``[length][D]``."""
     rows = np.empty((length, cache.shape[-1]), dtype=np.float64)

@@ -11,6 +11,7 @@
 import math
 import os
 import random
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -21,6 +22,7 @@ from oracle import allocator as OA
 from oracle import attention as OT
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BLOCK = 256
 
 
 # ----------------------------------------------------------------------------- hash
@@ -466,6 +468,149 @@ def test_shared_prefix_outputs_identical_and_prefix_cache_transparent():
     for i in (1, 2):
         n = cu[i + 1] - cu[i]
         assert np.allclose(out1[cu1[i]:cu1[i + 1]], out[cu[i] + 512:cu[i] + n], atol=1e-13, rtol=0)
+
+
+# ------------------------------------------------------------------- int8 quantising store
+def _golden_int8_store():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "int8_store.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, *xs = line.split()
+            vals[name] = [float(x) for x in xs]
+    return vals
+
+
+def _quant_cache(nb, hkv, d):
+    return (np.zeros((nb, hkv, BLOCK, d), dtype=np.int8), np.zeros((nb, hkv, BLOCK, d), dtype=np.int8),
+            np.zeros((nb, hkv), dtype=np.float32), np.zeros((nb, hkv), dtype=np.float32))
+
+
+def test_int8_store_hand_example():
+    g = _golden_int8_store()
+    kc, vc, ks, vs = _quant_cache(1, 1, 2)
+    for c in (1, 2, 3):
+        off = int(g[f"call{c}_offset"][0])
+        rows = np.array(g[f"call{c}_rows"], dtype=np.float32).reshape(-1, 1, 2)
+        slots = np.arange(off, off + rows.shape[0])
+        kc, vc, ks, vs = OT.kv_store_quant(kc, vc, ks, vs, rows, -rows, slots)
+        codes = np.array(g[f"call{c}_codes"], dtype=np.int8).reshape(-1, 2)
+        m, e = g[f"call{c}_scale"]
+        assert ks[0, 0] == np.float32(math.ldexp(m, int(e))) and vs[0, 0] == ks[0, 0]
+        assert np.array_equal(kc[0, 0, :codes.shape[0]], codes)
+        assert np.array_equal(vc[0, 0, :codes.shape[0]], -codes)  # V took the negated rows
+
+
+def _rint_even(fr):
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem != Fraction(1, 2):
+        return fl + (1 if rem > Fraction(1, 2) else 0)
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def _store_quant_exact(cache, scale, new, slots):
+    """The quantising store in exact rational arithmetic, pure Python (no NumPy arithmetic):
+    quotients are exact and rounded half to even; the scale is absmax/127 rounded to fp64 and
+    then to fp32, as the rule states."""
+    n = len(slots)
+    t = 0
+    while t < n:
+        if slots[t] < 0:
+            t += 1
+            continue
+        blk, o0 = divmod(slots[t], BLOCK)
+        t1 = t + 1
+        while t1 < n and slots[t1] == slots[t] + (t1 - t) and o0 + (t1 - t) < BLOCK:
+            t1 += 1
+        for h in range(len(scale[blk])):
+            amax = max(abs(Fraction(float(new[r][h][d]))) for r in range(t, t1) for d in range(len(new[r][h])))
+            cand = Fraction(float(np.float32(float(amax / 127))))
+            old = Fraction(float(scale[blk][h])) if o0 > 0 else Fraction(0)
+            s_new = max(old, cand)
+            if o0 > 0 and s_new > old:
+                for r in range(o0):
+                    cache[blk][h][r] = [max(-127, min(127, _rint_even(c * old / s_new))) for c in cache[blk][h][r]]
+            for r in range(t, t1):
+                cache[blk][h][o0 + r - t] = [0 if s_new == 0 else max(-127, min(127, _rint_even(Fraction(float(x)) / s_new)))
+                                             for x in new[r][h]]
+            scale[blk][h] = float(s_new)
+        t = t1
+
+
+def test_int8_store_matches_exact_rational_brute_force():
+    rng = np.random.default_rng(7)
+    nb, hkv, d = 3, 2, 4
+    kc, vc, ks, vs = _quant_cache(nb, hkv, d)
+    ex_cache = [[[[0] * d for _ in range(BLOCK)] for _ in range(hkv)] for _ in range(nb)]
+    ex_scale = [[0.0] * hkv for _ in range(nb)]
+    # a prompt store (run from offset 0, a skipped row, a second block), then appends whose
+    # values sometimes raise the block's absmax, a zero row, and a store into a reused block
+    calls = [
+        [0, 1, 2, -1, 256, 257],
+        [3], [4], [258], [5], [6], [259],
+        [512, 513, 514, 515], [516], [0, 1],
+    ]
+    for i, slots in enumerate(calls):
+        x = rng.standard_normal((len(slots), hkv, d)).astype(np.float32) * np.float32(2.0 ** rng.integers(-3, 4))
+        x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+        if i == 4:
+            x[:] = 0.0
+        kc, vc, ks, vs = OT.kv_store_quant(kc, vc, ks, vs, x, x, np.array(slots))
+        _store_quant_exact(ex_cache, ex_scale, x.tolist(), slots)
+        assert np.array_equal(kc, np.array(ex_cache, dtype=np.int8)), f"call {i}"
+        assert np.array_equal(ks, np.array(ex_scale, dtype=np.float32)), f"call {i}"
+        assert np.array_equal(vc, kc) and np.array_equal(vs, ks)
+
+
+def test_int8_store_one_shot_bounds_and_full_code_range():
+    rng = np.random.default_rng(8)
+    kc, vc, ks, vs = _quant_cache(2, 3, 16)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((300, 3, 16)).astype(np.float32)))
+    x[256:, 2] = 0.0
+    slots = np.concatenate([np.arange(256, 512), np.arange(0, 44)])  # block 1 full, block 0 partial
+    kc, vc, ks, vs = OT.kv_store_quant(kc, vc, ks, vs, x, x * 3, slots)
+    for blk, (lo, hi) in ((1, (0, 256)), (0, (256, 300))):
+        for h in range(3):
+            for cache, scale, mul in ((kc, ks, 1), (vc, vs, 3)):
+                vals = x[lo:hi, h].astype(np.float64) * mul
+                s = float(scale[blk, h])
+                codes = cache[blk, h, :hi - lo].astype(np.float64)
+                if not vals.any():
+                    assert s == 0 and not codes.any()
+                    continue
+                assert s == np.float32(np.abs(vals).max() / 127.0)
+                assert np.abs(codes).max() == 127
+                assert np.abs(codes * s - vals).max() <= s / 2 * (1 + 1e-6)
+
+
+def test_int8_store_appends_that_keep_the_absmax_equal_one_shot():
+    rng = np.random.default_rng(9)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((40, 2, 8)).astype(np.float32)))
+    x[0, :, 0] = 8.0  # the first token holds every head's absmax, so no later append re-quantises
+    one = OT.kv_store_quant(*_quant_cache(1, 2, 8), x, x, np.arange(40))
+    inc = _quant_cache(1, 2, 8)
+    for t in range(40):
+        inc = OT.kv_store_quant(*inc, x[t:t + 1], x[t:t + 1], np.array([t]))
+    for a, b in zip(one, inc):
+        assert np.array_equal(a, b)
+
+
+def test_int8_store_requantises_by_the_scale_ratio_with_ties_to_even():
+    kc, vc, ks, vs = _quant_cache(1, 1, 8)
+    kc[0, 0, 0] = [1, 2, 3, -3, 5, -5, 127, -127]
+    ks[0, 0] = np.float32(0.5)
+    # a new row whose absmax is 127 gives scale 1.0 = twice the old one: codes halve, ties to even;
+    # the new row's own quotients x / 1.0 include exact ties too
+    row = np.array([[[127.0, 2.5, -2.5, 0.5, 1.5, -0.5, 3.5, 0.0]]], dtype=np.float32)
+    kc, vc, ks, vs = OT.kv_store_quant(kc, vc, ks, vs, row, row, np.array([1]))
+    assert ks[0, 0] == 1.0
+    assert list(kc[0, 0, 0]) == [0, 1, 2, -2, 2, -2, 64, -64]
+    assert list(kc[0, 0, 1]) == [127, 2, -2, 0, 2, 0, 4, 0]
+    # a store at offset 0 starts a fresh block: the old scale is ignored
+    small = np.zeros((1, 1, 8), dtype=np.float32)
+    small[0, 0, 0] = 1.0
+    kc, vc, ks, vs = OT.kv_store_quant(kc, vc, ks, vs, small, small, np.array([0]))
+    assert ks[0, 0] == np.float32(1.0 / 127.0) and kc[0, 0, 0, 0] == 127
 
 
 # ------------------------------------------------------------------------ generators

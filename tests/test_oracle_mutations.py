@@ -152,6 +152,48 @@ def _pop_keeps_hash(self):
     return b
 
 
+def _codes_half_away(x, scale):  # rint rounding half away from zero instead of half to even
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.int8)
+    q = x / float(scale)
+    return np.clip(np.sign(q) * np.floor(np.abs(q) + 0.5), -127, 127).astype(np.int8)
+
+
+def _codes_truncate(x, scale):  # truncation instead of rounding
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.int8)
+    return np.clip(np.trunc(x / float(scale)), -127, 127).astype(np.int8)
+
+
+def _store_quant_variant(requant=True, fresh_resets=True, keep_old=True):
+    def store(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slot_mapping):
+        kc, vc, ks, vs = k_cache.copy(), v_cache.copy(), k_scale.copy(), v_scale.copy()
+        slots = [int(x) for x in slot_mapping]
+        t = 0
+        while t < len(slots):
+            if slots[t] < 0:
+                t += 1
+                continue
+            blk, o0 = divmod(slots[t], BLOCK)
+            t1 = t + 1
+            while t1 < len(slots) and slots[t1] == slots[t] + (t1 - t) and o0 + (t1 - t) < BLOCK:
+                t1 += 1
+            for cache, scale, new in ((kc, ks, k_new), (vc, vs, v_new)):
+                for g in range(cache.shape[1]):
+                    x = np.asarray(new[t:t1, g], dtype=np.float64)
+                    cand = np.float32(np.abs(x).max() / 127.0)
+                    old = np.float32(scale[blk, g]) if (o0 > 0 or not fresh_resets) else np.float32(0.0)
+                    s_new = max(old, cand) if keep_old else cand
+                    if requant and o0 > 0 and s_new > old:
+                        c = cache[blk, g, :o0].astype(np.float64)
+                        cache[blk, g, :o0] = np.clip(np.rint(c * float(old) / float(s_new)), -127, 127).astype(np.int8)
+                    cache[blk, g, o0:o0 + (t1 - t)] = OT._int8_codes(x, s_new)
+                    scale[blk, g] = s_new
+            t = t1
+        return kc, vc, ks, vs
+    return store
+
+
 OT_attend_orig = OT.attend
 OT_gather_orig = OT.gather
 OA_block_hash_orig = OA.block_hash
@@ -175,6 +217,13 @@ ALLOC_PINS = [
     P.test_append_hashes_full_block_for_later_reuse,
     P.test_shared_prefix_outputs_identical_and_prefix_cache_transparent,
 ]
+QUANT_PINS = [
+    P.test_int8_store_hand_example,
+    P.test_int8_store_matches_exact_rational_brute_force,
+    P.test_int8_store_one_shot_bounds_and_full_code_range,
+    P.test_int8_store_appends_that_keep_the_absmax_equal_one_shot,
+    P.test_int8_store_requantises_by_the_scale_ratio_with_ties_to_even,
+]
 HASH_PINS = [lambda: [P.test_fnv1a64_published_vectors(d, e) for d, e in P._golden_fnv()],
              P.test_block_hash_closed_forms]
 
@@ -195,6 +244,12 @@ MUTANTS = {
     "free list popped LIFO": (OA.Allocator, "_pop_fresh", _pop_lifo, ALLOC_PINS),
     "free_seq in forward order": (OA.Allocator, "free_seq", _free_forward, ALLOC_PINS),
     "popped block keeps its hash": (OA.Allocator, "_pop_fresh", _pop_keeps_hash, ALLOC_PINS),
+    "int8 codes round half away from zero": (OT, "_int8_codes", _codes_half_away, QUANT_PINS),
+    "int8 codes truncate": (OT, "_int8_codes", _codes_truncate, QUANT_PINS),
+    "int8 store never re-quantises": (OT, "kv_store_quant", _store_quant_variant(requant=False), QUANT_PINS),
+    "int8 store keeps a fresh block's old scale": (OT, "kv_store_quant", _store_quant_variant(fresh_resets=False),
+                                                   QUANT_PINS),
+    "int8 scale from the new rows only": (OT, "kv_store_quant", _store_quant_variant(keep_old=False), QUANT_PINS),
 }
 
 
