@@ -375,6 +375,74 @@ def bench_prefill(args, cfg):
     return res
 
 
+# ------------------------------------------------------------------------- int8 quantising store
+def bench_int8_store(args, cfg):
+    """The prefill workload's new K/V rows (bf16) written by the quantising store into int8 caches:
+    one step = every chunk's store, in chunk order."""
+    import torch
+    import workloads as W
+    from paged_kv_cache_kvcache_amd import I8, store_runs
+    from paged_kv_cache_kvcache_amd import runner as R
+
+    dev = torch.device("cuda:0")
+    Hkv, D = cfg["Hkv"], cfg["D"]
+    wl = W.prefill_workload(cfg, args.seed)
+    prompts = wl["prompts"]
+    kv = R.PagedKV(wl["num_blocks"], Hkv, D, I8, wl["free_order"], device=dev)
+    ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+    n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
+    chunks = W.pack_chunks(n_new, cfg["chunk"])
+    dchunks, blocks = [], 0
+    for ch in chunks:
+        _, _, slots = kv.alloc.prefill_slots(ch, sum(n_new[i] for i in ch))
+        runs, n_runs, longest = store_runs(slots)
+        dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), dev)
+        dchunks.append(dict(k=dv("k"), v=dv("v"), slots=torch.from_numpy(np.ascontiguousarray(slots)).to(dev),
+                            runs=(torch.from_numpy(runs).to(dev), n_runs, longest)))
+        blocks += n_runs
+    total_new = sum(n_new)
+    # algorithmic bytes per step: bf16 rows read, int8 codes written, one fp32 scale per (block, head)
+    # written, for K and V
+    step_bytes = 2 * (total_new * Hkv * D * (2 + 1) + blocks * Hkv * 4)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def run(j=None):
+        if j is not None:
+            ev[j][0].record(stream)
+        for d in dchunks:
+            kv.store_quant(d["slots"], d["k"], d["v"], d["runs"])
+        if j is not None:
+            ev[j][1].record(stream)
+
+    gc.collect()
+    gc.disable()
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        run(j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gc.enable()
+    kern_s = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 1e3
+    gbs = step_bytes / kern_s / 1e9
+    log(f"[bench] int8 store: {len(dchunks)} chunks, {total_new} new tokens, {step_bytes / 1e6:.1f} MB; "
+        f"{kern_s * 1e6:.1f} us/step -> {gbs:.0f} GB/s")
+    return dict(
+        metric="int8 quantising store: stored tokens/s + HBM GB/s (% of peak)",
+        value=total_new * args.steps / elapsed, unit="stored tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=elapsed / args.steps * 1e3, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16->i8", data="synthetic",
+        config=dict(workload=cfg["name"], prompts=cfg["B"], new_tokens=total_new, kv_heads=Hkv, head_dim=D,
+                    block_size=256, chunks=len(dchunks), seed=args.seed),
+        store_kernel_us=kern_s * 1e6,
+        roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                      traffic=None, kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
+    )
+
+
 def cpu_baseline_prefill(wl, first=4):
     """The oracle's chunked prefill (its block manager, store, fp64 attention) on the first n prompts."""
     from threadpoolctl import threadpool_limits
@@ -427,6 +495,8 @@ def main():
     cfg = W.config(args.config)
     if cfg["kind"] == "decode":
         res = bench_decode(args, cfg)
+    elif cfg["kind"] == "store":
+        res = bench_int8_store(args, cfg)
     else:
         res = bench_prefill(args, cfg)
     print(json.dumps(res), flush=True)

@@ -163,6 +163,43 @@ int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const void* v_ne
                  float* k_scale, float* v_scale, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Quantising store into int8 caches.  The pages name INT8 KV as an engine option
+ * (intelliparadigm.com Nano-vLLM article, §2.2 混合精度计算流水线) and give no encoding;
+ * this one keeps one fp32 scale per (physical block, KV head), k_scale / v_scale
+ * [num_blocks][num_kv_heads], and a code c stands for c * scale.
+ *
+ * The new rows of one call that land in one block must form one run of consecutive batch
+ * rows with consecutive slots (as pkv_alloc_prefill_slots and decode appends produce); a run
+ * starting at offset o0 > 0 of its block treats rows 0..o0-1 of that block and the block's
+ * scale as earlier output of this function.  Per run, KV head, and K / V separately:
+ *   candidate = absmax of the run's values / 127 (fp64 quotient rounded to fp32);
+ *   old = the block's scale if o0 > 0, else 0;  new = max(old, candidate);
+ *   if new > old the rows 0..o0-1 are re-quantised: code = rint(code * old / new);
+ *   the run's rows become clamp(rint(x / new), -127, 127) (all 0 when new == 0);
+ *   the block's scale becomes new.
+ * rint rounds the exact quotient half to even.  Rows with slot < 0 are skipped.
+ *
+ * k_new, v_new: device [n][num_kv_heads][head_dim] of new_dtype (PKV_BF16 or PKV_F32),
+ * finite values; slot_mapping: device int32[n]; runs: device int32[2 * n_runs], the runs of
+ * slot_mapping as pkv_store_runs gives them (first row, length); max_run: host, the longest
+ * run's length (1..256; it selects the launch shape); k_cache, v_cache: device int8 caches
+ * (desc->kv_dtype must be PKV_I8); k_scale, v_scale: device fp32 [num_blocks][num_kv_heads].
+ * Two runs in one call must not share a block (the result is then undefined).  n_runs may be 0.
+ * ------------------------------------------------------------------------------------------ */
+int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
+                       int32_t new_dtype, const int32_t* slot_mapping, int32_t n, const int32_t* runs,
+                       int32_t n_runs, int32_t max_run, void* k_cache, void* v_cache, float* k_scale,
+                       float* v_scale, void* stream);
+
+/* The runs of a slot mapping for pkv_kv_store_quant (host): maximal groups of consecutive batch
+ * rows whose slots are consecutive and in one block; rows with slot < 0 belong to none.
+ * slot_mapping: host int32[n]; runs: host int32[2 * cap], filled with (first row, length) per
+ * run in batch order; *n_runs = the number of runs, *max_run = the longest (0 when none).
+ * PKV_ERR_SMALL_BUFFER when there are more than cap runs (cap = n always suffices). */
+int pkv_store_runs(const int32_t* slot_mapping, int32_t n, int32_t* runs, int32_t cap,
+                   int32_t* n_runs, int32_t* max_run);
+
+/* ------------------------------------------------------------------------------------------
  * Paged decode attention: one query token per sequence.
  *
  * The context of each sequence is cut into splits of blocks_per_split blocks; one

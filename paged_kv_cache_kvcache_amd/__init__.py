@@ -57,6 +57,8 @@ SIGNATURES = {
     "pkv_alloc_prefill_slots": (_i32, [_vp, _p64, _i32, _p32, _p32, _p32, _i32, _p32]),
     "pkv_alloc_debug_constant_hash": (_i32, [_vp, _i32, _u64]),
     "pkv_kv_store": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_kv_store_quant": (_i32, [_pdesc, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_store_runs": (_i32, [_p32, _i32, _p32, _i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "pkv_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _p32, _p32]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
@@ -117,6 +119,10 @@ def _host_i64(values):
 
 def cache_desc(num_blocks, num_kv_heads, head_dim, kv_dtype):
     return CacheDesc(int(num_blocks), BLOCK, int(num_kv_heads), int(head_dim), int(kv_dtype))
+
+
+def _dtype_code(t):
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8}[t.dtype]
 
 
 def desc_of(k_cache):
@@ -214,6 +220,38 @@ def kv_store(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale_new=None, v_s
     _check(lib().pkv_kv_store(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_scale_new), _ptr(v_scale_new),
                               _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                               _stream(stream)), "pkv_kv_store")
+
+
+def store_runs(slot_mapping):
+    """Runs of a host int32 slot mapping for :func:`kv_store_quant`: (runs int32 [2 n_runs] as
+    (first row, length) pairs, n_runs, longest run)."""
+    import numpy as np
+    slots, ps = _host_i32(slot_mapping)
+    n = len(slots)
+    runs = np.empty(2 * max(n, 1), dtype=np.int32)
+    nr, mx = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pkv_store_runs(ps, n, runs.ctypes.data_as(_p32), n, ctypes.byref(nr), ctypes.byref(mx)),
+           "pkv_store_runs")
+    return runs[:2 * nr.value], nr.value, mx.value
+
+
+def kv_store_quant(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, runs=None, stream=None):
+    """Quantising store: bf16/fp32 rows k_new/v_new [n][Hkv][D] into int8 caches with one fp32 scale per
+    (block, KV head), re-quantising a block's earlier rows when its scale grows.  ``runs`` = (device int32
+    [2 n_runs], n_runs, longest run) from :func:`store_runs`; when None it is built from a host copy of
+    ``slot_mapping``."""
+    desc = desc_of(k_cache)
+    n = int(slot_mapping.shape[0])
+    new_dt = _dtype_code(k_new)
+    if _dtype_code(v_new) != new_dt:
+        raise ValueError("k_new and v_new must have the same dtype")
+    if runs is None:
+        r, nr, mx = store_runs(slot_mapping.cpu().numpy() if isinstance(slot_mapping, torch.Tensor) else slot_mapping)
+        runs = (torch.from_numpy(r).to(k_cache.device), nr, mx)
+    rt, nr, mx = runs
+    _check(lib().pkv_kv_store_quant(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), new_dt, _ptr(slot_mapping), n,
+                                    _ptr(rt), int(nr), int(mx), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _stream(stream)), "pkv_kv_store_quant")
 
 
 def decode_plan(B, num_kv_heads, max_context_len, max_splits=0):

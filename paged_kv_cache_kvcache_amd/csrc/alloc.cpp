@@ -339,4 +339,30 @@ int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int3
     return PKV_OK;
 }
 
+int pkv_store_runs(const int32_t* slot_mapping, int32_t n, int32_t* runs, int32_t cap, int32_t* n_runs,
+                   int32_t* max_run) {
+    PKV_REQUIRE(n >= 0 && cap >= 0, PKV_ERR_INVALID, "n = %d, cap = %d", n, cap);
+    PKV_REQUIRE(n_runs != nullptr && max_run != nullptr, PKV_ERR_INVALID, "NULL argument");
+    PKV_REQUIRE(n == 0 || (slot_mapping != nullptr && runs != nullptr), PKV_ERR_INVALID, "NULL argument");
+    int32_t r = 0, longest = 0;
+    for (int32_t t = 0; t < n;) {
+        const int32_t s0 = slot_mapping[t];
+        if (s0 < 0) {
+            ++t;
+            continue;
+        }
+        int32_t len = 1;
+        while (t + len < n && slot_mapping[t + len] == s0 + len && s0 % kBlock + len < kBlock) ++len;
+        if (r >= cap) return fail(PKV_ERR_SMALL_BUFFER, "more than %d runs", cap);
+        runs[2 * r] = t;
+        runs[2 * r + 1] = len;
+        ++r;
+        longest = std::max(longest, len);
+        t += len;
+    }
+    *n_runs = r;
+    *max_run = longest;
+    return PKV_OK;
+}
+
 }  // extern "C"

@@ -93,3 +93,216 @@ extern "C" int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "kv_store launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+// ------------------------------------------------------------------------------------------
+// Quantising store into int8 caches.  The pages name INT8 KV as an engine option
+// (intelliparadigm.com Nano-vLLM article, §2.2 混合精度计算流水线) without an encoding; this
+// library's encoding keeps one fp32 scale per (physical block, KV head):
+//   * the new rows of one call that land in one block form a run of consecutive slots (the
+//     allocator hands out a prompt's tokens and a decode append this way);
+//   * candidate = fl32(absmax of the run's new values / 127) (the quotient in fp64);
+//   * old = the block's scale when the run starts at offset o0 > 0, else 0 (a fresh block);
+//   * new = max(old, candidate); when new > old, rows 0..o0-1 are re-quantised,
+//     code -> rint(code * old / new);
+//   * the run's rows become clamp(rint(x / new), -127, 127) (0 when new = 0); scale = new.
+// rint rounds half to even, on the exact quotient.  A quotient of an 8..32-bit value by a
+// 24-bit scale is never within 2^-33 (relative) of a half-integer unless it is one, so rounding
+// the fp64 quotient and rounding the exact quotient agree.
+//
+// One workgroup per (run, KV head, K or V), from a run list the host builds with the slot
+// mapping (pkv_store_runs).  Short runs (decode appends) take one wavefront, long ones four.
+namespace {
+
+struct QuantArgs {
+    const char* k_new;
+    const char* v_new;
+    const int32_t* slots;
+    const int32_t* runs;   // (first row, length) per run
+    int8_t* k_cache;
+    int8_t* v_cache;
+    float* k_scale;
+    float* v_scale;
+    int32_t num_kv_heads;
+};
+
+// The fp32 estimate q = x * fl(1/s) of x / s has relative error below 2^-23 + 2^-48 (below
+// 3 * 2^-24 when x itself is rounded to fp32 first), so |q - x / s| < 2.3e-5 for |x / s| <= 128:
+// q rounds like x / s unless it lies within kNearHalf of a half-integer.  Only then the exact
+// fp64 residual 2 (x - k s) decides.
+constexpr float kNearHalf = 6e-5f;
+
+__device__ __forceinline__ int fix_rint(int k, double x, double s) {
+    const double r2 = 2.0 * __builtin_fma(-double(k), s, x);  // exact
+    const bool odd = (k & 1) != 0;
+    return k + int(r2 > s || (r2 == s && odd)) - int(r2 < -s || (r2 == -s && odd));
+}
+
+// rint(x / s), ties to even, clamped to +-127; x, s exact in fp64, s > 0.
+__device__ __forceinline__ int quant_div(double x, double s, float rcp) {
+    const float q = float(x) * rcp;
+    int k = int(__builtin_rintf(q));
+    if (fabsf(q - __builtin_floorf(q) - 0.5f) < kNearHalf) k = fix_rint(k, x, s);
+    return min(max(k, -127), 127);
+}
+
+// Eight codes rint(x[e] / s), clamped, for values exact in fp32 (one branch per 8 values).
+__device__ __forceinline__ uint2 quant8(const float (&x)[8], float s, float rcp) {
+    int k[8];
+    bool near = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float q = x[e] * rcp;
+        k[e] = int(__builtin_rintf(q));
+        near |= fabsf(q - __builtin_floorf(q) - 0.5f) < kNearHalf;
+    }
+    if (near) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k[e] = fix_rint(k[e], double(x[e]), double(s));
+    }
+    uint32_t w[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= uint32_t(uint8_t(int8_t(min(max(k[e], -127), 127)))) << (8 * (e & 3));
+    return make_uint2(w[0], w[1]);
+}
+
+template <int D, bool F32, int NT>
+__global__ __launch_bounds__(NT) void kv_store_quant_kernel(QuantArgs a) {
+    constexpr int PR = D / 8;      // 8-value pieces per row
+    constexpr int RS = NT / PR;    // rows per pass
+    constexpr int CR = D / 16;     // 16-code pieces per cache row
+    constexpr int CS = NT / CR;    // cache rows per pass
+    constexpr int MR = (NT == 64 ? 16 : pkv::kBlock) / RS;  // rows per thread for the longest run
+    constexpr int NWAVE = NT / 64;
+    const int h = blockIdx.y;
+    const bool is_v = blockIdx.z != 0;
+    const int t0 = a.runs[2 * blockIdx.x], len = a.runs[2 * blockIdx.x + 1];
+    const int32_t s0 = a.slots[t0];
+    const int64_t blk = s0 / pkv::kBlock;
+    const int o0 = s0 % pkv::kBlock;
+    float* scale = (is_v ? a.v_scale : a.k_scale) + blk * a.num_kv_heads + h;
+    const float old = o0 > 0 ? *scale : 0.f;  // requested early: its latency overlaps the row loads
+
+    const char* src = is_v ? a.v_new : a.k_new;
+    const size_t row_stride = size_t(a.num_kv_heads) * D * (F32 ? 4 : 2);
+    const int pc = threadIdx.x % PR, r0 = threadIdx.x / PR;
+    // batch row t, values 8 pc .. 8 pc + 7 of head h
+    auto load8 = [&](int t, float (&x)[8]) {
+        const char* p = src + size_t(t) * row_stride + (size_t(h) * D + 8 * pc) * (F32 ? 4 : 2);
+        if constexpr (F32) {
+            const uint4 u0 = reinterpret_cast<const uint4*>(p)[0], u1 = reinterpret_cast<const uint4*>(p)[1];
+            const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
+        } else {
+            const uint4 u = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = __uint_as_float(w[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+        }
+    };
+
+    // The run's rows, all loaded at once (a run has at most 256 rows, or 16 for one wavefront):
+    // thread (r0, pc) holds rows r0 + u RS.  Slots past the run re-read its last row.
+    float x[MR][8];
+#pragma unroll
+    for (int u = 0; u < MR; ++u) load8(t0 + min(r0 + u * RS, len - 1), x[u]);
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < MR; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[u][e]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if constexpr (NWAVE > 1) {
+        __shared__ float s_red[NWAVE];
+        if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NWAVE; ++i) amax = fmaxf(amax, s_red[i]);
+    }
+    const float sn = fmaxf(old, float(double(amax) / 127.0));  // the same value in every thread
+    int8_t* cache = (is_v ? a.v_cache : a.k_cache) + ((blk * a.num_kv_heads + h) * pkv::kBlock) * D;
+
+    // re-quantise the block's earlier rows when the scale grows
+    if (o0 > 0 && sn > old) {
+        const float rcp = 1.f / sn;
+        const int cp = threadIdx.x % CR;
+        for (int r = threadIdx.x / CR; r < o0; r += CS) {
+            uint4* p = reinterpret_cast<uint4*>(cache + size_t(r) * D + 16 * cp);
+            const uint4 u = *p;
+            uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t o = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int c = int(int8_t(w[e] >> (8 * b)));
+                    const int q = quant_div(double(c) * double(old), double(sn), rcp);
+                    o |= uint32_t(uint8_t(int8_t(q))) << (8 * b);
+                }
+                w[e] = o;
+            }
+            *p = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+
+    // quantise the run's rows
+    const float rcp = sn > 0.f ? 1.f / sn : 0.f;
+#pragma unroll
+    for (int u = 0; u < MR; ++u) {
+        const int r = r0 + u * RS;
+        if (r >= len) break;
+        *reinterpret_cast<uint2*>(cache + size_t(o0 + r) * D + 8 * pc) =
+            sn > 0.f ? quant8(x[u], sn, rcp) : make_uint2(0, 0);
+    }
+    if (threadIdx.x == 0) *scale = sn;
+}
+
+template <int D, int NT>
+void launch_quant(const QuantArgs& a, int n_runs, bool f32, hipStream_t st) {
+    const dim3 grid(unsigned(n_runs), unsigned(a.num_kv_heads), 2);
+    if (f32) hipLaunchKernelGGL((kv_store_quant_kernel<D, true, NT>), grid, dim3(NT), 0, st, a);
+    else hipLaunchKernelGGL((kv_store_quant_kernel<D, false, NT>), grid, dim3(NT), 0, st, a);
+}
+
+}  // namespace
+
+extern "C" int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
+                                  int32_t new_dtype, const int32_t* slot_mapping, int32_t n, const int32_t* runs,
+                                  int32_t n_runs, int32_t max_run, void* k_cache, void* v_cache, float* k_scale,
+                                  float* v_scale, void* stream) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    PKV_REQUIRE(desc->kv_dtype == PKV_I8, PKV_ERR_UNSUPPORTED, "the quantising store writes int8 caches only");
+    PKV_REQUIRE(new_dtype == PKV_BF16 || new_dtype == PKV_F32, PKV_ERR_UNSUPPORTED,
+                "new rows must be bf16 or f32 (dtype %d)", new_dtype);
+    PKV_REQUIRE(n >= 0 && n_runs >= 0 && n_runs <= n, PKV_ERR_INVALID, "n = %d, n_runs = %d", n, n_runs);
+    PKV_REQUIRE(desc->num_kv_heads <= 65535, PKV_ERR_UNSUPPORTED, "num_kv_heads must be at most 65535");
+    if (n_runs == 0) return PKV_OK;
+    PKV_REQUIRE(max_run >= 1 && max_run <= pkv::kBlock, PKV_ERR_INVALID, "max_run = %d (1..256)", max_run);
+    PKV_REQUIRE(k_new && v_new && slot_mapping && runs && k_cache && v_cache && k_scale && v_scale,
+                PKV_ERR_INVALID, "NULL pointer");
+    const uintptr_t mis = uintptr_t(k_new) | uintptr_t(v_new) | uintptr_t(k_cache) | uintptr_t(v_cache);
+    PKV_REQUIRE((mis & 15) == 0, PKV_ERR_INVALID, "K/V pointers must be 16-byte aligned");
+    QuantArgs a;
+    a.k_new = static_cast<const char*>(k_new);
+    a.v_new = static_cast<const char*>(v_new);
+    a.slots = slot_mapping;
+    a.runs = runs;
+    a.k_cache = static_cast<int8_t*>(k_cache);
+    a.v_cache = static_cast<int8_t*>(v_cache);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.num_kv_heads = desc->num_kv_heads;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool f32 = new_dtype == PKV_F32;
+    const bool wide = max_run > 16;  // four wavefronts per run once a run has more than 16 rows
+    if (desc->head_dim == 64) wide ? launch_quant<64, 256>(a, n_runs, f32, st) : launch_quant<64, 64>(a, n_runs, f32, st);
+    else wide ? launch_quant<128, 256>(a, n_runs, f32, st) : launch_quant<128, 64>(a, n_runs, f32, st);
+    hipError_t e = hipGetLastError();
+    PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "quantising store launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+}

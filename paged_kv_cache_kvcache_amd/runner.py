@@ -10,7 +10,7 @@ import numpy as np
 import torch
 
 from . import (BF16, BLOCK, F32, I8, Allocator, decode_store_attend, decode_workspace_bytes, kv_store,
-               paged_attn_decode, paged_attn_prefill)
+               kv_store_quant, paged_attn_decode, paged_attn_prefill)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 
@@ -51,6 +51,11 @@ class PagedKV:
         """Scatter device rows [n][Hkv][D] to device int32 slots[n]."""
         kv_store(k_rows, v_rows, slots, self.k_cache, self.v_cache, k_scale_rows, v_scale_rows,
                  self.k_scale, self.v_scale)
+
+    def store_quant(self, slots, k_rows, v_rows, runs=None):
+        """int8 pools: quantise bf16/fp32 device rows [n][Hkv][D] into the cache at slots[n]; ``runs`` as
+        :func:`store_runs` gives them, uploaded (built from a host copy of ``slots`` when None)."""
+        kv_store_quant(k_rows, v_rows, slots, self.k_cache, self.v_cache, self.k_scale, self.v_scale, runs=runs)
 
 
 class DecodeBatch:

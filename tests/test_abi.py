@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch  # noqa: F401  (loaded first, so libpkv binds to torch's HIP runtime)
 
@@ -70,6 +71,51 @@ def test_kv_store_scale_pointer_rules():
     assert _store(_desc(), n=-1) == P.ERR_INVALID
     assert _store(_desc(), ptr=ctypes.c_void_p(8)) == P.ERR_INVALID  # misaligned
     assert _store(_desc(), n=0) == P.OK  # empty store enqueues nothing
+
+
+def test_quantising_store_rejects_bad_arguments():
+    i8 = _desc(kv_dtype=P.I8)
+
+    def call(desc, new_dt=P.BF16, n=4, n_runs=1, max_run=4, runs=FAKE, ptr=FAKE, scales=FAKE):
+        return P.lib().pkv_kv_store_quant(ctypes.byref(desc), ptr, ptr, new_dt, FAKE, n, runs, n_runs, max_run, ptr,
+                                          ptr, scales, scales, None)
+    assert call(_desc(kv_dtype=P.BF16)) == P.ERR_UNSUPPORTED   # writes int8 caches only
+    assert call(i8, new_dt=P.I8) == P.ERR_UNSUPPORTED           # rows must be bf16 or f32
+    assert call(i8, n=-1) == P.ERR_INVALID
+    assert call(i8, n_runs=5) == P.ERR_INVALID                  # more runs than rows
+    assert call(i8, max_run=0) == P.ERR_INVALID
+    assert call(i8, max_run=257) == P.ERR_INVALID
+    assert call(i8, runs=None) == P.ERR_INVALID                 # run list required
+    assert call(i8, scales=None) == P.ERR_INVALID               # scales required
+    assert call(i8, ptr=ctypes.c_void_p(8)) == P.ERR_INVALID    # misaligned
+    assert call(i8, n_runs=0) == P.OK
+
+
+def test_store_runs():
+    runs, nr, mx = P.store_runs([5, 6, 7, -1, 8, 255, 256, 257, 1000, 1002, -1])
+    # 5..7 (run), -1 breaks it, 8 alone, 255 is a block's last slot, 256..257 open the next block,
+    # 1000 and 1002 are not consecutive
+    assert nr == 6 and mx == 3
+    assert runs.reshape(-1, 2).tolist() == [[0, 3], [4, 1], [5, 1], [6, 2], [8, 1], [9, 1]]
+    assert P.store_runs([])[1:] == (0, 0)
+    assert P.store_runs([-1, -1])[1:] == (0, 0)
+    full = P.store_runs(list(range(512, 1024)))
+    assert full[1:] == (2, 256) and full[0].tolist() == [0, 256, 256, 256]
+    rng = np.random.default_rng(3)
+    for _ in range(20):   # the runs cover exactly the rows with a slot, each maximal
+        slots = []
+        for _ in range(rng.integers(1, 8)):
+            start = int(rng.integers(0, 4 * 256))
+            slots += list(range(start, start + int(rng.integers(1, 300)))) + ([-1] if rng.random() < 0.3 else [])
+        runs, nr, mx = P.store_runs(slots)
+        rows = []
+        for t, ln in runs.reshape(-1, 2):
+            assert all(slots[t + i] == slots[t] + i for i in range(ln)) and slots[t] % 256 + ln <= 256
+            end = t + ln
+            assert not (end < len(slots) and slots[end] == slots[end - 1] + 1 and slots[end] % 256 != 0)
+            rows += range(t, t + ln)
+        assert rows == [t for t, s in enumerate(slots) if s >= 0]
+        assert mx == max(runs[1::2], default=0)
 
 
 def _decode(desc, B=2, Hq=4, max_blocks=3, max_ctx=600, splits=0, ks=None, vs=None, ws=None, ws_bytes=0,

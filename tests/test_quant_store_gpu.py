@@ -1,0 +1,151 @@
+"""Quantising int8 store on the GPU against the oracle, bit for bit (codes and scales).
+
+A prompt store (runs from offset 0, skipped rows, a prompt stored in two calls so that the second
+run starts mid-block), then decode appends in which some tokens raise their block's absmax and
+force a re-quantisation, and all-zero rows.  After every call the whole int8 caches and scale
+tables must equal the oracle's.  Finally paged decode reads the quantised caches.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_kvcache_amd as P
+import workloads as W
+from oracle import attention as OT
+from tests.gpu_cases import say
+
+pytestmark = pytest.mark.gpu
+BLOCK = 256
+CODE_FILL = 85       # untouched cache rows keep this code
+SCALE_FILL = -7.0    # untouched scale entries keep this value
+
+
+def _rows(rng, shape, src, mul=1.0):
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(mul)
+    if src == "bf16":
+        x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+    return x
+
+
+def _dev(x, src, device):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return t.to(torch.bfloat16) if src == "bf16" else t
+
+
+class Both:
+    """The same int8 caches on the GPU and in the oracle."""
+
+    def __init__(self, nb, hkv, d, device):
+        self.kc = np.full((nb, hkv, BLOCK, d), CODE_FILL, dtype=np.int8)
+        self.vc = self.kc.copy()
+        self.ks = np.full((nb, hkv), SCALE_FILL, dtype=np.float32)
+        self.vs = self.ks.copy()
+        self.g = [torch.from_numpy(a.copy()).to(device) for a in (self.kc, self.vc, self.ks, self.vs)]
+        self.device = device
+
+    def store(self, k, v, slots, src, what):
+        say(f"  store {what}: {len(slots)} rows")
+        sm = torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(self.device)
+        P.kv_store_quant(_dev(k, src, self.device), _dev(v, src, self.device), sm, *self.g)
+        self.kc, self.vc, self.ks, self.vs = OT.kv_store_quant(self.kc, self.vc, self.ks, self.vs, k, v, slots)
+        torch.cuda.synchronize()
+        for got, ref, name in zip(self.g, (self.kc, self.vc, self.ks, self.vs), ("K codes", "V codes", "K scales",
+                                                                                  "V scales")):
+            g = got.cpu().numpy()
+            if not np.array_equal(g, ref):
+                bad = np.argwhere(g != ref)
+                raise AssertionError(f"{what}: {name} differ at {len(bad)} places, first {bad[:4].tolist()}")
+
+
+@pytest.mark.parametrize("D,hkv,src", [(128, 4, "bf16"), (64, 2, "f32")])
+def test_quantising_store_matches_oracle_bitwise(gpu, D, hkv, src):
+    rng = np.random.default_rng(11)
+    lens = [1, 255, 256, 300, 700]
+    nblk = [-(-(L + 40) // BLOCK) for L in lens]   # room for 40 appends
+    nb = sum(nblk) + 3
+    perm = rng.permutation(nb)
+    tables, o = [], 0
+    for k in nblk:
+        tables.append(perm[o:o + k])
+        o += k
+    slot = lambda b, pos: int(tables[b][pos // BLOCK]) * BLOCK + pos % BLOCK
+    st = Both(nb, hkv, D, gpu)
+
+    # prompts: sequence 3 (300 tokens) is stored in two calls, 200 then 100, so its second run starts
+    # at offset 200 of a block; a skipped row sits between two sequences
+    slots, src_rows = [], []
+    for b, L in enumerate(lens):
+        n = 200 if b == 3 else L
+        slots += [slot(b, p) for p in range(n)] + ([-1] if b == 1 else [])
+    k = _rows(rng, (len(slots), hkv, D), src)
+    v = _rows(rng, (len(slots), hkv, D), src, 0.5)
+    k[3, 0] = 0.0                                          # one all-zero row for one head
+    st.store(k, v, slots, src, "prompts")
+    rest = [slot(3, p) for p in range(200, 300)]
+    st.store(_rows(rng, (100, hkv, D), src, 3.0), _rows(rng, (100, hkv, D), src, 0.25), rest, src,
+             "second part of prompt 3 (raises the absmax mid-block)")
+
+    # decode appends: one token per sequence per call; some tokens are large (re-quantisation),
+    # some all-zero, one sequence sits out a step with slot -1
+    pos = list(lens)
+    for step in range(40):
+        mul = 8.0 if step % 7 == 3 else 1.0
+        k = _rows(rng, (len(lens), hkv, D), src, mul)
+        v = _rows(rng, (len(lens), hkv, D), src, min(mul, 2.0))  # V stays small: the decode check is absolute
+        if step % 5 == 2:
+            k[1] = 0.0
+        slots = [slot(b, pos[b]) for b in range(len(lens))]
+        if step == 9:
+            slots[4] = -1
+        st.store(k, v, slots, src, f"append step {step}")
+        for b in range(len(lens)):
+            if slots[b] >= 0:
+                pos[b] += 1
+
+    # paged decode over the quantised caches
+    Hq = 2 * hkv
+    q = rng.standard_normal((len(lens), Hq, D)).astype(np.float32)
+    max_blocks = max(nblk)
+    bt = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    for b, t in enumerate(tables):
+        bt[b, :len(t)] = t
+    out = torch.empty((len(lens), Hq, D), dtype=torch.bfloat16, device=gpu)
+    kc, vc, ks, vs = st.g
+    P.paged_attn_decode(torch.from_numpy(q).to(gpu).to(torch.bfloat16), kc, vc,
+                        torch.from_numpy(bt).to(gpu), torch.tensor(pos, dtype=torch.int32, device=gpu), max(pos),
+                        1.0 / math.sqrt(D), out=out, k_scale=ks, v_scale=vs)
+    qb = W.bf16_bits_to_f32(W.f32_to_bf16_bits(q))
+    ref = OT.decode(qb, st.kc, st.vc, bt, pos, 1.0 / math.sqrt(D), st.ks, st.vs)
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    say(f"  decode over the quantised cache: max-abs {err:.3e}")
+    assert err < 5e-2
+
+
+def test_quantising_store_of_a_prompt_chunk_matches_oracle(gpu):
+    """The first chunk of the int8_store workload (prompts with shared prefixes, slots from the
+    native allocator) stored on the GPU and by the oracle."""
+    from paged_kv_cache_kvcache_amd import runner as R
+    cfg = W.config("int8_store")
+    wl = W.prefill_workload(cfg, 0)
+    prompts = wl["prompts"]
+    kv = R.PagedKV(wl["num_blocks"], cfg["Hkv"], cfg["D"], P.I8, wl["free_order"], device=gpu, fill=CODE_FILL)
+    kv.k_scale.fill_(SCALE_FILL)
+    kv.v_scale.fill_(SCALE_FILL)
+    ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+    n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
+    ch = W.pack_chunks(n_new, cfg["chunk"])[0]
+    _, _, slots = kv.alloc.prefill_slots(ch, sum(n_new[i] for i in ch))
+    k = np.concatenate([W.bf16_bits_to_f32(prompts[i]["k"][ncached[i]:]) for i in ch])
+    v = np.concatenate([W.bf16_bits_to_f32(prompts[i]["v"][ncached[i]:]) for i in ch])
+    say(f"  chunk of {len(ch)} prompts, {len(slots)} new tokens")
+    kv.store_quant(torch.from_numpy(slots).to(gpu), _dev(k, "bf16", gpu), _dev(v, "bf16", gpu))
+    shape = (wl["num_blocks"], cfg["Hkv"], BLOCK, cfg["D"])
+    ref = OT.kv_store_quant(np.full(shape, CODE_FILL, np.int8), np.full(shape, CODE_FILL, np.int8),
+                            np.full(shape[:2], SCALE_FILL, np.float32), np.full(shape[:2], SCALE_FILL, np.float32),
+                            k, v, slots)
+    torch.cuda.synchronize()
+    for got, want in zip((kv.k_cache, kv.v_cache, kv.k_scale, kv.v_scale), ref):
+        assert np.array_equal(got.cpu().numpy(), want)

@@ -51,6 +51,10 @@ CONFIGS = {
                         dtype="bf16", value_scale=1.0, pool=None),
     "int8_decode": dict(id=5, kind="decode", B=128, ctx=(512, 8192), Hq=32, Hkv=32, D=128,
                         dtype="i8", value_scale=1.0, pool=None),
+    # the prompts of prefill_prefix (same seeds, same draws), stored by the quantising store into
+    # int8 caches; dtype is that of the new rows
+    "int8_store": dict(id=3, kind="store", B=32, ctx=(100, 1024), Hq=16, Hkv=8, D=128,
+                       dtype="bf16", value_scale=1.0, pool=None, group=8, shared=512, chunk=4096),
 }
 
 _P_LEN, _P_SEQ, _P_GROUP, _P_POOL, _P_STEP = 0, 1, 2, 3, 4
