@@ -60,7 +60,8 @@ def log(*a):
 
 # ------------------------------------------------------------------------------------ profiles
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = {"decode_split_kernel": "decode.hip", "prefill_kernel": "prefill.hip", "kv_store_kernel": "kv_store.hip"}
+KERNEL_SOURCES = {"decode_split_kernel": "decode.hip", "prefill_kernel": "prefill.hip", "kv_store_kernel": "kv_store.hip",
+                  "kv_store_quant_kernel": "kv_store.hip"}
 
 
 def source_hash(kernel):
@@ -100,7 +101,7 @@ def summarize(name, prof_dir, cmd):
         if scale:
             out.append("copy calibration (bytes of a 1 GiB copy / counter bytes): " +
                        ", ".join(f"{k} x{v:.4f}" for k, v in sorted(scale.items())))
-        for kern in ("decode_split_kernel", "prefill_kernel"):  # the dominant kernels
+        for kern in ("decode_split_kernel", "prefill_kernel", "kv_store_quant_kernel"):  # the dominant kernels
             f = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "FETCH_SIZE"]
             w = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "WRITE_SIZE"]
             if f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
@@ -428,6 +429,8 @@ def bench_int8_store(args, cfg):
     gc.enable()
     kern_s = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 1e3
     gbs = step_bytes / kern_s / 1e9
+    # counter traffic per dispatch (mean over the chunks), when taken on the current kernel source
+    traffic = stored_traffic("kv_store_quant_kernel") if args.seed == 0 else None
     log(f"[bench] int8 store: {len(dchunks)} chunks, {total_new} new tokens, {step_bytes / 1e6:.1f} MB; "
         f"{kern_s * 1e6:.1f} us/step -> {gbs:.0f} GB/s")
     return dict(
@@ -439,7 +442,8 @@ def bench_int8_store(args, cfg):
                     block_size=256, chunks=len(dchunks), seed=args.seed),
         store_kernel_us=kern_s * 1e6,
         roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                      traffic=None, kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
+                      traffic=None if traffic is None else traffic * len(dchunks),
+                      kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
     )
 
 
