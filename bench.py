@@ -306,18 +306,25 @@ def bench_prefill(args, cfg):
     t0 = time.perf_counter()
     ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
     n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
-    chunks = W.pack_chunks(n_new, cfg["chunk"])
+    # chunks as segments (prompt, start, end) of the prompts' new tokens: whole prompts, or prompts
+    # split across chunks when the workload asks for it
+    chunks = (W.pack_chunks_split(n_new, cfg["chunk"]) if cfg.get("split") else
+              [[(i, 0, n_new[i]) for i in ch] for ch in W.pack_chunks(n_new, cfg["chunk"])])
     metas = []
     for ch in chunks:
-        cu, lk, slots = kv.alloc.prefill_slots(ch, sum(n_new[i] for i in ch))
-        mb = max(1, -(-int(lk.max()) // 256))
-        tab, _ = kv.alloc.block_tables(ch, mb)
+        ids = [i for i, _, _ in ch]
+        cu, lk, slots = kv.alloc.prefill_segment_slots(ids, [a for _, a, _ in ch], [b for _, _, b in ch],
+                                                       sum(b - a for _, a, b in ch))
+        tab, lens = kv.alloc.block_tables(ids, wl["num_blocks"])  # whole sequences, later segments included
+        mb = max(1, -(-int(lens.max()) // 256))
+        tab = np.ascontiguousarray(tab[:, :mb])
         metas.append((cu, lk, slots, tab, mb))
     host_s = time.perf_counter() - t0
     # device-resident inputs of every chunk
     dchunks, flops = [], 0
     for ch, (cu, lk, slots, tab, mb) in zip(chunks, metas):
-        dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), dev)
+        dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i] + a:ncached[i] + b]
+                                                       for i, a, b in ch]), dev)
         q, k, v = dv("q"), dv("k"), dv("v")
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         dchunks.append(dict(q=q, k=k, v=v, cu=to(cu), lk=to(lk), slots=to(slots), tab=to(tab).view(len(ch), mb),
@@ -372,7 +379,8 @@ def bench_prefill(args, cfg):
                       flops_per_step=flops),
     )
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_prefill(wl, args.cpu_sample or 4)
+        res["cpu_baseline"] = (cpu_baseline_prefill_rows(wl) if cfg.get("split") else
+                               cpu_baseline_prefill(wl, args.cpu_sample or 4))
     return res
 
 
@@ -445,6 +453,32 @@ def bench_int8_store(args, cfg):
                       traffic=None if traffic is None else traffic * len(dchunks),
                       kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
     )
+
+
+def cpu_baseline_prefill_rows(wl, budget_s=10.0):
+    """Prompts longer than a chunk: the oracle's causal attention (plain definition, fp64) for the
+    last rows of the longest prompt, one row at a time, for about ``budget_s`` seconds."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as OT
+    import workloads as W
+    cfg = wl["cfg"]
+    G = cfg["Hq"] // cfg["Hkv"]
+    p = max(wl["prompts"], key=lambda x: len(x["tokens"]))
+    L = len(p["tokens"])
+    k, v, q = (W.bf16_bits_to_f32(p[x]).astype(np.float64) for x in ("k", "v", "q"))
+    scale = 1.0 / math.sqrt(cfg["D"])
+    n = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s and n < L:
+            pos = L - 1 - n
+            for h in range(cfg["Hq"]):
+                OT.attend(q[pos, h], k[:pos + 1, h // G], v[:pos + 1, h // G], scale)
+            n += 1
+        dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="prefill tokens/s", cores=1, kind="oracle",
+                sample=f"last {n} rows of the {L}-token prompt, all {cfg['Hq']} heads: fp64 causal attention, "
+                       f"{dt:.1f}s on one thread")
 
 
 def cpu_baseline_prefill(wl, first=4):

@@ -144,6 +144,17 @@ int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int3
                             int32_t* cu_seqlens_q, int32_t* seqlens_k, int32_t* slot_mapping,
                             int32_t cap, int32_t* n_slots);
 
+/* Chunked prefill of long prompts ("Nano-vLLM性能调优实战", §3.2 关键调度参数 caps the new tokens
+ * of one step): a prompt's new tokens may be computed over several steps.  Like
+ * pkv_alloc_prefill_slots, for segments [starts[i], ends[i]) of each sequence's new tokens
+ * (0 <= start <= end <= new-token count): cu_seqlens_q[n+1] = prefix sums of the segment
+ * lengths, seqlens_k[n] = n_cached + ends[i] (keys visible to the segment: its cached prefix,
+ * earlier segments and itself), slot_mapping[cap] the segments' slots in order. */
+int pkv_alloc_prefill_segment_slots(const pkv_allocator* a, const int64_t* seq_ids,
+                                    const int32_t* starts, const int32_t* ends, int32_t n,
+                                    int32_t* cu_seqlens_q, int32_t* seqlens_k,
+                                    int32_t* slot_mapping, int32_t cap, int32_t* n_slots);
+
 /* Test hook: when enable != 0 every block hashes to `value`, forcing collisions so that
  * the token-comparison guard can be exercised. */
 int pkv_alloc_debug_constant_hash(pkv_allocator* a, int32_t enable, uint64_t value);

@@ -225,6 +225,26 @@ class Allocator:
             lens_k.append(n)
         return cu, lens_k, slots
 
+    def prefill_segment_slots(self, seq_ids, starts, ends):
+        """Segments [start, end) of each sequence's new tokens, computed over several steps when a
+        prompt exceeds one step's token budget ("Nano-vLLM性能调优实战", §3.2 关键调度参数): the
+        segment's queries see the cached prefix, the earlier segments and themselves, so its key
+        count is n_cached + end."""
+        cu = [0]
+        lens_k = []
+        slots = []
+        for sid, a, b in zip(seq_ids, starts, ends):
+            s = self.seqs.get(sid)
+            if s is None:
+                raise AllocError("UNKNOWN_SEQ", str(sid))
+            if not 0 <= a <= b <= len(s.tokens) - s.n_cached:
+                raise AllocError("INVALID", f"segment [{a}, {b})")
+            for pos in range(s.n_cached + a, s.n_cached + b):
+                slots.append(s.blocks[pos // BLOCK] * BLOCK + pos % BLOCK)
+            cu.append(cu[-1] + b - a)
+            lens_k.append(s.n_cached + b)
+        return cu, lens_k, slots
+
     # -- introspection for invariant tests --------------------------------
     def check_invariants(self):
         owners = [0] * self.num_blocks

@@ -58,6 +58,8 @@ SIGNATURES = {
     "pkv_alloc_debug_constant_hash": (_i32, [_vp, _i32, _u64]),
     "pkv_kv_store": (_i32, [_pdesc, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pkv_kv_store_quant": (_i32, [_pdesc, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_alloc_prefill_segment_slots": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), _p32, _p32, _i32, _p32, _p32, _p32,
+                                                _i32, ctypes.POINTER(ctypes.c_int32)]),
     "pkv_store_runs": (_i32, [_p32, _i32, _p32, _i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "pkv_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _p32, _p32]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -204,6 +206,22 @@ class Allocator:
         _check(lib().pkv_alloc_prefill_slots(self._h, pi, n, cu.ctypes.data_as(_p32), lk.ctypes.data_as(_p32),
                                              slots.ctypes.data_as(_p32), int(cap), ctypes.byref(ns)),
                "pkv_alloc_prefill_slots")
+        return cu, lk[:n], slots[:ns.value]
+
+    def prefill_segment_slots(self, seq_ids, starts, ends, cap):
+        """As :meth:`prefill_slots` for segments [starts[i], ends[i]) of each sequence's new tokens."""
+        import numpy as np
+        ids, pi = _host_i64(seq_ids)
+        st, ps = _host_i32(starts)
+        en, pe = _host_i32(ends)
+        n = len(ids)
+        cu = np.empty(n + 1, dtype=np.int32)
+        lk = np.empty(max(n, 1), dtype=np.int32)
+        slots = np.empty(max(int(cap), 1), dtype=np.int32)
+        ns = ctypes.c_int32()
+        _check(lib().pkv_alloc_prefill_segment_slots(self._h, pi, ps, pe, n, cu.ctypes.data_as(_p32),
+                                                     lk.ctypes.data_as(_p32), slots.ctypes.data_as(_p32), int(cap),
+                                                     ctypes.byref(ns)), "pkv_alloc_prefill_segment_slots")
         return cu, lk[:n], slots[:ns.value]
 
     def debug_constant_hash(self, enable, value=0):

@@ -339,6 +339,39 @@ int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int3
     return PKV_OK;
 }
 
+int pkv_alloc_prefill_segment_slots(const pkv_allocator* a, const int64_t* seq_ids, const int32_t* starts,
+                                    const int32_t* ends, int32_t n, int32_t* cu_seqlens_q, int32_t* seqlens_k,
+                                    int32_t* slot_mapping, int32_t cap, int32_t* n_slots) {
+    PKV_REQUIRE(a != nullptr && cu_seqlens_q != nullptr && n_slots != nullptr, PKV_ERR_INVALID, "NULL argument");
+    PKV_REQUIRE(n >= 0 && cap >= 0, PKV_ERR_INVALID, "n = %d, cap = %d", n, cap);
+    PKV_REQUIRE(n == 0 || (seq_ids != nullptr && starts != nullptr && ends != nullptr && seqlens_k != nullptr),
+                PKV_ERR_INVALID, "NULL argument");
+    int64_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = a->seqs.find(seq_ids[i]);
+        if (it == a->seqs.end())
+            return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+        const int32_t n_new = int32_t(it->second.tokens.size()) - it->second.n_cached;
+        PKV_REQUIRE(0 <= starts[i] && starts[i] <= ends[i] && ends[i] <= n_new, PKV_ERR_INVALID,
+                    "segment [%d, %d) of sequence %lld with %d new tokens", starts[i], ends[i],
+                    (long long)seq_ids[i], n_new);
+        total += ends[i] - starts[i];
+    }
+    if (total > cap) return fail(PKV_ERR_SMALL_BUFFER, "%lld new tokens > slot capacity %d", (long long)total, cap);
+    PKV_REQUIRE(total == 0 || slot_mapping != nullptr, PKV_ERR_INVALID, "slot_mapping is NULL");
+    int32_t k = 0;
+    cu_seqlens_q[0] = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq& s = a->seqs.find(seq_ids[i])->second;
+        for (int32_t p = s.n_cached + starts[i]; p < s.n_cached + ends[i]; ++p)
+            slot_mapping[k++] = s.blocks[p / kBlock] * kBlock + p % kBlock;
+        cu_seqlens_q[i + 1] = k;
+        seqlens_k[i] = s.n_cached + ends[i];
+    }
+    *n_slots = k;
+    return PKV_OK;
+}
+
 int pkv_store_runs(const int32_t* slot_mapping, int32_t n, int32_t* runs, int32_t cap, int32_t* n_runs,
                    int32_t* max_run) {
     PKV_REQUIRE(n >= 0 && cap >= 0, PKV_ERR_INVALID, "n = %d, cap = %d", n, cap);

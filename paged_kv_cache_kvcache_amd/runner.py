@@ -147,6 +147,32 @@ def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None,
     return ncached
 
 
+def prefill_segments(kv, segments, q_new, k_new, v_new, softmax_scale, causal=True, out=None):
+    """One prefill chunk made of segments (seq_id, start, end) of admitted sequences' new tokens, so
+    that a prompt longer than the chunk's token budget is computed over several chunks: store the
+    segments' K/V, then attend (each segment sees its cached prefix, earlier segments and itself).
+
+    q_new [n][Hq][D], k_new/v_new [n][Hkv][D] (device bf16, segments in order).
+    """
+    dev = kv.device
+    n_new = int(q_new.shape[0])
+    ids = [s[0] for s in segments]
+    cu, lk, slots = kv.alloc.prefill_segment_slots(ids, [s[1] for s in segments], [s[2] for s in segments], n_new)
+    # a table row holds all of the sequence's blocks, including those of later segments
+    tab, lens = kv.alloc.block_tables(ids, kv.num_blocks)
+    mb = max(1, -(-int(lens.max()) // BLOCK))
+    tab = np.ascontiguousarray(tab[:, :mb])
+    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel()]).astype(np.int32), dev)
+    B = len(ids)
+    d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
+    d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
+    d_tab = meta[2 * B + 1 + n_new:].view(B, mb)
+    kv.store(d_slots, k_new, v_new)
+    n_q = np.diff(cu)
+    return paged_attn_prefill(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache, d_tab,
+                              softmax_scale, causal, out=out)
+
+
 def prefill_chunk(kv, seq_ids, q_new, k_new, v_new, softmax_scale, causal=True, out=None):
     """One prefill chunk over already-admitted sequences: store the new tokens' K/V, then attend.
 

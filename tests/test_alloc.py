@@ -179,3 +179,46 @@ def test_prefill_workload_prefix_sharing_matches():
         cu, lk, slots = native.prefill_slots(ids, 40000)
         ocu, olk, oslots = oracle.prefill_slots(ids)
         assert (cu.tolist(), lk.tolist(), slots.tolist()) == (ocu, olk, oslots)
+
+
+def test_long_prompts_split_into_chunks_match():
+    """Chunked prefill of prompts longer than a chunk: the segments of every chunk (native vs
+    oracle, bit for bit), and over all chunks they give exactly the whole-prompt slots."""
+    cfg = W.config("prefill_long")
+    for seed in (0, 1):
+        wl = W.prefill_workload(cfg, seed)
+        native = P.Allocator(wl["num_blocks"], wl["free_order"])
+        oracle = OA.Allocator(wl["num_blocks"], wl["free_order"])
+        nc = [native.add_seq(i, p["tokens"]) for i, p in enumerate(wl["prompts"])]
+        assert nc == [oracle.add_seq(i, p["tokens"]) for i, p in enumerate(wl["prompts"])]
+        assert nc[1] > 0 and nc[3] > 0   # the second of each pair reuses the shared prefix
+        n_new = [len(p["tokens"]) - c for p, c in zip(wl["prompts"], nc)]
+        chunks = W.pack_chunks_split(n_new, cfg["chunk"])
+        assert all(sum(b - a for _, a, b in ch) == cfg["chunk"] for ch in chunks[:-1])
+        assert 0 < sum(b - a for _, a, b in chunks[-1]) <= cfg["chunk"]
+        got = {i: [] for i in range(len(n_new))}
+        for ch in chunks:
+            ids, st, en = [s[0] for s in ch], [s[1] for s in ch], [s[2] for s in ch]
+            cu, lk, slots = native.prefill_segment_slots(ids, st, en, cfg["chunk"])
+            ocu, olk, oslots = oracle.prefill_segment_slots(ids, st, en)
+            assert (cu.tolist(), lk.tolist(), slots.tolist()) == (ocu, olk, oslots)
+            for k, (i, a, b) in enumerate(ch):
+                assert lk[k] == nc[i] + b
+                got[i] += slots[cu[k]:cu[k + 1]].tolist()
+        _, _, whole = native.prefill_slots(list(range(len(n_new))), sum(n_new))
+        assert sum((got[i] for i in range(len(n_new))), []) == whole.tolist()
+
+
+def test_segment_slots_reject_bad_segments():
+    native = P.Allocator(8, list(range(8)))
+    native.add_seq(0, list(range(300)))
+    with pytest.raises(P.PkvError):
+        native.prefill_segment_slots([0], [10], [5], 100)      # start after end
+    with pytest.raises(P.PkvError):
+        native.prefill_segment_slots([0], [0], [301], 400)     # past the new tokens
+    with pytest.raises(P.PkvError):
+        native.prefill_segment_slots([7], [0], [1], 10)        # unknown sequence
+    with pytest.raises(P.PkvError):
+        native.prefill_segment_slots([0], [0], [300], 100)     # capacity
+    cu, lk, slots = native.prefill_segment_slots([0, 0], [0, 256], [256, 300], 300)
+    assert cu.tolist() == [0, 256, 300] and lk.tolist() == [256, 300] and slots.tolist() == list(range(300))

@@ -26,6 +26,10 @@ Workloads (the shapes of the Qwen3-0.6B / 7B engines the pages benchmark;
 * ``int8_decode`` -- batch 128, context U[512, 8192], 32 Q / 32 KV heads,
   head_dim 128; K/V drawn N(0,1), rounded to bf16, then stored as int8 with one
   fp32 absmax/127 scale per (block, KV head); bf16 query.
+* ``prefill_long`` -- 4 prompts of length U[4096, 12288] in pairs that share
+  their first 2048 tokens, 16 Q / 8 KV heads, head_dim 128, bf16, N(0,1); each
+  chunk is filled to 4096 new tokens, splitting prompts across chunks.
+* ``int8_store`` -- the prompts of ``prefill_prefix``, for the quantising store.
 
 Pool size (the Qwen3 workload asks for "total tokens x 1.1", which does not fit
 once every sequence rounds up to whole blocks): ceil(1.1 * sum(ceil(L/256)))
@@ -51,6 +55,10 @@ CONFIGS = {
                         dtype="bf16", value_scale=1.0, pool=None),
     "int8_decode": dict(id=5, kind="decode", B=128, ctx=(512, 8192), Hq=32, Hkv=32, D=128,
                         dtype="i8", value_scale=1.0, pool=None),
+    # prompts longer than one step's token budget, computed over several chunks
+    "prefill_long": dict(id=7, kind="prefill", B=4, ctx=(4096, 12288), Hq=16, Hkv=8, D=128,
+                         dtype="bf16", value_scale=1.0, pool=None, group=2, shared=2048, chunk=4096,
+                         split=True),
     # the prompts of prefill_prefix (same seeds, same draws), stored by the quantising store into
     # int8 caches; dtype is that of the new rows
     "int8_store": dict(id=3, kind="store", B=32, ctx=(100, 1024), Hq=16, Hkv=8, D=128,
@@ -225,6 +233,26 @@ def prefill_workload(cfg, seed):
     nb = pool_blocks(cfg, lens)
     return dict(cfg=cfg, seed=seed, lens=lens, num_blocks=nb, free_order=free_order(cfg, seed, nb),
                 prompts=prompts)
+
+
+def pack_chunks_split(n_new, budget):
+    """Prompts in order, each chunk filled to ``budget`` new tokens: a prompt that does not fit is
+    split, its first part ending the chunk and the rest continuing in the next.  Returns chunks as
+    lists of (prompt, start, end) segments of the prompts' new tokens."""
+    chunks, cur, room = [], [], budget
+    for i, n in enumerate(n_new):
+        a = 0
+        while a < n:
+            b = min(n, a + room)
+            cur.append((i, a, b))
+            room -= b - a
+            a = b
+            if room == 0:
+                chunks.append(cur)
+                cur, room = [], budget
+    if cur:
+        chunks.append(cur)
+    return chunks
 
 
 def pack_chunks(n_new, budget):
