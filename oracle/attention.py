@@ -148,11 +148,13 @@ def attend(q, k, v, scale):
     return p @ v
 
 
-def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None):
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None, window=0):
     """Paged decode attention: one query token per sequence.
 
     q ``[B][Hq][D]``; caches ``[nb][Hkv][256][D]``; block_tables ``[B][max_blocks]``;
-    context_lens ``[B]``.  Returns float64 ``[B][Hq][D]``.
+    context_lens ``[B]``.  ``window`` > 0: sliding-window attention (intelliparadigm.com Nano-vLLM
+    article, §7.2 关键优化点), the query at position L-1 sees only its last ``window`` keys
+    L-window..L-1.  Returns float64 ``[B][Hq][D]``.
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, D = q.shape
@@ -164,18 +166,20 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None,
         for g in range(Hkv):
             k = gather(k_cache, block_tables[b], L, g, k_scale)
             v = gather(v_cache, block_tables[b], L, g, v_scale)
+            lo = max(0, L - window) if window > 0 else 0
             for h in range(g * group, (g + 1) * group):
-                out[b, h] = attend(q[b, h], k, v, scale)
+                out[b, h] = attend(q[b, h], k[lo:], v[lo:], scale)
     return out
 
 
-def prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, seqlens_k, scale, causal=True):
+def prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, seqlens_k, scale, causal=True, window=0):
     """Varlen paged prefill attention.
 
     q ``[Nq][Hq][D]`` holds the new tokens of all sequences back to back
     (sequence b owns rows cu_seqlens_q[b]..cu_seqlens_q[b+1]-1); seqlens_k[b]
-    counts all keys of sequence b, cached prefix included.  Returns float64
-    ``[Nq][Hq][D]``.
+    counts all keys of sequence b, cached prefix included.  ``window`` > 0 (causal
+    only): sliding-window attention, the query at position P sees keys
+    P-window+1..P.  Returns float64 ``[Nq][Hq][D]``.
     """
     q = np.asarray(q, dtype=np.float64)
     Nq, Hq, D = q.shape
@@ -190,6 +194,7 @@ def prefill(q, k_cache, v_cache, block_tables, cu_seqlens_q, seqlens_k, scale, c
             v = gather(v_cache, block_tables[b], Lk, g)
             for i in range(n_q):
                 visible = Lk - n_q + i + 1 if causal else Lk
+                lo = max(0, visible - window) if window > 0 else 0
                 for h in range(g * group, (g + 1) * group):
-                    out[q0 + i, h] = attend(q[q0 + i, h], k[:visible], v[:visible], scale)
+                    out[q0 + i, h] = attend(q[q0 + i, h], k[lo:visible], v[lo:visible], scale)
     return out

@@ -470,6 +470,93 @@ def test_shared_prefix_outputs_identical_and_prefix_cache_transparent():
         assert np.allclose(out1[cu1[i]:cu1[i + 1]], out[cu[i] + 512:cu[i] + n], atol=1e-13, rtol=0)
 
 
+# -------------------------------------------------------------------- sliding-window attention
+def test_window_one_returns_the_newest_value():
+    rng = np.random.default_rng(21)
+    q, kc, vc, bt, _, v_seq = _rand_paged(rng, 3, 4, 2, 8, [1, 300, 513])
+    out = OT.decode(q, kc, vc, bt, [1, 300, 513], 0.3, window=1)
+    for b, L in enumerate([1, 300, 513]):
+        for h in range(4):
+            assert np.array_equal(out[b, h], v_seq[b][L - 1, h // 2])
+    cu = [0, 1, 41, 141]
+    qn = rng.standard_normal((141, 4, 8))
+    outp = OT.prefill(qn, kc, vc, bt, cu, [1, 300, 513], 0.3, window=1)
+    for b, (L, nq) in enumerate(zip([1, 300, 513], [1, 40, 100])):
+        for i in range(nq):
+            for h in range(4):
+                assert np.array_equal(outp[cu[b] + i, h], v_seq[b][L - nq + i, h // 2])
+
+
+def test_window_covering_every_key_is_full_attention():
+    rng = np.random.default_rng(22)
+    lens = [300, 7, 600]
+    q, kc, vc, bt, _, _ = _rand_paged(rng, 3, 4, 2, 8, lens)
+    assert np.array_equal(OT.decode(q, kc, vc, bt, lens, 0.3, window=600), OT.decode(q, kc, vc, bt, lens, 0.3))
+    cu = [0, 50, 57, 157]
+    qn = rng.standard_normal((157, 4, 8))
+    full = OT.prefill(qn, kc, vc, bt, cu, lens, 0.3)
+    assert np.array_equal(OT.prefill(qn, kc, vc, bt, cu, lens, 0.3, window=600), full)
+    assert not np.allclose(OT.prefill(qn, kc, vc, bt, cu, lens, 0.3, window=599), full)
+
+
+def test_windowed_decode_matches_pure_python_brute_force():
+    rng = np.random.default_rng(23)
+    for trial in range(20):
+        B = int(rng.integers(1, 3))
+        D = int(rng.integers(1, 5))
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * int(rng.integers(1, 3))
+        lens = [int(x) for x in rng.integers(1, 9, size=B)]
+        w = int(rng.integers(1, 6))
+        q, kc, vc, bt, k_seq, v_seq = _rand_paged(rng, B, Hq, Hkv, D, lens)
+        out = OT.decode(q, kc, vc, bt, lens, 0.7, window=w)
+        for b in range(B):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                keys = k_seq[b][:, g].tolist()[-w:]
+                vals = v_seq[b][:, g].tolist()[-w:]
+                assert np.allclose(out[b, h], _brute(q[b, h].tolist(), keys, vals, 0.7), rtol=0, atol=1e-13)
+
+
+def _band_mask(n_q, L, window):
+    """Bottom-right causal mask limited to the last ``window`` keys of each query."""
+    m = np.full((n_q, L), -np.inf)
+    for i in range(n_q):
+        p = L - n_q + i
+        m[i, max(0, p - window + 1):p + 1] = 0.0
+    return m
+
+
+def test_windowed_prefill_equals_sdpa_with_band_mask():
+    rng = np.random.default_rng(24)
+    Hq, Hkv, D = 4, 2, 8
+    lens_k = [300, 5, 520]
+    n_q = [45, 5, 264]
+    q_all, kc, vc, bt, k_seq, v_seq = _rand_paged(rng, 3, Hq, Hkv, D, lens_k)
+    cu = np.concatenate([[0], np.cumsum(n_q)])
+    q = rng.standard_normal((cu[-1], Hq, D))
+    for window in (1, 3, 64, 100, 257):
+        out = OT.prefill(q, kc, vc, bt, cu, lens_k, 0.4, window=window)
+        for b in range(3):
+            k = np.repeat(k_seq[b].transpose(1, 0, 2), 2, axis=0)
+            v = np.repeat(v_seq[b].transpose(1, 0, 2), 2, axis=0)
+            qb = q[cu[b]:cu[b + 1]].transpose(1, 0, 2)
+            ref = _sdpa(qb, k, v, 0.4, _band_mask(n_q[b], lens_k[b], window)).transpose(1, 0, 2)
+            assert np.max(np.abs(out[cu[b]:cu[b + 1]] - ref)) < 1e-12, (window, b)
+
+
+def test_windowed_prefill_last_row_equals_windowed_decode():
+    rng = np.random.default_rng(25)
+    lens = [300, 600]
+    q, kc, vc, bt, _, _ = _rand_paged(rng, 2, 4, 2, 8, lens)
+    cu = [0, 20, 70]
+    qn = rng.standard_normal((70, 4, 8))
+    qn[19], qn[69] = q[0], q[1]
+    outp = OT.prefill(qn, kc, vc, bt, cu, lens, 0.3, window=130)
+    outd = OT.decode(q, kc, vc, bt, lens, 0.3, window=130)
+    assert np.allclose(outp[[19, 69]], outd, rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------------------- int8 quantising store
 def _golden_int8_store():
     vals = {}

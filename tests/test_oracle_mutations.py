@@ -194,6 +194,45 @@ def _store_quant_variant(requant=True, fresh_resets=True, keep_old=True):
     return store
 
 
+def _decode_window_short(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None, v_scale=None,
+                         window=0):
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    G = Hq // k_cache.shape[1]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(context_lens[b])
+        for h in range(Hq):
+            k = OT.gather(k_cache, block_tables[b], L, h // G, k_scale)
+            v = OT.gather(v_cache, block_tables[b], L, h // G, v_scale)
+            lo = max(0, L - window + 1) if window > 0 else 0   # one key short
+            out[b, h] = OT.attend(q[b, h], k[lo:], v[lo:], scale)
+    return out
+
+
+def _prefill_window_variant(shift=0, from_start=False):
+    def prefill(q, k_cache, v_cache, block_tables, cu, lk, scale, causal=True, window=0):
+        q = np.asarray(q, dtype=np.float64)
+        Nq, Hq, D = q.shape
+        G = Hq // k_cache.shape[1]
+        out = np.zeros((Nq, Hq, D))
+        for b in range(len(lk)):
+            q0, q1 = int(cu[b]), int(cu[b + 1])
+            n_q, L = q1 - q0, int(lk[b])
+            for h in range(Hq):
+                k = OT.gather(k_cache, block_tables[b], L, h // G)
+                v = OT.gather(v_cache, block_tables[b], L, h // G)
+                for i in range(n_q):
+                    vis = L - n_q + i + 1 if causal else L
+                    lo = max(0, vis - window + shift) if window > 0 else 0
+                    hi = vis
+                    if from_start and window > 0:
+                        lo, hi = 0, min(window, vis)
+                    out[q0 + i, h] = OT.attend(q[q0 + i, h], k[lo:hi], v[lo:hi], scale)
+        return out
+    return prefill
+
+
 OT_attend_orig = OT.attend
 OT_gather_orig = OT.gather
 OA_block_hash_orig = OA.block_hash
@@ -224,6 +263,13 @@ QUANT_PINS = [
     P.test_int8_store_appends_that_keep_the_absmax_equal_one_shot,
     P.test_int8_store_requantises_by_the_scale_ratio_with_ties_to_even,
 ]
+WINDOW_PINS = [
+    P.test_window_one_returns_the_newest_value,
+    P.test_window_covering_every_key_is_full_attention,
+    P.test_windowed_decode_matches_pure_python_brute_force,
+    P.test_windowed_prefill_equals_sdpa_with_band_mask,
+    P.test_windowed_prefill_last_row_equals_windowed_decode,
+]
 HASH_PINS = [lambda: [P.test_fnv1a64_published_vectors(d, e) for d, e in P._golden_fnv()],
              P.test_block_hash_closed_forms]
 
@@ -250,6 +296,11 @@ MUTANTS = {
     "int8 store keeps a fresh block's old scale": (OT, "kv_store_quant", _store_quant_variant(fresh_resets=False),
                                                    QUANT_PINS),
     "int8 scale from the new rows only": (OT, "kv_store_quant", _store_quant_variant(keep_old=False), QUANT_PINS),
+    "decode window one key short": (OT, "decode", _decode_window_short, WINDOW_PINS),
+    "prefill window one key long": (OT, "prefill", _prefill_window_variant(shift=-1), WINDOW_PINS),
+    "prefill window one key short": (OT, "prefill", _prefill_window_variant(shift=1), WINDOW_PINS),
+    "prefill window counted from the first key": (OT, "prefill", _prefill_window_variant(from_start=True),
+                                                  WINDOW_PINS),
 }
 
 
