@@ -248,6 +248,20 @@ int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, 
                           int32_t max_context_len, int32_t max_splits, float softmax_scale,
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sliding-window decode (intelliparadigm.com Nano-vLLM article, §7.2 关键优化点 lists sliding-
+ * window attention): as pkv_paged_attn_decode, but sequence b attends only its last `window`
+ * keys, positions max(0, context_lens[b] - window) .. context_lens[b] - 1; window = 0 attends
+ * every key.  The split plan covers the window's blocks only (a workspace sized by
+ * pkv_decode_workspace_bytes for max_context_len is always enough).  window < 0 is
+ * PKV_ERR_INVALID. */
+int pkv_paged_attn_decode_window(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_tables,
+                                 int32_t max_blocks, const int32_t* context_lens,
+                                 const int32_t* seq_order, int32_t max_context_len,
+                                 int32_t max_splits, float softmax_scale, int32_t window, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* pkv_decode_store_attend: one decode step's store and attention in one launch -- the
  * engine's store_kvcache write of each step's new token followed by attention over the cache
  * ("Nano-vLLM性能调优实战", §2.2 缓存复用策略), fused.
@@ -287,6 +301,17 @@ int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q, int32_t Hq
                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
                            int32_t max_blocks, float softmax_scale, int32_t causal, void* out,
                            void* stream);
+
+/* Sliding-window prefill (intelliparadigm.com Nano-vLLM article, §7.2 关键优化点 lists
+ * sliding-window attention): pkv_paged_attn_prefill with causal = 1, where the query at position
+ * P sees keys max(0, P - window + 1) .. P; window = 0 sees every key up to P.  Key tiles before
+ * a query tile's window are not read.  window < 0 is PKV_ERR_INVALID. */
+int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                  const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                  int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks,
+                                  float softmax_scale, int32_t window, void* out, void* stream);
 
 #ifdef __cplusplus
 }

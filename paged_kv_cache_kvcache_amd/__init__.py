@@ -65,10 +65,14 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _f32, _vp, _vp, _sz, _vp]),
+    "pkv_paged_attn_decode_window": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                            _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_decode_store_attend": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i32, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attn_prefill": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                       _f32, _i32, _vp, _vp]),
+    "pkv_paged_attn_prefill_window": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                             _i32, _f32, _i32, _vp, _vp]),
 }
 
 _lib = None
@@ -286,9 +290,10 @@ def decode_workspace_bytes(B, Hq, head_dim, num_kv_heads, max_context_len, max_s
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, softmax_scale,
                       out=None, workspace=None, max_splits=0, k_scale=None, v_scale=None, seq_order=None,
-                      stream=None):
+                      stream=None, window=0):
     """Decode attention; q [B][Hq][D].  Allocates ``out`` / ``workspace`` with torch when not given.
-    ``seq_order`` (device int32 [B], optional): launch order of the sequences, e.g. longest first."""
+    ``seq_order`` (device int32 [B], optional): launch order of the sequences, e.g. longest first.
+    ``window`` > 0: sliding window, each sequence attends its last ``window`` keys."""
     desc = desc_of(k_cache)
     B, Hq, D = q.shape
     if out is None:
@@ -297,6 +302,13 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if window:
+        _check(lib().pkv_paged_attn_decode_window(
+            ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), _ptr(seq_order),
+            int(max_context_len), int(max_splits), float(softmax_scale), int(window), _ptr(out), _ptr(workspace),
+            ws_bytes, _stream(stream)), "pkv_paged_attn_decode_window")
+        return out
     _check(lib().pkv_paged_attn_decode(ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), int(block_tables.shape[1]),
                                        _ptr(context_lens), _ptr(seq_order), int(max_context_len), int(max_splits),
@@ -329,13 +341,23 @@ def decode_store_attend(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_t
 
 
 def paged_attn_prefill(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache, block_tables,
-                       softmax_scale, causal=True, out=None, stream=None):
-    """Varlen prefill; q [total_q][Hq][D] bf16, cu_seqlens_q [B+1], seqlens_k [B] (device int32)."""
+                       softmax_scale, causal=True, out=None, stream=None, window=0):
+    """Varlen prefill; q [total_q][Hq][D] bf16, cu_seqlens_q [B+1], seqlens_k [B] (device int32).
+    ``window`` > 0 (causal): sliding window, the query at position P sees keys P-window+1..P."""
     desc = desc_of(k_cache)
     total_q, Hq, _ = q.shape
     B = int(seqlens_k.shape[0])
     if out is None:
         out = torch.empty_like(q)
+    if window:
+        if not causal:
+            raise ValueError("a sliding window needs causal attention")
+        _check(lib().pkv_paged_attn_prefill_window(
+            ctypes.byref(desc), _ptr(q), int(Hq), _ptr(cu_seqlens_q), _ptr(seqlens_k), B, int(total_q),
+            int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            int(block_tables.shape[1]), float(softmax_scale), int(window), _ptr(out), _stream(stream)),
+            "pkv_paged_attn_prefill_window")
+        return out
     _check(lib().pkv_paged_attn_prefill(ctypes.byref(desc), _ptr(q), int(Hq), _ptr(cu_seqlens_q), _ptr(seqlens_k),
                                         B, int(total_q), int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache),
                                         _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]),

@@ -240,6 +240,7 @@ struct DecodeArgs {
     int32_t num_q_heads;
     int32_t splits;
     int32_t blocks_per_split;
+    int32_t window;    // > 0: sliding window, the last `window` keys of each sequence
     float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -253,7 +254,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int b = a.seq_order != nullptr ? a.seq_order[blockIdx.z] : int(blockIdx.z);
     const int ctx = a.context_lens[b];
     const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
-    const int blk0 = s * a.blocks_per_split;
+    // keys lo..ctx-1 are attended: all of them, or the last `window` (splits start at lo's block)
+    const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
+    const int blk0 = lo / pkv::kBlock + s * a.blocks_per_split;
     const int blk1 = min(nblk, blk0 + a.blocks_per_split);
     if (a.splits > 1 && blk0 >= blk1) return;  // empty split: the reduce kernel skips it
 
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             ks *= a.k_scale[phys * a.num_kv_heads + g];
             vs = a.v_scale[phys * a.num_kv_heads + g];
         }
-        const bool row_ok = 4 * c + r < valid;
+        const bool row_ok = 4 * c + r < valid && blk * pkv::kBlock + w * kTile + 4 * c + r >= lo;
 
         float p[G];
 #pragma unroll
@@ -464,7 +467,8 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int ctx = a.context_lens[b];
     const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
-    const int active = min(a.splits, (nblk + a.blocks_per_split - 1) / a.blocks_per_split);
+    const int lo_blk = (a.window > 0 ? max(0, ctx - a.window) : 0) / pkv::kBlock;
+    const int active = min(a.splits, (nblk - lo_blk + a.blocks_per_split - 1) / a.blocks_per_split);
     const size_t base = (size_t(b) * a.num_q_heads + h) * a.splits;
     float M = kNegInf;
     for (int s = 0; s < active; ++s) M = fmaxf(M, a.ws_ml[2 * (base + s)]);
@@ -574,7 +578,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
                 const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* block_tables,
                 int32_t max_blocks, const int32_t* context_lens, const int32_t* seq_order, int32_t max_context_len,
                 int32_t max_splits, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-                const NewTokens* nt, void* stream) {
+                const NewTokens* nt, int32_t window, void* stream) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     const int Hkv = desc->num_kv_heads, D = desc->head_dim;
@@ -589,6 +593,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
                 "max_blocks %d cannot hold max_context_len %d", max_blocks, max_context_len);
     PKV_REQUIRE(B <= 65535 && Hkv <= 65535, PKV_ERR_UNSUPPORTED, "B and Hkv must be at most 65535");
     PKV_REQUIRE(std::isfinite(softmax_scale), PKV_ERR_INVALID, "softmax_scale is not finite");
+    PKV_REQUIRE(window >= 0, PKV_ERR_INVALID, "window = %d", window);
     const bool i8 = desc->kv_dtype == PKV_I8;
     PKV_REQUIRE(i8 == (k_scale != nullptr) && i8 == (v_scale != nullptr), PKV_ERR_INVALID,
                 "k_scale / v_scale are required for int8 caches and rejected otherwise");
@@ -619,6 +624,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
     a.num_kv_heads = Hkv;
     a.num_q_heads = Hq;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.window = window;
     if (nt != nullptr) {
         a.new_slots = nt->slot_mapping;
         a.k_new = static_cast<const char*>(nt->k_new);
@@ -630,7 +636,10 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
         a.k_scale_store = nt->k_scale;
         a.v_scale_store = nt->v_scale;
     }
-    plan(B, Hkv, max_context_len, max_splits, &a.splits, &a.blocks_per_split);
+    // a window of W keys spans at most ceil((W + 255) / 256) blocks
+    const int span = window > 0 ? int(std::min<int64_t>(max_context_len, int64_t(window) + pkv::kBlock - 1))
+                                : max_context_len;
+    plan(B, Hkv, span, max_splits, &a.splits, &a.blocks_per_split);
     if (a.splits > 1) {
         const size_t need = size_t(B) * Hq * a.splits * (size_t(D) + 2) * sizeof(float);
         PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_SMALL_BUFFER,
@@ -660,7 +669,19 @@ extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, 
                                      void* workspace, size_t workspace_bytes, void* stream) {
     return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
                        seq_order, max_context_len, max_splits, softmax_scale, out, workspace, workspace_bytes,
-                       nullptr, stream);
+                       nullptr, 0, stream);
+}
+
+extern "C" int pkv_paged_attn_decode_window(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                            const void* k_cache, const void* v_cache, const float* k_scale,
+                                            const float* v_scale, const int32_t* block_tables,
+                                            int32_t max_blocks, const int32_t* context_lens,
+                                            const int32_t* seq_order, int32_t max_context_len,
+                                            int32_t max_splits, float softmax_scale, int32_t window, void* out,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
+                       seq_order, max_context_len, max_splits, softmax_scale, out, workspace, workspace_bytes,
+                       nullptr, window, stream);
 }
 
 extern "C" int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
@@ -682,5 +703,5 @@ extern "C" int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q
     nt.v_scale = v_scale;
     return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
                        seq_order, max_context_len, max_splits, softmax_scale, out, workspace, workspace_bytes, &nt,
-                       stream);
+                       0, stream);
 }

@@ -61,6 +61,7 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     int32_t num_q_heads;
     int32_t causal;
+    int32_t window;  // > 0 (causal only): a query at position P sees keys P - window + 1 .. P
     float scale_log2;
 };
 
@@ -171,6 +172,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     }
     const int pw_max = __builtin_amdgcn_readfirstlane(pw);
     const int pw_min = __builtin_amdgcn_readfirstlane(pm);
+    // sliding window: the first key this column sees; over the wavefront the smallest (tiles below
+    // it are skipped) and the largest (tiles from it on need no lower mask).  The workgroup's first
+    // tile holds the first key of its first token.
+    const int Lo = a.window > 0 ? max(0, P - a.window + 1) : 0;
+    int lw = Lo, lm = Lo;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lw = min(lw, __shfl_xor(lw, o, 64));
+        lm = max(lm, __shfl_xor(lm, o, 64));
+    }
+    const int lw_min = __builtin_amdgcn_readfirstlane(lw);
+    const int lw_max = __builtin_amdgcn_readfirstlane(lm);
+    const int kt0 = a.window > 0 ? max(0, pos0 - a.window + 1) / kKT : 0;
 
     // ---- this sequence's block table, 64 entries at a time: lane i holds entry 64 win + i, and a
     // tile reads its physical block with readlane (no memory access per tile).  The first window
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    if (ntiles > 0) dma(0, lds[0]);
+    if (kt0 < ntiles) dma(kt0, lds[0]);
 
     // ---- Q^T operand: column col = query row, 8 consecutive d per k-step.  Q is multiplied by
     // softmax_scale * log2(e) (fp32, rounded once to bf16), so S comes out in log2 units.  Loaded
@@ -274,7 +288,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         wait_dma();
         __syncthreads();
         if (kt + 1 < ntiles) dma(kt + 1, lds[buf ^ 1]);
-        if (kt * kKT > pw_max) return;  // every key of this tile is masked for this wavefront
+        // every key of this tile is masked for this wavefront (past its last key, or before its window)
+        if (kt * kKT > pw_max || kt * kKT + kKT - 1 < lw_min) return;
 
         const char* Ks = lds[buf];
         const char* Vs = lds[buf] + TB;
@@ -316,15 +331,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
                     va[mt][kk][dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
         __builtin_amdgcn_sched_barrier(0);
-        // mask (diagonal tiles only) and tile max
+        // mask (diagonal and window-edge tiles only) and tile max
         float tmax = kNegInf;
-        if (kt * kKT + kKT - 1 > pw_min) {
+        if (kt * kKT + kKT - 1 > pw_min || kt * kKT < lw_max) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = kt * kKT + 32 * mt + 8 * (i / 4) + 4 * h + (i % 4);
-                    s[mt][i] = key <= P ? s[mt][i] : kNegInf;
+                    s[mt][i] = key <= P && key >= Lo ? s[mt][i] : kNegInf;
                     tmax = fmaxf(tmax, s[mt][i]);
                 }
         } else {
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
             }
         }
     };
-    for (int kt = 0; kt < ntiles; kt += 2) {
+    for (int kt = kt0; kt < ntiles; kt += 2) {
         step(kt, std::integral_constant<int, 0>{});
         if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
     }
@@ -445,12 +460,12 @@ int current_num_cus() {
 
 }  // namespace
 
-extern "C" int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q, int32_t Hq,
-                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
-                                      int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                                      int32_t max_blocks, float softmax_scale, int32_t causal, void* out,
-                                      void* stream) {
+namespace {
+
+int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const int32_t* cu_seqlens_q,
+                 const int32_t* seqlens_k, int32_t B, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                 const void* k_cache, const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
+                 float softmax_scale, int32_t causal, int32_t window, void* out, void* stream) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     PKV_REQUIRE(desc->kv_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED, "prefill supports bf16 caches only");
@@ -469,6 +484,8 @@ extern "C" int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q,
     PKV_REQUIRE(Hkv <= 65535, PKV_ERR_UNSUPPORTED, "Hkv must be at most 65535");
     PKV_REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, PKV_ERR_INVALID,
                 "softmax_scale must be finite and positive");
+    PKV_REQUIRE(window >= 0 && (window == 0 || causal), PKV_ERR_INVALID,
+                "window = %d: a sliding window needs causal attention and window >= 0", window);
     if (B == 0 || total_q == 0) return PKV_OK;
     PKV_REQUIRE(q && cu_seqlens_q && seqlens_k && k_cache && v_cache && block_tables && out, PKV_ERR_INVALID,
                 "NULL pointer");
@@ -487,10 +504,33 @@ extern "C" int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q,
     a.num_kv_heads = Hkv;
     a.num_q_heads = Hq;
     a.causal = causal != 0;
+    a.window = window;
     a.scale_log2 = softmax_scale * kLog2e;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int cus = current_num_cus();
     const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, st) : launch_g<128>(a, total_q, G, cus, st);
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attn_prefill(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                      int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                      int32_t max_blocks, float softmax_scale, int32_t causal, void* out,
+                                      void* stream) {
+    return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
+                        v_cache, block_tables, max_blocks, softmax_scale, causal, 0, out, stream);
+}
+
+extern "C" int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                             const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                             int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                             const void* k_cache, const void* v_cache,
+                                             const int32_t* block_tables, int32_t max_blocks,
+                                             float softmax_scale, int32_t window, void* out, void* stream) {
+    return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
+                        v_cache, block_tables, max_blocks, softmax_scale, 1, window, out, stream);
 }
