@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--config", default="qwen3_decode")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window attention: each query attends its last W keys (0: every key)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
     ap.add_argument("--copy-calib", action="store_true",
@@ -157,8 +159,10 @@ def bench_decode(args, cfg):
                       [None if p[2] is None else p[2][:-1] for p in parts],
                       [None if p[3] is None else p[3][:-1] for p in parts])
     max_ctx = max(lens) + nsteps
-    batch = R.DecodeBatch(kv, Hq, ids, max_ctx, args.max_splits)
-    splits, bps = decode_plan(B, Hkv, max_ctx, args.max_splits)
+    batch = R.DecodeBatch(kv, Hq, ids, max_ctx, args.max_splits, window=args.window)
+    # the plan the kernel uses: a window of W keys spans at most ceil((W + 255) / 256) blocks
+    span = min(max_ctx, args.window + 255) if args.window > 0 else max_ctx
+    splits, bps = decode_plan(B, Hkv, span, args.max_splits)
 
     # per-step inputs, resident on the device before timing
     steps = []
@@ -198,6 +202,8 @@ def bench_decode(args, cfg):
     esize = {"f32": 4, "bf16": 2, "i8": 1}[dtype]
 
     def kv_bytes(ctx):
+        # the keys attended: the whole context, or the last `window` of it
+        ctx = [min(c, args.window) if args.window > 0 else c for c in ctx]
         b = sum(ctx) * Hkv * D * esize * 2
         if dtype == "i8":
             b += sum(-(-c // 256) for c in ctx) * Hkv * 2 * 4
@@ -244,16 +250,16 @@ def bench_decode(args, cfg):
         dtype=dtype, data="synthetic",
         config=dict(workload=cfg["name"], batch=B, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]" if isinstance(
             cfg["ctx"], tuple) else str(cfg["ctx"]), q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256,
-            splits=splits, blocks_per_split=bps, seed=args.seed),
+            splits=splits, blocks_per_split=bps, window=args.window, seed=args.seed),
         decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
         kv_gbs=achieved,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
                       traffic=stored_traffic("decode_split_kernel") if cfg["name"] == "qwen3_decode" and splits == 1
-                      and args.seed == 0 else None,
+                      and args.seed == 0 and args.window == 0 else None,
                       kernel="decode (split kernel + LSE reduce when splits > 1)",
                       bytes_per_launch=bytes_per_launch),
     )
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.window == 0:
         res["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_sample or 8)
     return res
 
@@ -331,7 +337,9 @@ def bench_prefill(args, cfg):
                             max_q=int(np.diff(cu).max()), max_k=int(lk.max()), out=torch.empty_like(q)))
         for b in range(len(ch)):
             nq, L = int(cu[b + 1] - cu[b]), int(lk[b])
-            flops += 4 * D * Hq * sum(L - nq + i + 1 for i in range(nq))
+            # causal pairs (within the window when there is one)
+            flops += 4 * D * Hq * sum(min(L - nq + i + 1, args.window) if args.window > 0 else L - nq + i + 1
+                                      for i in range(nq))
     scale = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream()
     nch = len(dchunks)
@@ -344,7 +352,7 @@ def bench_prefill(args, cfg):
             if timed is not None:
                 ev[timed][c][0].record(stream)
             paged_attn_prefill(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache, d["tab"],
-                               scale, True, out=d["out"])
+                               scale, True, out=d["out"], window=args.window)
             if timed is not None:
                 ev[timed][c][1].record(stream)
 
@@ -370,7 +378,8 @@ def bench_prefill(args, cfg):
         warmup=args.warmup, ms_per_step=elapsed / args.steps * 1e3, higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=cfg["name"], prompts=cfg["B"], prompt_len=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]",
-                    shared_prefix=cfg["shared"], group=cfg["group"], chunk_tokens=cfg["chunk"], q_heads=Hq,
+                    shared_prefix=cfg["shared"], group=cfg["group"], chunk_tokens=cfg["chunk"], window=args.window,
+                    q_heads=Hq,
                     kv_heads=Hkv, head_dim=D, block_size=256, chunks=nch, new_tokens=total_new,
                     cached_tokens=sum(ncached), seed=args.seed),
         prefill_kernel_us=kern_s * 1e6, prefill_tflops=tflops, host_admit_us=host_s * 1e6,
@@ -378,7 +387,7 @@ def bench_prefill(args, cfg):
                       frac=tflops / BF16_PEAK_TFLOPS, traffic=None, kernel="prefill (all chunks of one step)",
                       flops_per_step=flops),
     )
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.window == 0:
         res["cpu_baseline"] = (cpu_baseline_prefill_rows(wl) if cfg.get("split") else
                                cpu_baseline_prefill(wl, args.cpu_sample or 4))
     return res

@@ -62,7 +62,7 @@ class DecodeBatch:
     """A batch of sequences in decode: history admitted and stored, then one token per step
     (``fused``: the step's store and attention in one launch, pkv_decode_store_attend)."""
 
-    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False):
+    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False, window=0):
         self.kv = kv
         self.Hq = int(Hq)
         self.ids = np.asarray(seq_ids, dtype=np.int64)
@@ -71,6 +71,9 @@ class DecodeBatch:
         self.max_context_len = int(max_context_len)
         self.max_splits = max_splits
         self.fused = fused
+        self.window = int(window)  # > 0: sliding-window attention over the last `window` keys
+        if self.fused and self.window:
+            raise ValueError("the fused store+attend step has no sliding window")
         dev = kv.device
         # pinned staging for the per-step metadata: slots[B] | lens[B] | order[B] | tables[B][max_blocks]
         self._pin = torch.empty(3 * self.B + self.B * self.max_blocks, dtype=torch.int32).pin_memory()
@@ -119,7 +122,7 @@ class DecodeBatch:
         return paged_attn_decode(q, self.kv.k_cache, self.kv.v_cache, self.block_tables, self.context_lens,
                                 self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale,
-                                seq_order=self.seq_order)
+                                seq_order=self.seq_order, window=self.window)
 
 
 def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None, v_scale_rows=None):
