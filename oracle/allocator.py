@@ -163,12 +163,52 @@ class Allocator:
         self.seqs[seq_id] = s
         return s.n_cached
 
-    def append(self, seq_id, token):
-        """Add one decoded token; returns its cache slot."""
+    def fork(self, parent_id, child_id):
+        """Parallel sampling / beam search (ocdem.com nano-vllm article, §2.1: sequences of one
+        request share physical blocks): the child takes the parent's tokens and every one of its
+        blocks, each block's reference count growing by one.  A partially filled last block stays
+        shared until one of its owners appends (:meth:`append_cow`)."""
+        if child_id in self.seqs:
+            raise AllocError("DUP_SEQ", str(child_id))
+        p = self.seqs.get(parent_id)
+        if p is None:
+            raise AllocError("UNKNOWN_SEQ", str(parent_id))
+        c = _Seq()
+        c.blocks = list(p.blocks)
+        c.tokens = list(p.tokens)
+        c.n_cached = len(p.tokens)
+        c.last_hash = p.last_hash
+        for b in c.blocks:
+            self.ref[b] += 1
+        self.seqs[child_id] = c
+
+    def append_cow(self, seq_id, token):
+        """:meth:`append` with copy-on-write: when the token lands in a partially filled block that
+        other sequences still hold, the sequence first moves to a fresh block, into which the caller
+        copies the shared block's contents.  Returns (slot, src, dst), src = dst = -1 without a copy."""
         s = self.seqs.get(seq_id)
         if s is None:
             raise AllocError("UNKNOWN_SEQ", str(seq_id))
         pos = len(s.tokens)
+        src = dst = -1
+        if pos % BLOCK != 0 and self.ref[s.blocks[pos // BLOCK]] > 1:
+            if not self.free:
+                raise AllocError("NO_BLOCKS", "copy-on-write")
+            src = s.blocks[pos // BLOCK]
+            dst = self._pop_fresh()
+            self.ref[src] -= 1
+            s.blocks[pos // BLOCK] = dst
+        return self.append(seq_id, token), src, dst
+
+    def append(self, seq_id, token):
+        """Add one decoded token; returns its cache slot.  A partially filled block shared with a
+        fork must go through :meth:`append_cow`."""
+        s = self.seqs.get(seq_id)
+        if s is None:
+            raise AllocError("UNKNOWN_SEQ", str(seq_id))
+        pos = len(s.tokens)
+        if pos % BLOCK != 0 and self.ref[s.blocks[pos // BLOCK]] > 1:
+            raise AllocError("INVALID", "the block is shared with a fork: append with copy-on-write")
         if pos % BLOCK == 0:
             if not self.free:
                 raise AllocError("NO_BLOCKS", "append")

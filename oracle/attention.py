@@ -125,6 +125,16 @@ def kv_store_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slot_mappin
     return kc, vc, ks, vs
 
 
+def copy_blocks(caches, src, dst):
+    """Copy-on-write of shared blocks: block dst[i] of every cache array (K, V and, for int8, the
+    per-(block, head) scales) becomes a copy of block src[i].  Returns new arrays."""
+    out = [c.copy() for c in caches]
+    for a, b in zip(src, dst):
+        for c in out:
+            c[int(b)] = c[int(a)]
+    return out
+
+
 def gather(cache, table_row, length, head, scale=None):
     """Rows 0..length-1 of one sequence for one KV head, as float64 ``[length][D]``."""
     rows = np.empty((length, cache.shape[-1]), dtype=np.float64)

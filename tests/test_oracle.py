@@ -215,6 +215,91 @@ def test_random_ops_keep_invariants():
         a.check_invariants()
 
 
+def test_fork_shares_every_block_and_copies_on_write():
+    a = _alloc(10)
+    a.add_seq(0, list(range(300)))            # blocks 0 (full) and 1 (44 tokens)
+    a.fork(0, 1)
+    assert a.seqs[1].blocks == [0, 1] and a.ref[:2] == [2, 2] and a.seq_len(1) == 300
+    with pytest.raises(OA.AllocError) as e:
+        a.append(1, 7)                        # shared partial block: only with copy-on-write
+    assert e.value.kind == "INVALID"
+    slot, src, dst = a.append_cow(1, 7)       # the child moves to the next fresh block
+    assert (src, dst) == (1, 2) and slot == 2 * 256 + 44
+    assert a.seqs[1].blocks == [0, 2] and a.ref[:3] == [2, 1, 1]
+    slot, src, dst = a.append_cow(0, 8)       # the parent now owns block 1 alone: no copy
+    assert (src, dst) == (-1, -1) and slot == 1 * 256 + 44
+    a.fork(1, 2)
+    for t in range(211):                      # child 2 fills the shared block's copy; the first append copies
+        slot, src, dst = a.append_cow(2, t)
+        assert (src, dst) == ((2, 3) if t == 0 else (-1, -1))
+    assert a.seqs[2].blocks == [0, 3] and a.seq_len(2) == 512
+    slot, src, dst = a.append_cow(2, 0)       # a full last block: a fresh one, nothing to copy
+    assert (src, dst) == (-1, -1) and a.seqs[2].blocks == [0, 3, 4]
+    for sid in (0, 1, 2):
+        a.free_seq(sid)
+    a.check_invariants()
+    assert a.num_free() == 10
+
+
+def test_random_ops_with_forks_keep_invariants():
+    rnd = random.Random(4)
+    a = _alloc(48, order=list(np.random.default_rng(4).permutation(48)))
+    live, nid = [], 0
+    for _ in range(600):
+        op = rnd.random()
+        try:
+            if op < 0.2:
+                n = rnd.randint(1, 700)
+                a.add_seq(nid, [rnd.randint(0, 3) for _ in range(n)])
+                live.append(nid)
+                nid += 1
+            elif op < 0.35 and live:
+                a.fork(rnd.choice(live), nid)
+                live.append(nid)
+                nid += 1
+            elif op < 0.85 and live:
+                a.append_cow(rnd.choice(live), rnd.randint(0, 3))
+            elif live:
+                a.free_seq(live.pop(rnd.randrange(len(live))))
+        except OA.AllocError as e:
+            assert e.kind == "NO_BLOCKS"
+        a.check_invariants()
+
+
+def test_copy_on_write_keeps_each_sequence_its_own_keys():
+    """A forked sequence attends exactly what its parent did until they diverge; after each
+    appends its own token, each sees its own (the copy holds the shared rows, the original block
+    keeps the other owner's row)."""
+    rng = np.random.default_rng(5)
+    Hkv, D, nb = 2, 4, 8
+    a = _alloc(nb)
+    kc = rng.standard_normal((nb, Hkv, 256, D))
+    vc = rng.standard_normal((nb, Hkv, 256, D))
+    a.add_seq(0, list(range(300)))
+    a.fork(0, 1)
+    q = rng.standard_normal((2, 2, D))
+    bt = np.array(a.block_tables([0, 1], 3))
+    before = OT.decode(q, kc, vc, bt, [300, 300], 0.5)
+    assert np.array_equal(before[0], OT.decode(q[:1], kc, vc, bt[:1], [300], 0.5)[0])
+    assert np.array_equal(OT.decode(q[1:], kc, vc, bt[1:], [300], 0.5)[0], OT.decode(q[1:], kc, vc, bt[:1], [300], 0.5)[0])
+    new = rng.standard_normal((2, Hkv, D))
+    slots = []
+    for sid in (1, 0):
+        slot, src, dst = a.append_cow(sid, 9)
+        if src >= 0:
+            kc, vc = OT.copy_blocks([kc, vc], [src], [dst])
+        slots.append(slot)
+    kc, vc = OT.kv_store(kc, vc, new[[1, 0]], new[[1, 0]], slots)
+    bt = np.array(a.block_tables([0, 1], 3))
+    assert bt[0, 1] != bt[1, 1] and bt[0, 0] == bt[1, 0]
+    for b in (0, 1):
+        k_seq = OT.gather(kc, bt[b], 301, 0)
+        k_par = OT.gather(kc, np.array(a.block_tables([0], 3))[0], 300, 0)
+        assert np.array_equal(k_seq[:300], k_par)            # shared history, bit for bit
+        assert np.array_equal(k_seq[300], new[b, 0])         # its own new token
+    a.check_invariants()
+
+
 # ------------------------------------------------------------------------- attention
 def _rand_paged(rng, B, Hq, Hkv, D, lens, nb=None):
     """Random contiguous per-sequence K/V plus a random paged placement of them."""

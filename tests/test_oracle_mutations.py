@@ -233,9 +233,41 @@ def _prefill_window_variant(shift=0, from_start=False):
     return prefill
 
 
+def _append_cow_never_copies(self, seq_id, token):
+    s = self.seqs[seq_id]
+    pos = len(s.tokens)
+    if pos % BLOCK != 0:
+        self.ref[s.blocks[pos // BLOCK]] = 1   # pretend it is private: writes into the shared block
+    return OA_append_orig(self, seq_id, token), -1, -1
+
+
+def _append_cow_keeps_ref(self, seq_id, token):
+    s = self.seqs.get(seq_id)
+    pos = len(s.tokens)
+    src = dst = -1
+    if pos % BLOCK != 0 and self.ref[s.blocks[pos // BLOCK]] > 1:
+        src = s.blocks[pos // BLOCK]
+        dst = self._pop_fresh()
+        s.blocks[pos // BLOCK] = dst            # the shared block keeps its old count
+        self.ref[src] += 0
+        saved, self.ref[src] = self.ref[src], 1
+        slot = OA_append_orig(self, seq_id, token)
+        self.ref[src] = saved
+        return slot, src, dst
+    return OA_append_orig(self, seq_id, token), src, dst
+
+
+def _fork_no_refs(self, parent_id, child_id):
+    p = self.seqs[parent_id]
+    c = OA._Seq()
+    c.blocks, c.tokens, c.n_cached, c.last_hash = list(p.blocks), list(p.tokens), len(p.tokens), p.last_hash
+    self.seqs[child_id] = c
+
+
 OT_attend_orig = OT.attend
 OT_gather_orig = OT.gather
 OA_block_hash_orig = OA.block_hash
+OA_append_orig = OA.Allocator.append
 
 ATTN_PINS = [
     P.test_hand_worked_example,
@@ -270,6 +302,11 @@ WINDOW_PINS = [
     P.test_windowed_prefill_equals_sdpa_with_band_mask,
     P.test_windowed_prefill_last_row_equals_windowed_decode,
 ]
+FORK_PINS = [
+    P.test_fork_shares_every_block_and_copies_on_write,
+    P.test_random_ops_with_forks_keep_invariants,
+    P.test_copy_on_write_keeps_each_sequence_its_own_keys,
+]
 HASH_PINS = [lambda: [P.test_fnv1a64_published_vectors(d, e) for d, e in P._golden_fnv()],
              P.test_block_hash_closed_forms]
 
@@ -297,6 +334,9 @@ MUTANTS = {
                                                    QUANT_PINS),
     "int8 scale from the new rows only": (OT, "kv_store_quant", _store_quant_variant(keep_old=False), QUANT_PINS),
     "decode window one key short": (OT, "decode", _decode_window_short, WINDOW_PINS),
+    "copy-on-write never copies": (OA.Allocator, "append_cow", _append_cow_never_copies, FORK_PINS),
+    "copy-on-write keeps the shared block's count": (OA.Allocator, "append_cow", _append_cow_keeps_ref, FORK_PINS),
+    "fork takes no references": (OA.Allocator, "fork", _fork_no_refs, FORK_PINS),
     "prefill window one key long": (OT, "prefill", _prefill_window_variant(shift=-1), WINDOW_PINS),
     "prefill window one key short": (OT, "prefill", _prefill_window_variant(shift=1), WINDOW_PINS),
     "prefill window counted from the first key": (OT, "prefill", _prefill_window_variant(from_start=True),
