@@ -125,13 +125,20 @@ def kv_store_quant(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slot_mappin
     return kc, vc, ks, vs
 
 
-def copy_blocks(caches, src, dst):
-    """Copy-on-write of shared blocks: block dst[i] of every cache array (K, V and, for int8, the
-    per-(block, head) scales) becomes a copy of block src[i].  Returns new arrays."""
+def copy_blocks(caches, src, dst, rows=None):
+    """Copy-on-write of shared blocks (ocdem.com nano-vllm article, §2.1): block dst[i] of every
+    cache array (K, V and, for int8, the per-(block, head) scales) becomes a copy of block src[i].
+    With ``rows``, only rows 0..rows[i]-1 of each KV head's K/V tile are copied: the rows the
+    shared block holds when a sequence leaves it (its later rows are written before anything reads
+    them); per-block arrays such as scales are copied whole.  Returns new arrays."""
     out = [c.copy() for c in caches]
-    for a, b in zip(src, dst):
+    for i, (a, b) in enumerate(zip(src, dst)):
         for c in out:
-            c[int(b)] = c[int(a)]
+            if rows is not None and c.ndim == 4:
+                r = int(rows[i])
+                c[int(b), :, :r] = c[int(a), :, :r]
+            else:
+                c[int(b)] = c[int(a)]
     return out
 
 

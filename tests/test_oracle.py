@@ -286,8 +286,8 @@ def test_copy_on_write_keeps_each_sequence_its_own_keys():
     slots = []
     for sid in (1, 0):
         slot, src, dst = a.append_cow(sid, 9)
-        if src >= 0:
-            kc, vc = OT.copy_blocks([kc, vc], [src], [dst])
+        if src >= 0:  # the rows in use: the appended token's offset
+            kc, vc = OT.copy_blocks([kc, vc], [src], [dst], [slot % 256])
         slots.append(slot)
     kc, vc = OT.kv_store(kc, vc, new[[1, 0]], new[[1, 0]], slots)
     bt = np.array(a.block_tables([0, 1], 3))

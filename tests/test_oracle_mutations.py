@@ -264,6 +264,11 @@ def _fork_no_refs(self, parent_id, child_id):
     self.seqs[child_id] = c
 
 
+def _copy_one_row_short(caches, src, dst, rows=None):
+    return OT_copy_blocks_orig(caches, src, dst, None if rows is None else [max(0, int(r) - 1) for r in rows])
+
+
+OT_copy_blocks_orig = OT.copy_blocks
 OT_attend_orig = OT.attend
 OT_gather_orig = OT.gather
 OA_block_hash_orig = OA.block_hash
@@ -337,6 +342,7 @@ MUTANTS = {
     "copy-on-write never copies": (OA.Allocator, "append_cow", _append_cow_never_copies, FORK_PINS),
     "copy-on-write keeps the shared block's count": (OA.Allocator, "append_cow", _append_cow_keeps_ref, FORK_PINS),
     "fork takes no references": (OA.Allocator, "fork", _fork_no_refs, FORK_PINS),
+    "copy-on-write copies one row short": (OT, "copy_blocks", _copy_one_row_short, FORK_PINS),
     "prefill window one key long": (OT, "prefill", _prefill_window_variant(shift=-1), WINDOW_PINS),
     "prefill window one key short": (OT, "prefill", _prefill_window_variant(shift=1), WINDOW_PINS),
     "prefill window counted from the first key": (OT, "prefill", _prefill_window_variant(from_start=True),
