@@ -7,6 +7,9 @@ slots go to the device in one pinned copy, kv_store writes the new K/V rows, and
 attend over the whole paged context.  Contexts therefore grow by one token per step, as in a real
 decode loop.  All inputs are seeded synthetic data and are resident in HBM before timing starts.
 
+``--config beam_decode`` times beam search (64 requests x 4 beams that re-fork every step, with
+copy-on-write of shared partial blocks) over the same context mix.
+
 ``--config prefill_prefix`` times the chunked varlen prefill workload instead (32 prompts with a
 shared 512-token prefix per group of 8, chunks of at most 4096 new tokens): one step is the
 whole workload -- every chunk's store and prefill attention.
@@ -464,6 +467,124 @@ def bench_int8_store(args, cfg):
     )
 
 
+def bench_beam(args, cfg):
+    """Beam search over decode prompts: every step each request's new beams fork from seeded parents
+    among its current beams (ocdem.com nano-vllm article, §2.1: the sequences of a request share
+    blocks), the old beams end, one token is appended per beam with copy-on-write (all but the last
+    appender into a shared partial block copy its rows in use), then the store and the attention
+    over every beam."""
+    import torch
+    import workloads as W
+    from paged_kv_cache_kvcache_amd import BF16
+    from paged_kv_cache_kvcache_amd import runner as R
+
+    dev = torch.device("cuda:0")
+    NR, NBM, Hq, Hkv, D = cfg["B"], cfg["beams"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    B = NR * NBM
+    nsteps = args.warmup + args.steps
+    wl = W.decode_workload(cfg, args.seed)
+    lens = wl["lens"]
+    # prompts, plus per beam a private partial block and the blocks its appends open
+    nb = W.pool_blocks(cfg, lens) + B * (2 + -(-nsteps // 256))
+    kv = R.PagedKV(nb, Hkv, D, BF16, W.free_order(cfg, args.seed, nb), device=dev)
+    R.admit_and_store(kv, list(range(NR)), [s["tokens"] for s in wl["seqs"]], [s["k"] for s in wl["seqs"]],
+                      [s["v"] for s in wl["seqs"]])
+    max_ctx = max(lens) + nsteps
+    batch = R.DecodeBatch(kv, Hq, list(range(B)), max_ctx, args.max_splits, cow=True)
+    steps = []
+    for s in range(nsteps):
+        inp = W.decode_step_inputs(cfg, args.seed, s, B)
+        steps.append(dict(tokens=inp["tokens"], parents=W.beam_parents(cfg, args.seed, s),
+                          q=R.bf16_tensor(inp["q"], dev), k=R.bf16_tensor(inp["k"], dev),
+                          v=R.bf16_tensor(inp["v"], dev)))
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    row_bytes = Hkv * D * 2
+    stream = torch.cuda.current_stream()
+    mk = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+    ev_copy, ev_dec = mk(), mk()
+    state = dict(beams=[[r] for r in range(NR)], next_id=NR)
+    log_rows, log_copies, log_tables = [], [], []
+
+    def unique_rows(tab, lens):
+        """Rows of the distinct physical blocks the step's beams attend (each block read once)."""
+        used = {}
+        for row, L in zip(tab, lens):
+            for j in range(-(-int(L) // 256)):
+                b = int(row[j])
+                used[b] = max(used.get(b, 0), min(256, int(L) - 256 * j))
+        return sum(used.values())
+
+    def run(i, timed_idx=None):
+        st = steps[i]
+        alloc = kv.alloc
+        nid = state["next_id"]
+        par = [cur[int(p) % len(cur)] for cur, ps in zip(state["beams"], st["parents"]) for p in ps]
+        new = list(range(nid, nid + B))
+        alloc.fork_batch(par, new)
+        alloc.free_batch([sid for cur in state["beams"] for sid in cur])
+        state["beams"] = [new[r * NBM:(r + 1) * NBM] for r in range(NR)]
+        state["next_id"] = nid + B
+        slots, src, dst, rows = alloc.append_batch_cow(new, st["tokens"])
+        batch.set_sequences(new)
+        batch.upload_step_metadata(slots, (src, dst, rows))
+        if timed_idx is not None:
+            ev_copy[timed_idx][0].record(stream)
+        batch.copy_blocks()
+        if timed_idx is not None:
+            ev_copy[timed_idx][1].record(stream)
+        kv.store(batch.slots, st["k"], st["v"])
+        if timed_idx is not None:
+            ev_dec[timed_idx][0].record(stream)
+        batch.attend(st["q"], scale, out)
+        if timed_idx is not None:
+            ev_dec[timed_idx][1].record(stream)
+            log_rows.append(int(rows.sum()))
+            log_copies.append(len(src))
+            log_tables.append((batch.host_block_tables.copy(), batch.host_context_lens.copy()))
+
+    gc.collect()
+    gc.disable()
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        run(args.warmup + j, j)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gc.enable()
+    dec_s = sum(a.elapsed_time(b) for a, b in ev_dec) / args.steps / 1e3
+    copy_s = sum(a.elapsed_time(b) for a, b in ev_copy) / args.steps / 1e3
+    dec_bytes = sum(int(lens.sum()) for _, lens in log_tables) / args.steps * row_bytes * 2
+    # HBM bytes: beams of one request share all but their last blocks, so each distinct block once
+    uniq_bytes = sum(unique_rows(tab, lens) for tab, lens in log_tables) / args.steps * row_bytes * 2
+    # copy traffic: the rows in use of each copied block, read and written, for K and V
+    copy_bytes = sum(log_rows) / args.steps * row_bytes * 2 * 2
+    dec_gbs, copy_gbs = dec_bytes / dec_s / 1e9, copy_bytes / max(copy_s, 1e-12) / 1e9
+    uniq_gbs = uniq_bytes / dec_s / 1e9
+    log(f"[bench] beam: {NR} requests x {NBM} beams; {sum(log_copies) / args.steps:.1f} block copies/step "
+        f"({copy_bytes / 1e6:.1f} MB, {copy_s * 1e6:.1f} us, {copy_gbs:.0f} GB/s); decode {dec_s * 1e6:.1f} us "
+        f"({uniq_gbs:.0f} GB/s of distinct blocks, {dec_gbs:.0f} GB/s counting every beam's reads); "
+        f"step {elapsed / args.steps * 1e3:.3f} ms")
+    return dict(
+        metric="beam-search decode: tokens/s (one per beam) + decode KV GB/s; copy-on-write GB/s",
+        value=B * args.steps / elapsed, unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=elapsed / args.steps * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=cfg["name"], requests=NR, beams=NBM, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]",
+                    q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256, seed=args.seed),
+        decode_kernel_us=dec_s * 1e6, decode_gbs_all_beam_reads=dec_gbs,
+        copies_per_step=sum(log_copies) / args.steps, copy_kernel_us=copy_s * 1e6,
+        copy=dict(bound="hbm", achieved=copy_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=copy_gbs / HBM_PEAK_GBS,
+                  bytes_per_step=copy_bytes),
+        roofline=dict(bound="hbm", achieved=uniq_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=uniq_gbs / HBM_PEAK_GBS,
+                      traffic=None, kernel="decode over every beam's context (bytes: distinct blocks once)",
+                      bytes_per_launch=uniq_bytes),
+    )
+
+
 def cpu_baseline_prefill_rows(wl, budget_s=10.0):
     """Prompts longer than a chunk: the oracle's causal attention (plain definition, fp64) for the
     last rows of the longest prompt, one row at a time, for about ``budget_s`` seconds."""
@@ -544,6 +665,8 @@ def main():
         res = bench_decode(args, cfg)
     elif cfg["kind"] == "store":
         res = bench_int8_store(args, cfg)
+    elif cfg["kind"] == "beam":
+        res = bench_beam(args, cfg)
     else:
         res = bench_prefill(args, cfg)
     print(json.dumps(res), flush=True)

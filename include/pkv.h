@@ -102,7 +102,14 @@ const char* pkv_version(void);
  *     a block is hashed and registered when it becomes full.
  *   - free_seq: references are dropped in reverse block order; a block whose
  *     count reaches 0 goes to the tail of the free deque.
- *   - add_seq, append and append_batch are atomic: on failure nothing changes.
+ *   - fork: the child takes the parent's tokens, blocks and hash chain; every block
+ *     gains a reference, and the child's whole length counts as cached.
+ *   - append_batch_cow: before a token lands in a partially filled block whose
+ *     count exceeds 1, the sequence drops that reference and takes the head of
+ *     the free deque instead (the caller copies the old block into it); plain
+ *     append and append_batch refuse such a token (PKV_ERR_INVALID).
+ *   - add_seq, append, append_batch and append_batch_cow are atomic: on failure
+ *     nothing changes.
  *   - With prefix_cache = 0 nothing is hashed.
  *
  * A handle is not thread-safe: use one thread per handle.
@@ -127,7 +134,28 @@ int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t token, int32_t* s
 int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32_t* tokens,
                            int32_t n, int32_t* slots);
 
+/* Parallel sampling and beam search (ocdem.com nano-vllm article, §2.1: the sequences of one
+ * request share physical blocks through reference counts).  pkv_alloc_fork admits child_id as
+ * a copy of parent_id that shares all of its blocks (PKV_ERR_DUP_SEQ for an existing child,
+ * checked first, PKV_ERR_UNKNOWN_SEQ for a missing parent).  pkv_alloc_append_batch_cow is
+ * pkv_alloc_append_batch with copy-on-write: copy_src[k], copy_dst[k] (host int32[n], k <
+ * *n_copies) receive the block pairs whose contents the caller must copy (pkv_copy_blocks)
+ * before storing the batch's new rows, and copy_rows[k] the rows of the source in use (the
+ * appending sequence's offset in the block, 1..255); a pair appears in the order the batch
+ * reached it, and no destination is a source of another pair.  PKV_ERR_NO_BLOCKS when the fresh blocks for new
+ * block starts and copies exceed the free deque. */
+int pkv_alloc_fork(pkv_allocator* a, int64_t parent_id, int64_t child_id);
+/* A beam search step's forks in one call: pkv_alloc_fork(parent_ids[i], child_ids[i]) for i < n
+ * in order (a child may be the parent of a later entry), atomically. */
+int pkv_alloc_fork_batch(pkv_allocator* a, const int64_t* parent_ids, const int64_t* child_ids, int32_t n);
+int pkv_alloc_append_batch_cow(pkv_allocator* a, const int64_t* seq_ids, const int32_t* tokens,
+                               int32_t n, int32_t* slots, int32_t* copy_src, int32_t* copy_dst,
+                               int32_t* copy_rows, int32_t* n_copies);
+
 int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id);
+/* pkv_alloc_free_seq(seq_ids[i]) for i < n in order, atomically (PKV_ERR_UNKNOWN_SEQ when an id is
+ * unknown or repeated). */
+int pkv_alloc_free_batch(pkv_allocator* a, const int64_t* seq_ids, int32_t n);
 int pkv_alloc_num_free(const pkv_allocator* a, int32_t* out);
 
 /* Rows of int32[n][max_blocks] (host): each sequence's physical blocks, padded with -1.
@@ -165,7 +193,9 @@ int pkv_alloc_debug_constant_hash(pkv_allocator* a, int32_t enable, uint64_t val
  * k_cache / v_cache at that slot.  An exact copy: the rows must already be in the
  * cache dtype (f32, bf16 or int8 codes).  For int8 caches k_scale_new / v_scale_new
  * ([n][Hkv] fp32, device) are written to k_scale / v_scale at [slot / 256][h]; for
- * other dtypes all four scale pointers must be NULL.
+ * other dtypes all four scale pointers must be NULL.  A block holds one scale per KV
+ * head, so rows of one call that land in one block must carry equal scales, and slots
+ * must be distinct; otherwise which value is kept is unspecified.
  * k_new, v_new: device [n][Hkv][head_dim]; slot_mapping: device int32[n]; n may be 0.
  * ------------------------------------------------------------------------------------------ */
 int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const void* v_new,
@@ -201,6 +231,16 @@ int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new, const void
                        int32_t new_dtype, const int32_t* slot_mapping, int32_t n, const int32_t* runs,
                        int32_t n_runs, int32_t max_run, void* k_cache, void* v_cache, float* k_scale,
                        float* v_scale, void* stream);
+
+/* Copy-on-write block copies (ocdem.com nano-vllm article, §2.1): for k < n, rows 0..rows[k]-1
+ * of every KV head of physical block dst[k] in both caches become copies of those of block
+ * src[k] (the other rows are left as they are), and for int8 caches the block's k_scale / v_scale
+ * entries are copied.  src, dst: device int32[n], valid block ids, with no dst equal to any src
+ * or to another dst (pkv_alloc_append_batch_cow's pairs are such); rows: device int32[n] with
+ * values in 0..256, or NULL for whole blocks.  k_scale, v_scale: int8 caches only, else NULL.
+ * n may be 0. */
+int pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t* src, const int32_t* dst, const int32_t* rows,
+                    int32_t n, void* k_cache, void* v_cache, float* k_scale, float* v_scale, void* stream);
 
 /* The runs of a slot mapping for pkv_kv_store_quant (host): maximal groups of consecutive batch
  * rows whose slots are consecutive and in one block; rows with slot < 0 belong to none.

@@ -51,6 +51,10 @@ SIGNATURES = {
     "pkv_alloc_add_seq": (_i32, [_vp, _i64, _p32, _i32, _p32]),
     "pkv_alloc_append": (_i32, [_vp, _i64, _i32, _p32]),
     "pkv_alloc_append_batch": (_i32, [_vp, _p64, _p32, _i32, _p32]),
+    "pkv_alloc_fork": (_i32, [_vp, _i64, _i64]),
+    "pkv_alloc_fork_batch": (_i32, [_vp, _p64, _p64, _i32]),
+    "pkv_alloc_free_batch": (_i32, [_vp, _p64, _i32]),
+    "pkv_alloc_append_batch_cow": (_i32, [_vp, _p64, _p32, _i32, _p32, _p32, _p32, _p32, _p32]),
     "pkv_alloc_free_seq": (_i32, [_vp, _i64]),
     "pkv_alloc_num_free": (_i32, [_vp, _p32]),
     "pkv_alloc_block_tables": (_i32, [_vp, _p64, _i32, _i32, _p32, _p32]),
@@ -60,6 +64,7 @@ SIGNATURES = {
     "pkv_kv_store_quant": (_i32, [_pdesc, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pkv_alloc_prefill_segment_slots": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), _p32, _p32, _i32, _p32, _p32, _p32,
                                                 _i32, ctypes.POINTER(ctypes.c_int32)]),
+    "pkv_copy_blocks": (_i32, [_pdesc, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pkv_store_runs": (_i32, [_p32, _i32, _p32, _i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "pkv_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _p32, _p32]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -180,6 +185,43 @@ class Allocator:
                "pkv_alloc_append_batch")
         return slots
 
+    def fork(self, parent_id, child_id):
+        """Admit ``child_id`` sharing every block of ``parent_id`` (parallel sampling, beam search)."""
+        _check(lib().pkv_alloc_fork(self._h, int(parent_id), int(child_id)), "pkv_alloc_fork")
+
+    def fork_batch(self, parent_ids, child_ids):
+        """:meth:`fork` for each (parent, child) pair in order, atomically."""
+        par, pp = _host_i64(parent_ids)
+        chi, pc = _host_i64(child_ids)
+        if len(par) != len(chi):
+            raise ValueError("parent_ids and child_ids must have the same length")
+        _check(lib().pkv_alloc_fork_batch(self._h, pp, pc, len(par)), "pkv_alloc_fork_batch")
+
+    def free_batch(self, seq_ids):
+        """:meth:`free_seq` for each id in order, atomically."""
+        ids, pi = _host_i64(seq_ids)
+        _check(lib().pkv_alloc_free_batch(self._h, pi, len(ids)), "pkv_alloc_free_batch")
+
+    def append_batch_cow(self, seq_ids, tokens):
+        """:meth:`append_batch` with copy-on-write: (slots, copy_src, copy_dst, copy_rows) as int32
+        numpy arrays; the caller copies the rows in use of each block pair (:func:`copy_blocks`)
+        before storing the batch's rows."""
+        import numpy as np
+        ids, pi = _host_i64(seq_ids)
+        toks, pt = _host_i32(tokens)
+        n = len(ids)
+        slots = np.empty(n, dtype=np.int32)
+        src = np.empty(max(n, 1), dtype=np.int32)
+        dst = np.empty(max(n, 1), dtype=np.int32)
+        rows = np.empty(max(n, 1), dtype=np.int32)
+        nc = ctypes.c_int32()
+        _check(lib().pkv_alloc_append_batch_cow(self._h, pi, pt, n, slots.ctypes.data_as(_p32),
+                                                src.ctypes.data_as(_p32), dst.ctypes.data_as(_p32),
+                                                rows.ctypes.data_as(_p32), ctypes.byref(nc)),
+               "pkv_alloc_append_batch_cow")
+        k = nc.value
+        return slots, src[:k].copy(), dst[:k].copy(), rows[:k].copy()
+
     def free_seq(self, seq_id):
         _check(lib().pkv_alloc_free_seq(self._h, int(seq_id)), "pkv_alloc_free_seq")
 
@@ -242,6 +284,18 @@ def kv_store(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale_new=None, v_s
     _check(lib().pkv_kv_store(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_scale_new), _ptr(v_scale_new),
                               _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                               _stream(stream)), "pkv_kv_store")
+
+
+def copy_blocks(src, dst, k_cache, v_cache, rows=None, k_scale=None, v_scale=None, stream=None):
+    """Copy-on-write: rows 0..rows[i]-1 (all 256 when ``rows`` is None) of every KV head of physical
+    block dst[i] in both caches, and its int8 scales, become copies of block src[i]'s; src, dst,
+    rows device int32 [n]."""
+    desc = desc_of(k_cache)
+    n = int(src.shape[0])
+    if int(dst.shape[0]) != n or (rows is not None and int(rows.shape[0]) != n):
+        raise ValueError("src, dst and rows must have the same length")
+    _check(lib().pkv_copy_blocks(ctypes.byref(desc), _ptr(src), _ptr(dst), _ptr(rows), n, _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _stream(stream)), "pkv_copy_blocks")
 
 
 def store_runs(slot_mapping):

@@ -13,6 +13,7 @@
 #include <cstring>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -40,7 +41,8 @@ uint64_t chained_block_hash(uint64_t prev, const int32_t* toks) {
 
 struct Seq {
     std::vector<int32_t> blocks;
-    std::vector<int32_t> tokens;
+    std::vector<int32_t> tail;  // tokens of the partially filled last block (full blocks are hashed)
+    int32_t len = 0;            // tokens held
     int32_t n_cached = 0;
     uint64_t last_hash = 0;  // hash of the last full block (chain input for the next one)
 };
@@ -214,33 +216,45 @@ int pkv_alloc_add_seq(pkv_allocator* a, int64_t seq_id, const int32_t* tokens, i
         }
         if (s.hashed) seq.last_hash = s.h;
     }
-    seq.tokens.assign(tokens, tokens + n);
+    seq.len = n;
+    seq.tail.assign(tokens + size_t(n / kBlock) * kBlock, tokens + n);
     *n_cached = seq.n_cached;
     a->seqs.emplace(seq_id, std::move(seq));
     return PKV_OK;
 }
 
 static int32_t append_one(pkv_allocator* a, Seq& s, int32_t token) {
-    const int32_t pos = int32_t(s.tokens.size());
+    const int32_t pos = s.len;
     if (pos % kBlock == 0) s.blocks.push_back(a->pop_fresh());
-    s.tokens.push_back(token);
+    s.tail.push_back(token);
+    ++s.len;
     const int32_t slot = s.blocks[pos / kBlock] * kBlock + pos % kBlock;
-    if (a->prefix && s.tokens.size() % kBlock == 0) {
-        const size_t i = s.tokens.size() / kBlock - 1;
-        const int32_t* chunk = s.tokens.data() + i * kBlock;
-        const uint64_t h = a->hash_block(s.last_hash, chunk);
-        a->register_block(s.blocks[i], h, chunk);
-        s.last_hash = h;
+    if (s.len % kBlock == 0) {
+        if (a->prefix) {
+            const uint64_t h = a->hash_block(s.last_hash, s.tail.data());
+            a->register_block(s.blocks[pos / kBlock], h, s.tail.data());
+            s.last_hash = h;
+        }
+        s.tail.clear();
     }
     return slot;
+}
+
+// True when the next token of s lands in a partially filled block that another sequence holds.
+static bool needs_copy(const pkv_allocator* a, const Seq& s) {
+    const int32_t pos = s.len;
+    return pos % kBlock != 0 && a->ref[s.blocks[pos / kBlock]] > 1;
 }
 
 int pkv_alloc_append(pkv_allocator* a, int64_t seq_id, int32_t token, int32_t* slot) {
     PKV_REQUIRE(a != nullptr && slot != nullptr, PKV_ERR_INVALID, "NULL argument");
     auto it = a->seqs.find(seq_id);
     PKV_REQUIRE(it != a->seqs.end(), PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
-    PKV_REQUIRE(it->second.tokens.size() < size_t(INT32_MAX - 1), PKV_ERR_INVALID, "sequence too long");
-    if (it->second.tokens.size() % kBlock == 0 && a->nfree == 0)
+    PKV_REQUIRE(it->second.len < INT32_MAX - 1, PKV_ERR_INVALID, "sequence too long");
+    PKV_REQUIRE(!needs_copy(a, it->second), PKV_ERR_INVALID,
+                "sequence %lld: its last block is shared with a fork (use pkv_alloc_append_batch_cow)",
+                (long long)seq_id);
+    if (it->second.len % kBlock == 0 && a->nfree == 0)
         return fail(PKV_ERR_NO_BLOCKS, "no free block for sequence %lld", (long long)seq_id);
     *slot = append_one(a, it->second, token);
     return PKV_OK;
@@ -259,7 +273,10 @@ int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32
         auto it = a->seqs.find(seq_ids[i]);
         if (it == a->seqs.end())
             return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld (batch entry %d)", (long long)seq_ids[i], i);
-        auto ins = len.emplace(seq_ids[i], it->second.tokens.size());
+        PKV_REQUIRE(!needs_copy(a, it->second), PKV_ERR_INVALID,
+                    "sequence %lld: its last block is shared with a fork (use pkv_alloc_append_batch_cow)",
+                    (long long)seq_ids[i]);
+        auto ins = len.emplace(seq_ids[i], size_t(it->second.len));
         size_t& l = ins.first->second;
         if (l % kBlock == 0) ++need;
         ++l;
@@ -267,6 +284,88 @@ int pkv_alloc_append_batch(pkv_allocator* a, const int64_t* seq_ids, const int32
     if (need > a->nfree)
         return fail(PKV_ERR_NO_BLOCKS, "batch needs %d fresh blocks, %d free", need, a->nfree);
     for (int32_t i = 0; i < n; ++i) slots[i] = append_one(a, a->seqs.find(seq_ids[i])->second, tokens[i]);
+    return PKV_OK;
+}
+
+int pkv_alloc_fork(pkv_allocator* a, int64_t parent_id, int64_t child_id) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    PKV_REQUIRE(a->seqs.find(child_id) == a->seqs.end(), PKV_ERR_DUP_SEQ, "sequence %lld exists",
+                (long long)child_id);
+    auto it = a->seqs.find(parent_id);
+    PKV_REQUIRE(it != a->seqs.end(), PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)parent_id);
+    Seq c = it->second;  // blocks, length, partial-block tokens and hash chain
+    c.n_cached = c.len;
+    for (int32_t b : c.blocks) ++a->ref[b];
+    a->seqs.emplace(child_id, std::move(c));
+    return PKV_OK;
+}
+
+int pkv_alloc_fork_batch(pkv_allocator* a, const int64_t* parent_ids, const int64_t* child_ids, int32_t n) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    PKV_REQUIRE(n >= 0, PKV_ERR_INVALID, "n = %d", n);
+    if (n == 0) return PKV_OK;
+    PKV_REQUIRE(parent_ids && child_ids, PKV_ERR_INVALID, "NULL argument");
+    std::unordered_set<int64_t> born;  // children admitted earlier in this batch
+    for (int32_t i = 0; i < n; ++i) {
+        PKV_REQUIRE(a->seqs.find(child_ids[i]) == a->seqs.end() && born.insert(child_ids[i]).second,
+                    PKV_ERR_DUP_SEQ, "sequence %lld exists (batch entry %d)", (long long)child_ids[i], i);
+        PKV_REQUIRE(a->seqs.find(parent_ids[i]) != a->seqs.end() || (born.count(parent_ids[i]) &&
+                                                                     parent_ids[i] != child_ids[i]),
+                    PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld (batch entry %d)", (long long)parent_ids[i], i);
+    }
+    for (int32_t i = 0; i < n; ++i) pkv_alloc_fork(a, parent_ids[i], child_ids[i]);
+    return PKV_OK;
+}
+
+int pkv_alloc_append_batch_cow(pkv_allocator* a, const int64_t* seq_ids, const int32_t* tokens, int32_t n,
+                               int32_t* slots, int32_t* copy_src, int32_t* copy_dst, int32_t* copy_rows,
+                               int32_t* n_copies) {
+    PKV_REQUIRE(a != nullptr && n_copies != nullptr, PKV_ERR_INVALID, "NULL argument");
+    PKV_REQUIRE(n >= 0, PKV_ERR_INVALID, "n = %d", n);
+    *n_copies = 0;
+    if (n == 0) return PKV_OK;
+    PKV_REQUIRE(seq_ids && tokens && slots && copy_src && copy_dst && copy_rows, PKV_ERR_INVALID, "NULL argument");
+    // Dry run on the reference counts the batch touches: fresh blocks for block starts and for copies.
+    std::unordered_map<int64_t, std::pair<size_t, int32_t>> st;  // sequence -> (length, last block)
+    std::unordered_map<int32_t, int32_t> refs;                   // block -> reference count
+    int32_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = a->seqs.find(seq_ids[i]);
+        if (it == a->seqs.end())
+            return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld (batch entry %d)", (long long)seq_ids[i], i);
+        const Seq& s = it->second;
+        auto ins = st.emplace(seq_ids[i], std::make_pair(size_t(s.len),
+                                                         s.blocks.empty() ? -1 : s.blocks.back()));
+        auto& [l, last] = ins.first->second;
+        if (l % kBlock == 0) {
+            ++need;
+            last = -2 - i;  // a fresh block of this batch: private
+        } else if (last >= 0) {
+            auto r = refs.emplace(last, a->ref[last]).first;
+            if (r->second > 1) {
+                ++need;
+                --r->second;
+                last = -2 - i;
+            }
+        }
+        ++l;
+    }
+    if (need > a->nfree)
+        return fail(PKV_ERR_NO_BLOCKS, "batch needs %d fresh blocks, %d free", need, a->nfree);
+    for (int32_t i = 0; i < n; ++i) {
+        Seq& s = a->seqs.find(seq_ids[i])->second;
+        if (needs_copy(a, s)) {
+            const size_t k = size_t(s.len) / kBlock;
+            const int32_t src = s.blocks[k], dst = a->pop_fresh();
+            --a->ref[src];
+            s.blocks[k] = dst;
+            copy_src[*n_copies] = src;
+            copy_dst[*n_copies] = dst;
+            copy_rows[*n_copies] = s.len % kBlock;
+            ++*n_copies;
+        }
+        slots[i] = append_one(a, s, tokens[i]);
+    }
     return PKV_OK;
 }
 
@@ -278,6 +377,19 @@ int pkv_alloc_free_seq(pkv_allocator* a, int64_t seq_id) {
     for (auto r = bl.rbegin(); r != bl.rend(); ++r)
         if (--a->ref[*r] == 0) a->push_back(*r);
     a->seqs.erase(it);
+    return PKV_OK;
+}
+
+int pkv_alloc_free_batch(pkv_allocator* a, const int64_t* seq_ids, int32_t n) {
+    PKV_REQUIRE(a != nullptr, PKV_ERR_INVALID, "allocator is NULL");
+    PKV_REQUIRE(n >= 0, PKV_ERR_INVALID, "n = %d", n);
+    if (n == 0) return PKV_OK;
+    PKV_REQUIRE(seq_ids != nullptr, PKV_ERR_INVALID, "NULL argument");
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < n; ++i)
+        PKV_REQUIRE(a->seqs.find(seq_ids[i]) != a->seqs.end() && seen.insert(seq_ids[i]).second,
+                    PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld (batch entry %d)", (long long)seq_ids[i], i);
+    for (int32_t i = 0; i < n; ++i) pkv_alloc_free_seq(a, seq_ids[i]);
     return PKV_OK;
 }
 
@@ -307,7 +419,7 @@ int pkv_alloc_block_tables(const pkv_allocator* a, const int64_t* seq_ids, int32
         const size_t nb = s.blocks.size();
         std::copy(s.blocks.begin(), s.blocks.end(), row);
         std::fill(row + nb, row + max_blocks, -1);
-        if (context_lens) context_lens[i] = int32_t(s.tokens.size());
+        if (context_lens) context_lens[i] = s.len;
     }
     return PKV_OK;
 }
@@ -322,7 +434,7 @@ int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int3
         auto it = a->seqs.find(seq_ids[i]);
         if (it == a->seqs.end())
             return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
-        total += int64_t(it->second.tokens.size()) - it->second.n_cached;
+        total += int64_t(it->second.len) - it->second.n_cached;
     }
     if (total > cap) return fail(PKV_ERR_SMALL_BUFFER, "%lld new tokens > slot capacity %d", (long long)total, cap);
     PKV_REQUIRE(total == 0 || slot_mapping != nullptr, PKV_ERR_INVALID, "slot_mapping is NULL");
@@ -330,7 +442,7 @@ int pkv_alloc_prefill_slots(const pkv_allocator* a, const int64_t* seq_ids, int3
     cu_seqlens_q[0] = 0;
     for (int32_t i = 0; i < n; ++i) {
         const Seq& s = a->seqs.find(seq_ids[i])->second;
-        const int32_t len = int32_t(s.tokens.size());
+        const int32_t len = s.len;
         for (int32_t p = s.n_cached; p < len; ++p) slot_mapping[k++] = s.blocks[p / kBlock] * kBlock + p % kBlock;
         cu_seqlens_q[i + 1] = k;
         seqlens_k[i] = len;
@@ -351,7 +463,7 @@ int pkv_alloc_prefill_segment_slots(const pkv_allocator* a, const int64_t* seq_i
         auto it = a->seqs.find(seq_ids[i]);
         if (it == a->seqs.end())
             return fail(PKV_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
-        const int32_t n_new = int32_t(it->second.tokens.size()) - it->second.n_cached;
+        const int32_t n_new = it->second.len - it->second.n_cached;
         PKV_REQUIRE(0 <= starts[i] && starts[i] <= ends[i] && ends[i] <= n_new, PKV_ERR_INVALID,
                     "segment [%d, %d) of sequence %lld with %d new tokens", starts[i], ends[i],
                     (long long)seq_ids[i], n_new);

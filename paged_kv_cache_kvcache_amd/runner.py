@@ -9,7 +9,7 @@ libpkv; this module only moves arrays.
 import numpy as np
 import torch
 
-from . import (BF16, BLOCK, F32, I8, Allocator, decode_store_attend, decode_workspace_bytes, kv_store,
+from . import (BF16, BLOCK, F32, I8, Allocator, copy_blocks, decode_store_attend, decode_workspace_bytes, kv_store,
                kv_store_quant, paged_attn_decode, paged_attn_prefill)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
@@ -57,12 +57,20 @@ class PagedKV:
         :func:`store_runs` gives them, uploaded (built from a host copy of ``slots`` when None)."""
         kv_store_quant(k_rows, v_rows, slots, self.k_cache, self.v_cache, self.k_scale, self.v_scale, runs=runs)
 
+    def copy_on_write(self, src, dst, rows):
+        """Enqueue the block copies src[i] -> dst[i] of rows 0..rows[i]-1 (host int32, from
+        append_batch_cow) on the current stream; they must precede the store of the batch's rows."""
+        n = len(src)
+        if n:
+            t = _to_dev(np.concatenate([src, dst, rows]).astype(np.int32), self.device)
+            copy_blocks(t[:n], t[n:2 * n], self.k_cache, self.v_cache, t[2 * n:], self.k_scale, self.v_scale)
+
 
 class DecodeBatch:
     """A batch of sequences in decode: history admitted and stored, then one token per step
     (``fused``: the step's store and attention in one launch, pkv_decode_store_attend)."""
 
-    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False, window=0):
+    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False, window=0, cow=False):
         self.kv = kv
         self.Hq = int(Hq)
         self.ids = np.asarray(seq_ids, dtype=np.int64)
@@ -72,42 +80,72 @@ class DecodeBatch:
         self.max_splits = max_splits
         self.fused = fused
         self.window = int(window)  # > 0: sliding-window attention over the last `window` keys
+        self.cow = bool(cow)  # sequences share blocks (forks): appends copy shared partial blocks
         if self.fused and self.window:
             raise ValueError("the fused store+attend step has no sliding window")
         dev = kv.device
         # pinned staging for the per-step metadata: slots[B] | lens[B] | order[B] | tables[B][max_blocks]
-        self._pin = torch.empty(3 * self.B + self.B * self.max_blocks, dtype=torch.int32).pin_memory()
+        # and, with cow, the step's block copies: src[B] | dst[B] | rows[B]
+        nmeta = 3 * self.B + self.B * self.max_blocks
+        self._pin = torch.empty(nmeta + (3 * self.B if self.cow else 0), dtype=torch.int32).pin_memory()
         self._meta = torch.empty_like(self._pin, device=dev)
         self._copied = torch.cuda.Event()
         self._copied.record()
         self.slots = self._meta[:self.B]
         self.context_lens = self._meta[self.B:2 * self.B]
         self.seq_order = self._meta[2 * self.B:3 * self.B]
-        self.block_tables = self._meta[3 * self.B:].view(self.B, self.max_blocks)
+        self.block_tables = self._meta[3 * self.B:nmeta].view(self.B, self.max_blocks)
+        self._cow = self._meta[nmeta:]
+        self.n_copies = 0
         nbytes = decode_workspace_bytes(self.B, self.Hq, kv.D, kv.Hkv, self.max_context_len, max_splits)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
-    def upload_step_metadata(self, slots):
-        """Block tables and lengths of every sequence plus the new tokens' slots: one pinned H2D copy."""
+    def set_sequences(self, seq_ids):
+        """Point the batch at another set of B admitted sequences (e.g. the next step's beams)."""
+        ids = np.asarray(seq_ids, dtype=np.int64)
+        if len(ids) != self.B:
+            raise ValueError(f"the batch holds {self.B} sequences, got {len(ids)}")
+        self.ids = ids
+
+    def upload_step_metadata(self, slots, copies=None):
+        """Block tables and lengths of every sequence plus the new tokens' slots (and, with cow, the
+        step's block copies (src, dst, rows)): one pinned H2D copy."""
         self._copied.synchronize()  # the previous copy has left the staging buffer
         pin = self._pin.numpy()
         B, mb = self.B, self.max_blocks
         pin[:B] = slots
-        tab = pin[3 * B:].reshape(B, mb)
+        if copies is not None:
+            n = self.n_copies = len(copies[0])
+            cow = pin[3 * B + B * mb:]
+            for i, c in enumerate(copies):
+                cow[i * B:i * B + n] = c
+        tab = pin[3 * B:3 * B + B * mb].reshape(B, mb)
         lens = pin[B:2 * B]
         self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=lens)
+        self.host_context_lens, self.host_block_tables = lens, tab  # valid until the next upload
         pin[2 * B:3 * B] = np.argsort(-lens, kind="stable")  # longest contexts launch first
         self._meta.copy_(self._pin, non_blocking=True)
         self._copied.record()
 
     def step(self, tokens, q, k_new, v_new, softmax_scale, out=None, k_scale_new=None, v_scale_new=None):
         """One decode step: append one token per sequence, store its K/V, attend.  Returns out [B][Hq][D]."""
-        slots = self.kv.alloc.append_batch(self.ids, tokens)
-        self.upload_step_metadata(slots)
+        if self.cow:
+            slots, src, dst, rows = self.kv.alloc.append_batch_cow(self.ids, tokens)
+            self.upload_step_metadata(slots, (src, dst, rows))
+            self.copy_blocks()
+        else:
+            self.upload_step_metadata(self.kv.alloc.append_batch(self.ids, tokens))
         if self.fused:
             return self.store_attend(q, k_new, v_new, softmax_scale, out, k_scale_new, v_scale_new)
         self.kv.store(self.slots, k_new, v_new, k_scale_new, v_scale_new)
         return self.attend(q, softmax_scale, out)
+
+    def copy_blocks(self):
+        """The uploaded step's copy-on-write block copies (must precede the store)."""
+        n, B, kv = self.n_copies, self.B, self.kv
+        if n:
+            c = self._cow
+            copy_blocks(c[:n], c[B:B + n], kv.k_cache, kv.v_cache, c[2 * B:2 * B + n], kv.k_scale, kv.v_scale)
 
     def store_attend(self, q, k_new, v_new, softmax_scale, out=None, k_scale_new=None, v_scale_new=None):
         """The step's store of the new tokens and its attention, in one launch."""

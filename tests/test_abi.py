@@ -174,3 +174,16 @@ def test_prefill_rejects_bad_descriptor():
     rc = P.lib().pkv_paged_attn_prefill(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE, 1,
                                         0.1, 1, FAKE, None)
     assert rc == P.ERR_UNSUPPORTED
+
+
+def test_copy_blocks_rejects_bad_arguments():
+    def call(desc, n=2, ptr=FAKE, scales=(None, None)):
+        return P.lib().pkv_copy_blocks(ctypes.byref(desc), ptr, ptr, None, n, ptr, ptr, scales[0], scales[1], None)
+
+    assert call(_desc(), n=-1) == P.ERR_INVALID
+    assert call(_desc(), ptr=None) == P.ERR_INVALID
+    assert call(_desc(), scales=(FAKE, FAKE)) == P.ERR_INVALID          # only int8 takes scales
+    assert call(_desc(kv_dtype=P.I8)) == P.ERR_INVALID                  # int8 needs them
+    assert call(_desc(kv_dtype=P.I8), scales=(FAKE, None)) == P.ERR_INVALID
+    assert call(_desc(head_dim=80)) == P.ERR_UNSUPPORTED
+    assert call(_desc(), n=0, ptr=None) == P.OK                         # nothing to copy

@@ -222,3 +222,154 @@ def test_segment_slots_reject_bad_segments():
         native.prefill_segment_slots([0], [0], [300], 100)     # capacity
     cu, lk, slots = native.prefill_segment_slots([0, 0], [0, 256], [256, 300], 300)
     assert cu.tolist() == [0, 256, 300] and lk.tolist() == [256, 300] and slots.tolist() == list(range(300))
+
+
+def _oracle_batch_cow(oracle, ids, toks):
+    """The oracle's append_cow one token at a time, applied atomically (restored on failure)."""
+    import copy
+    snap = copy.deepcopy(oracle.__dict__)
+    try:
+        res = [oracle.append_cow(i, t) for i, t in zip(ids, toks)]
+    except OA.AllocError:
+        oracle.__dict__.clear()
+        oracle.__dict__.update(snap)
+        raise
+    slots = [r[0] for r in res]
+    cop = [r for r in res if r[1] >= 0]
+    return slots, [r[1] for r in cop], [r[2] for r in cop], [r[0] % 256 for r in cop]
+
+
+@pytest.mark.parametrize("seed,prefix", [(10, True), (11, False), (12, True)])
+def test_random_operations_with_forks_match_bit_for_bit(seed, prefix):
+    rnd = random.Random(seed)
+    native, oracle = _pair(40, seed, prefix)
+    live, nid, copies = [], 0, 0
+    shared = [rnd.randint(0, 50) for _ in range(600)]
+    for _ in range(400):
+        op = rnd.random()
+        if op < 0.15:
+            n = rnd.randint(1, 700)
+            share = rnd.choice([0, 256, 512])
+            toks = shared[:min(n, share)] + [rnd.randint(0, 10 ** 6) for _ in range(max(0, n - share))]
+            if _call(lambda: native.add_seq(nid, toks), lambda: oracle.add_seq(nid, toks)) is not None:
+                live.append(nid)
+            nid += 1
+        elif op < 0.3 and live:
+            parent = rnd.choice(live + [nid + 5])
+            child = rnd.choice([nid, live[0]])
+            _call(lambda: native.fork(parent, child), lambda: oracle.fork(parent, child))
+            if child == nid:
+                if parent in live:
+                    live.append(nid)
+                nid += 1
+        elif op < 0.65 and live:
+            ids = [rnd.choice(live) for _ in range(rnd.randint(1, 8))]
+            toks = [rnd.randint(0, 9) for _ in ids]
+            try:
+                expect = _oracle_batch_cow(oracle, ids, toks)
+            except OA.AllocError as e:
+                with pytest.raises(P.PkvError) as ne:
+                    native.append_batch_cow(ids, toks)
+                assert ne.value.kind == e.kind
+            else:
+                got = native.append_batch_cow(ids, toks)
+                assert [g.tolist() for g in got] == list(expect)
+                copies += len(expect[1])
+        elif op < 0.75 and live:
+            # plain appends agree with the oracle, refusals of shared partial blocks included
+            sid = rnd.choice(live)
+            _call(lambda: native.append(sid, 3), lambda: oracle.append(sid, 3))
+            ids = [rnd.choice(live) for _ in range(3)]
+            shared_tail = any(oracle.seq_len(i) % 256 and oracle.ref[oracle.seqs[i].blocks[oracle.seq_len(i) // 256]] > 1
+                              for i in ids)
+            if shared_tail:
+                with pytest.raises(P.PkvError) as ne:
+                    native.append_batch(ids, [1, 2, 3])
+                assert ne.value.kind == "INVALID"
+            else:
+                try:
+                    expect = _oracle_batch_cow(oracle, ids, [1, 2, 3])
+                except OA.AllocError as e:
+                    with pytest.raises(P.PkvError) as ne:
+                        native.append_batch(ids, [1, 2, 3])
+                    assert ne.value.kind == e.kind
+                else:
+                    assert expect[1] == []  # appends never make a block shared
+                    assert native.append_batch(ids, [1, 2, 3]).tolist() == expect[0]
+        elif live:
+            sid = live.pop(rnd.randrange(len(live)))
+            _call(lambda: native.free_seq(sid), lambda: oracle.free_seq(sid))
+        _same_state(native, oracle, live, 64)
+        if live:
+            cu, lk, slots = native.prefill_slots(live, 100000)
+            ocu, olk, oslots = oracle.prefill_slots(live)
+            assert cu.tolist() == ocu and lk.tolist() == olk and slots.tolist() == oslots
+        oracle.check_invariants()
+    assert copies > 0
+
+
+def test_fork_errors_and_copy_pairs():
+    native, oracle = _pair(8)
+    native.add_seq(0, list(range(300)))
+    oracle.add_seq(0, list(range(300)))
+    with pytest.raises(P.PkvError) as e:
+        native.fork(0, 0)
+    assert e.value.kind == "DUP_SEQ"
+    with pytest.raises(P.PkvError) as e:
+        native.fork(9, 1)
+    assert e.value.kind == "UNKNOWN_SEQ"
+    for c in (1, 2):
+        native.fork(0, c)
+        oracle.fork(0, c)
+    with pytest.raises(P.PkvError) as e:
+        native.append(1, 5)
+    assert e.value.kind == "INVALID"
+    # three owners of the partial block: the first two appenders copy, the last keeps it
+    slots, src, dst, rows = native.append_batch_cow([1, 0, 2, 1], [5, 6, 7, 8])
+    expect = _oracle_batch_cow(oracle, [1, 0, 2, 1], [5, 6, 7, 8])
+    assert [slots.tolist(), src.tolist(), dst.tolist(), rows.tolist()] == list(expect)
+    assert rows.tolist() == [44, 44]
+    assert len(src) == 2 and src[0] == src[1] and len(set(dst.tolist())) == 2
+    _same_state(native, oracle, [0, 1, 2], 4)
+    # not enough free blocks for every copy: nothing changes
+    for c in (3, 4, 5, 6, 7):
+        native.fork(2, c)
+        oracle.fork(2, c)
+    free = native.num_free()
+    with pytest.raises(P.PkvError) as e:
+        native.append_batch_cow([3, 4, 5, 6, 7], [1] * 5)
+    assert e.value.kind == "NO_BLOCKS"
+    assert native.num_free() == free
+    _same_state(native, oracle, [0, 1, 2, 3, 4, 5, 6, 7], 4)
+
+
+def test_batched_fork_and_free_match_one_by_one():
+    native, oracle = _pair(30, 4)
+    for sid, n in enumerate([300, 40, 513]):
+        toks = list(range(sid * 1000, sid * 1000 + n))
+        native.add_seq(sid, toks)
+        oracle.add_seq(sid, toks)
+    # a child may be the parent of a later entry
+    pairs = [(0, 10), (0, 11), (10, 12), (2, 13), (1, 14)]
+    native.fork_batch([p for p, _ in pairs], [c for _, c in pairs])
+    for p, c in pairs:
+        oracle.fork(p, c)
+    live = [0, 1, 2, 10, 11, 12, 13, 14]
+    _same_state(native, oracle, live, 4)
+    for bad_par, bad_chi, kind in [([0, 99], [20, 21], "UNKNOWN_SEQ"), ([0, 1], [20, 20], "DUP_SEQ"),
+                                   ([0], [10], "DUP_SEQ"), ([21, 0], [21, 22], "UNKNOWN_SEQ")]:
+        with pytest.raises(P.PkvError) as e:
+            native.fork_batch(bad_par, bad_chi)
+        assert e.value.kind == kind
+        _same_state(native, oracle, live, 4)  # nothing changed
+    for bad in ([0, 0], [1, 99]):
+        with pytest.raises(P.PkvError) as e:
+            native.free_batch(bad)
+        assert e.value.kind == "UNKNOWN_SEQ"
+        _same_state(native, oracle, live, 4)
+    native.free_batch([0, 12, 2])
+    for s in (0, 12, 2):
+        oracle.free_seq(s)
+        live.remove(s)
+    _same_state(native, oracle, live, 4)
+    oracle.check_invariants()

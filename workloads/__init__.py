@@ -59,13 +59,16 @@ CONFIGS = {
     "prefill_long": dict(id=7, kind="prefill", B=4, ctx=(4096, 12288), Hq=16, Hkv=8, D=128,
                          dtype="bf16", value_scale=1.0, pool=None, group=2, shared=2048, chunk=4096,
                          split=True),
+    # beam search over decode prompts: B requests x `beams` beams that re-fork every step
+    "beam_decode": dict(id=8, kind="beam", B=64, beams=4, ctx=(100, 2048), Hq=16, Hkv=8, D=128,
+                        dtype="bf16", value_scale=0.5, pool=None),
     # the prompts of prefill_prefix (same seeds, same draws), stored by the quantising store into
     # int8 caches; dtype is that of the new rows
     "int8_store": dict(id=3, kind="store", B=32, ctx=(100, 1024), Hq=16, Hkv=8, D=128,
                        dtype="bf16", value_scale=1.0, pool=None, group=8, shared=512, chunk=4096),
 }
 
-_P_LEN, _P_SEQ, _P_GROUP, _P_POOL, _P_STEP = 0, 1, 2, 3, 4
+_P_LEN, _P_SEQ, _P_GROUP, _P_POOL, _P_STEP, _P_BEAM = 0, 1, 2, 3, 4, 5
 
 
 def _rng(seed, cfg, purpose, index=0):
@@ -190,6 +193,13 @@ def decode_step_inputs(cfg, seed, step, B):
     Hq, Hkv, D, dt, vs = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["dtype"], cfg["value_scale"]
     return dict(tokens=rng.integers(0, VOCAB, size=B, dtype=np.int32), q=_normal(rng, (B, Hq, D), vs, dt),
                 k=_normal(rng, (B, Hkv, D), vs, dt), v=_normal(rng, (B, Hkv, D), vs, dt))
+
+
+def beam_parents(cfg, seed, step):
+    """Beam search step ``step``: for each request and each of its new beams, the index of the
+    current beam it continues (uniform draws; a beam picked twice is forked twice, one not picked
+    ends).  Returns int ``[B][beams]``."""
+    return _rng(seed, cfg, _P_BEAM, step).integers(0, cfg["beams"], size=(cfg["B"], cfg["beams"]))
 
 
 def int8_encode_token(x_f32, block_scale):
