@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window attention: each query attends its last W keys (0: every key)")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: replay each step's upload, store and attention from HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
     ap.add_argument("--copy-calib", action="store_true",
@@ -162,6 +164,8 @@ def bench_decode(args, cfg):
                       [None if p[2] is None else p[2][:-1] for p in parts],
                       [None if p[3] is None else p[3][:-1] for p in parts])
     max_ctx = max(lens) + nsteps
+    if args.graph and args.window:
+        raise SystemExit("--graph has no sliding window")
     batch = R.DecodeBatch(kv, Hq, ids, max_ctx, args.max_splits, window=args.window)
     # the plan the kernel uses: a window of W keys spans at most ceil((W + 255) / 256) blocks
     span = min(max_ctx, args.window + 255) if args.window > 0 else max_ctx
@@ -226,6 +230,18 @@ def bench_decode(args, cfg):
         if timed_idx is not None:
             ev[timed_idx][1].record(stream)
 
+    if args.graph:
+        # the step's inputs arrive in the graphs' fixed buffers with one device copy (as if the
+        # projections had written them there); upload, store and attention replay from graphs
+        gb = R.GraphedDecodeBatch(kv, Hq, ids, max_ctx, scale, args.max_splits)
+        for st in steps:
+            st["blob"] = gb.pack_inputs(*[st[x] for x in ("q", "k", "v", "ks", "vs") if st[x] is not None])
+
+        def run(i, timed_idx=None):  # noqa: F811
+            st = steps[i]
+            gb.inputs.copy_(st["blob"])
+            gb.step(st["tokens"], None if timed_idx is None else ev[timed_idx])
+
     # Python's cyclic GC can pause the host for tens of ms inside a step; like timeit (and serving
     # loops), collect once and keep it off while timing
     gc.collect()
@@ -253,7 +269,7 @@ def bench_decode(args, cfg):
         dtype=dtype, data="synthetic",
         config=dict(workload=cfg["name"], batch=B, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]" if isinstance(
             cfg["ctx"], tuple) else str(cfg["ctx"]), q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256,
-            splits=splits, blocks_per_split=bps, window=args.window, seed=args.seed),
+            splits=splits, blocks_per_split=bps, window=args.window, hip_graph=bool(args.graph), seed=args.seed),
         decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
         kv_gbs=achieved,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,

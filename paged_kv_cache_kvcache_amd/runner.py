@@ -110,6 +110,12 @@ class DecodeBatch:
     def upload_step_metadata(self, slots, copies=None):
         """Block tables and lengths of every sequence plus the new tokens' slots (and, with cow, the
         step's block copies (src, dst, rows)): one pinned H2D copy."""
+        self.fill_step_metadata(slots, copies)
+        self._meta.copy_(self._pin, non_blocking=True)
+        self._copied.record()
+
+    def fill_step_metadata(self, slots, copies=None):
+        """The host half of :meth:`upload_step_metadata`: fill the pinned staging buffer."""
         self._copied.synchronize()  # the previous copy has left the staging buffer
         pin = self._pin.numpy()
         B, mb = self.B, self.max_blocks
@@ -124,8 +130,6 @@ class DecodeBatch:
         self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=lens)
         self.host_context_lens, self.host_block_tables = lens, tab  # valid until the next upload
         pin[2 * B:3 * B] = np.argsort(-lens, kind="stable")  # longest contexts launch first
-        self._meta.copy_(self._pin, non_blocking=True)
-        self._copied.record()
 
     def step(self, tokens, q, k_new, v_new, softmax_scale, out=None, k_scale_new=None, v_scale_new=None):
         """One decode step: append one token per sequence, store its K/V, attend.  Returns out [B][Hq][D]."""
@@ -161,6 +165,107 @@ class DecodeBatch:
                                 self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale,
                                 seq_order=self.seq_order, window=self.window)
+
+
+class GraphedDecodeBatch:
+    """A :class:`DecodeBatch` whose device work is replayed from HIP graphs ("1200行代码挑战vLLM",
+    性能优化 §4 CUDA图支持: captured graphs cut per-launch overhead), captured on first use:
+    graph 1 holds the pinned metadata upload and the store (or the fused store + attend), graph 2
+    the attention (none when fused).  Two staging sets alternate, each with its own graphs, so the
+    host fills step i+1's metadata while step i runs.  The captured kernels read fixed device
+    buffers: the caller writes each step's inputs into ``q``, ``k_new``, ``v_new`` (int8 pools:
+    ``k_scale_new``, ``v_scale_new`` too) before :meth:`step`; the result lands in ``out``.  The
+    input buffers are views of one byte buffer, ``inputs``, so one copy can fill them all
+    (:meth:`pack_inputs` lays out such a copy source).  B, the context capacity and the split
+    plan are fixed at construction."""
+
+    def __init__(self, kv, Hq, seq_ids, max_context_len, softmax_scale, max_splits=0, fused=False):
+        self.kv = kv
+        self.fused = bool(fused)
+        self.scale = float(softmax_scale)
+        self.sets = [DecodeBatch(kv, Hq, seq_ids, max_context_len, max_splits, fused=fused) for _ in range(2)]
+        self.sets[1].workspace = self.sets[0].workspace  # one stream: the steps never overlap
+        self.B, dev = self.sets[0].B, kv.device
+        qdt = torch.float32 if kv.dtype == F32 else torch.bfloat16
+        self._layout = [("q", (self.B, Hq, kv.D), qdt), ("k_new", (self.B, kv.Hkv, kv.D), TORCH_DTYPE[kv.dtype]),
+                        ("v_new", (self.B, kv.Hkv, kv.D), TORCH_DTYPE[kv.dtype])]
+        if kv.dtype == I8:
+            self._layout += [("k_scale_new", (self.B, kv.Hkv), torch.float32),
+                             ("v_scale_new", (self.B, kv.Hkv), torch.float32)]
+        self.inputs = torch.zeros(self._offsets()[-1], dtype=torch.uint8, device=dev)
+        self.k_scale_new = self.v_scale_new = None
+        for name, t in zip([x[0] for x in self._layout], self.unpack(self.inputs)):
+            setattr(self, name, t)
+        self.out = torch.empty_like(self.q)
+        self.graphs = [None, None]
+        self.steps = 0
+
+    @property
+    def ids(self):
+        return self.sets[0].ids
+
+    def _offsets(self):
+        off = [0]
+        for _, shape, dt in self._layout:
+            n = int(np.prod(shape)) * torch.empty((), dtype=dt).element_size()
+            off.append(off[-1] + -(-n // 256) * 256)
+        return off
+
+    def unpack(self, buf):
+        """Typed views (q, k_new, v_new[, k_scale_new, v_scale_new]) of a byte buffer laid out like
+        ``inputs``."""
+        off = self._offsets()
+        return [buf[off[i]:off[i + 1]][:int(np.prod(shape)) * torch.empty((), dtype=dt).element_size()]
+                .view(dt).view(shape) for i, (_, shape, dt) in enumerate(self._layout)]
+
+    def pack_inputs(self, *tensors):
+        """A byte buffer laid out like ``inputs`` holding the given step inputs (same order)."""
+        buf = torch.zeros_like(self.inputs)
+        for view, t in zip(self.unpack(buf), tensors):
+            view.copy_(t)
+        return buf
+
+    def _capture(self, j):
+        b = self.sets[j]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=side):
+            b._meta.copy_(b._pin, non_blocking=True)
+            if self.fused:
+                b.store_attend(self.q, self.k_new, self.v_new, self.scale, self.out, self.k_scale_new,
+                               self.v_scale_new)
+            else:
+                self.kv.store(b.slots, self.k_new, self.v_new, self.k_scale_new, self.v_scale_new)
+        g2 = None
+        if not self.fused:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2, stream=side):
+                b.attend(self.q, self.scale, self.out)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graphs[j] = (g1, g2)
+
+    def step(self, tokens, events=None):
+        """Append one token per sequence (host), then replay the step's graphs on the current
+        stream.  ``events`` = (start, end) are recorded around the attention.  Returns ``out``."""
+        j = self.steps % 2
+        b = self.sets[j]
+        b.fill_step_metadata(self.kv.alloc.append_batch(b.ids, tokens))
+        if self.graphs[j] is None:
+            self._capture(j)
+        g1, g2 = self.graphs[j]
+        if events is not None and g2 is None:
+            events[0].record()
+        g1.replay()
+        b._copied.record()  # the staging buffer may be refilled once graph 1 has run
+        if g2 is not None:
+            if events is not None:
+                events[0].record()
+            g2.replay()
+        if events is not None:
+            events[1].record()
+        self.steps += 1
+        return self.out
 
 
 def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None, v_scale_rows=None):
