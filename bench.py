@@ -49,6 +49,9 @@ def parse():
                     help="sliding-window attention: each query attends its last W keys (0: every key)")
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's upload, store and attention from HIP graphs")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="decode: write this many MiB of scratch before every step (evicts L2 and MALL; the "
+                         "kernel time then reads a cold cache, the step time includes the write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
     ap.add_argument("--copy-calib", action="store_true",
@@ -219,8 +222,12 @@ def bench_decode(args, cfg):
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
+    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if args.flush_mb > 0 else None
+
     def run(i, timed_idx=None):
         st = steps[i]
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         slots = kv.alloc.append_batch(batch.ids, st["tokens"])
         batch.upload_step_metadata(slots)
         kv.store(batch.slots, st["k"], st["v"], st["ks"], st["vs"])
@@ -269,7 +276,8 @@ def bench_decode(args, cfg):
         dtype=dtype, data="synthetic",
         config=dict(workload=cfg["name"], batch=B, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]" if isinstance(
             cfg["ctx"], tuple) else str(cfg["ctx"]), q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256,
-            splits=splits, blocks_per_split=bps, window=args.window, hip_graph=bool(args.graph), seed=args.seed),
+            splits=splits, blocks_per_split=bps, window=args.window, hip_graph=bool(args.graph),
+            flush_mb=args.flush_mb, seed=args.seed),
         decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
         kv_gbs=achieved,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
