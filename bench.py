@@ -286,8 +286,8 @@ def bench_decode(args, cfg):
                       kernel="decode (split kernel + LSE reduce when splits > 1)",
                       bytes_per_launch=bytes_per_launch),
     )
-    if not args.no_cpu_baseline and args.window == 0:
-        res["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_sample or 8)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_sample or 8, args.window)
     return res
 
 
@@ -303,7 +303,7 @@ def _timed_sample(run, total, first=8, budget_s=10.0):
         n = min(total, max(2 * n, int(n * 1.2 * budget_s / max(dt, 1e-3))))
 
 
-def cpu_baseline_decode(wl, first=8):
+def cpu_baseline_decode(wl, first=8, window=0):
     """The oracle's whole decode step (its block manager, store and attention) on the first n sequences."""
     from threadpoolctl import threadpool_limits
     import workloads as W
@@ -315,13 +315,14 @@ def cpu_baseline_decode(wl, first=8):
         sub["seqs"] = wl["seqs"][:n]
         sub["num_blocks"] = W.pool_blocks(wl["cfg"], sub["lens"])
         sub["free_order"] = W.free_order(wl["cfg"], wl["seed"], sub["num_blocks"])
-        decode_step(sub)
+        decode_step(sub, window)
 
     with threadpool_limits(1):
         n, dt = _timed_sample(run, len(wl["lens"]), first)
+    win = f" over the last {window} keys" if window > 0 else ""
     return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"first {n} of {len(wl['lens'])} sequences ({sum(wl['lens'][:n])} context tokens), one decode "
-                       f"step: oracle block manager + store + fp64 attention, {dt:.1f}s on one thread")
+                       f"step: oracle block manager + store + fp64 attention{win}, {dt:.1f}s on one thread")
 
 
 # ------------------------------------------------------------------------------------ prefill
@@ -437,9 +438,12 @@ def bench_int8_store(args, cfg):
     ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
     n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
     chunks = W.pack_chunks(n_new, cfg["chunk"])
-    dchunks, blocks = [], 0
+    dchunks, blocks, host_first = [], 0, None
     for ch in chunks:
         _, _, slots = kv.alloc.prefill_slots(ch, sum(n_new[i] for i in ch))
+        if host_first is None:  # the first chunk's rows and slots, for the oracle baseline
+            host_first = (np.concatenate([prompts[i]["k"][ncached[i]:] for i in ch]),
+                          np.concatenate([prompts[i]["v"][ncached[i]:] for i in ch]), slots.copy())
         runs, n_runs, longest = store_runs(slots)
         dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), dev)
         dchunks.append(dict(k=dv("k"), v=dv("v"), slots=torch.from_numpy(np.ascontiguousarray(slots)).to(dev),
@@ -488,7 +492,29 @@ def bench_int8_store(args, cfg):
         roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
                       traffic=None if traffic is None else traffic * len(dchunks),
                       kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
+        cpu_baseline=None if args.no_cpu_baseline else cpu_baseline_int8_store(host_first, wl["num_blocks"], Hkv, D),
     )
+
+
+def cpu_baseline_int8_store(first_chunk, num_blocks, Hkv, D, budget_s=5.0):
+    """The oracle's quantising store of the first chunk's rows, repeated for about ``budget_s``."""
+    from threadpoolctl import threadpool_limits
+    import workloads as W
+    from oracle import attention as OT
+    k_bits, v_bits, slots = first_chunk
+    k, v = W.bf16_bits_to_f32(k_bits), W.bf16_bits_to_f32(v_bits)
+    kc = np.zeros((num_blocks, Hkv, 256, D), np.int8)
+    ks = np.zeros((num_blocks, Hkv), np.float32)
+    reps = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            OT.kv_store_quant(kc, kc, ks, ks, k, v, slots)
+            reps += 1
+        dt = time.perf_counter() - t0
+    return dict(value=reps * len(slots) / dt, unit="stored tokens/s", cores=1, kind="oracle",
+                sample=f"the first chunk's {len(slots)} new tokens (K and V, {Hkv} heads) stored {reps} times: "
+                       f"oracle quantising store, {dt:.1f}s on one thread")
 
 
 def bench_beam(args, cfg):
@@ -606,7 +632,52 @@ def bench_beam(args, cfg):
         roofline=dict(bound="hbm", achieved=uniq_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=uniq_gbs / HBM_PEAK_GBS,
                       traffic=None, kernel="decode over every beam's context (bytes: distinct blocks once)",
                       bytes_per_launch=uniq_bytes),
+        cpu_baseline=None if args.no_cpu_baseline else cpu_baseline_beam(wl, args.seed),
     )
+
+
+def cpu_baseline_beam(wl, seed, first=1):
+    """The oracle's beam step on the first n requests: admit and store the prompts, fork each into
+    its beams, append one token per beam with copy-on-write (block copies included), store the new
+    rows, attend over every beam."""
+    from threadpoolctl import threadpool_limits
+    import workloads as W
+    from oracle import allocator as OA
+    from oracle import attention as OT
+    cfg = wl["cfg"]
+    NBM, Hkv, D = cfg["beams"], cfg["Hkv"], cfg["D"]
+
+    def run(n):
+        seqs = wl["seqs"][:n]
+        nb = W.pool_blocks(cfg, wl["lens"][:n]) + 2 * n * NBM
+        a = OA.Allocator(nb, W.free_order(cfg, seed, nb))
+        kc = np.zeros((nb, Hkv, 256, D))
+        vc = np.zeros_like(kc)
+        for r, s in enumerate(seqs):
+            a.add_seq(r, s["tokens"])
+        _, _, slots = a.prefill_slots(list(range(n)))
+        kc, vc = OT.kv_store(kc, vc, np.concatenate([W.bf16_bits_to_f32(s["k"]) for s in seqs]),
+                             np.concatenate([W.bf16_bits_to_f32(s["v"]) for s in seqs]), slots)
+        beams = []  # step 0: every beam continues its request's prompt
+        for r in range(n):
+            for j in range(NBM):
+                a.fork(r, n + r * NBM + j)
+                beams.append(n + r * NBM + j)
+            a.free_seq(r)
+        inp = W.decode_step_inputs(cfg, seed, 0, n * NBM)
+        res = [a.append_cow(b, int(t)) for b, t in zip(beams, inp["tokens"])]
+        cop = [x for x in res if x[1] >= 0]
+        kc, vc = OT.copy_blocks([kc, vc], [x[1] for x in cop], [x[2] for x in cop], [x[0] % 256 for x in cop])
+        kc, vc = OT.kv_store(kc, vc, W.bf16_bits_to_f32(inp["k"]), W.bf16_bits_to_f32(inp["v"]), [x[0] for x in res])
+        lens = [a.seq_len(b) for b in beams]
+        OT.decode(W.bf16_bits_to_f32(inp["q"]), kc, vc, a.block_tables(beams, -(-max(lens) // 256)), lens,
+                  1.0 / math.sqrt(D))
+
+    with threadpool_limits(1):
+        n, dt = _timed_sample(run, len(wl["lens"]), first)
+    return dict(value=n * NBM / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {n} of {len(wl['lens'])} requests x {NBM} beams: oracle block manager (forks, "
+                       f"copy-on-write), block copies, store, fp64 attention, {dt:.1f}s on one thread")
 
 
 def cpu_baseline_prefill_rows(wl, budget_s=10.0):

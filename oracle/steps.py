@@ -26,8 +26,9 @@ def _rows(seq, dtype):
     return seq["k"], seq["v"], None, None
 
 
-def decode_step(wl):
-    """One decode step of a decode workload; returns float64 outputs [B][Hq][D]."""
+def decode_step(wl, window=0):
+    """One decode step of a decode workload; returns float64 outputs [B][Hq][D].  ``window`` > 0:
+    sliding-window attention over each sequence's last ``window`` keys."""
     cfg = wl["cfg"]
     dtype = cfg["dtype"]
     B, Hkv, D = len(wl["lens"]), cfg["Hkv"], cfg["D"]
@@ -61,7 +62,7 @@ def decode_step(wl):
     mb = max(1, -(-max(wl["lens"]) // 256))
     tables = a.block_tables(ids, mb)
     q = np.stack([_f64(s["q"]) for s in wl["seqs"]])
-    return OT.decode(q, kc, vc, tables, wl["lens"], 1.0 / np.sqrt(D), ksc, vsc)
+    return OT.decode(q, kc, vc, tables, wl["lens"], 1.0 / np.sqrt(D), ksc, vsc, window=window)
 
 
 def decode_one_sequence(cfg, seq, L):

@@ -79,3 +79,16 @@ def test_prefix_cache_changes_no_suffix_output():
         assert np.abs(a - b).max() < 2e-2
         r_on += n - c
         r_off += n
+
+
+def test_prefill_is_deterministic_and_placement_invariant():
+    """Reruns give bitwise the same outputs, and so does another physical placement of the blocks:
+    the kernel reads the same values in the same order wherever the blocks sit."""
+    cfg = W.config("prefill_prefix")
+    wl = W.prefill_workload(cfg, 0)
+    a = gpu_prefill(wl, "cuda")
+    b = gpu_prefill(wl, "cuda")
+    other = dict(wl, free_order=np.random.default_rng(9).permutation(wl["num_blocks"]).astype(np.int32))
+    c = gpu_prefill(other, "cuda")
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, c)
