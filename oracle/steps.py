@@ -65,15 +65,17 @@ def decode_step(wl, window=0):
     return OT.decode(q, kc, vc, tables, wl["lens"], 1.0 / np.sqrt(D), ksc, vsc, window=window)
 
 
-def decode_one_sequence(cfg, seq, L):
-    """Attention of one sequence's query over its own contiguous rows (sampled full-size checks)."""
+def decode_one_sequence(cfg, seq, L, window=0):
+    """Attention of one sequence's query over its own contiguous rows (sampled full-size checks);
+    ``window`` > 0: over its last ``window`` rows only."""
     G = cfg["Hq"] // cfg["Hkv"]
     D = cfg["D"]
+    lo = max(0, L - window) if window > 0 else 0
     if cfg["dtype"] == "i8":
-        k = seq["kq"][:L].astype(np.float64) * seq["k_tok_scale"][:L, :, None].astype(np.float64)
-        v = seq["vq"][:L].astype(np.float64) * seq["v_tok_scale"][:L, :, None].astype(np.float64)
+        k = seq["kq"][lo:L].astype(np.float64) * seq["k_tok_scale"][lo:L, :, None].astype(np.float64)
+        v = seq["vq"][lo:L].astype(np.float64) * seq["v_tok_scale"][lo:L, :, None].astype(np.float64)
     else:
-        k, v = _f64(seq["k"][:L]), _f64(seq["v"][:L])
+        k, v = _f64(seq["k"][lo:L]), _f64(seq["v"][lo:L])
     q = _f64(seq["q"])
     return np.stack([OT.attend(q[h], k[:, h // G], v[:, h // G], 1.0 / np.sqrt(D)) for h in range(cfg["Hq"])])
 

@@ -51,9 +51,10 @@ def kv_arrays(seq, dtype, sl=slice(None)):
     return seq["k"][sl], seq["v"][sl], None, None
 
 
-def gpu_decode(wl, device, max_splits=0, fill=None, free_order=None, max_context_len=None, fused=True):
+def gpu_decode(wl, device, max_splits=0, fill=None, free_order=None, max_context_len=None, fused=True, window=0):
     """History admitted and stored, then one decode step (append + store + attend) on the GPU, with
-    the store fused into the attention launch or (``fused=False``) as its own kv_store launch."""
+    the store fused into the attention launch or (``fused=False``) as its own kv_store launch;
+    ``window`` > 0: sliding-window attention (not fused)."""
     cfg = wl["cfg"]
     dtype = cfg["dtype"]
     B, Hq, Hkv, D = len(wl["lens"]), cfg["Hq"], cfg["Hkv"], cfg["D"]
@@ -63,7 +64,8 @@ def gpu_decode(wl, device, max_splits=0, fill=None, free_order=None, max_context
     parts = [kv_arrays(s, dtype, slice(0, -1)) for s in wl["seqs"]]
     R.admit_and_store(kv, ids, [s["tokens"][:-1] for s in wl["seqs"]], [p[0] for p in parts],
                       [p[1] for p in parts], [p[2] for p in parts], [p[3] for p in parts])
-    batch = R.DecodeBatch(kv, Hq, ids, max_context_len or max(wl["lens"]), max_splits, fused=fused)
+    batch = R.DecodeBatch(kv, Hq, ids, max_context_len or max(wl["lens"]), max_splits, fused=fused and not window,
+                          window=window)
     last = [kv_arrays(s, dtype, slice(-1, None)) for s in wl["seqs"]]
     k_new = dev_rows(np.concatenate([x[0] for x in last]), device)
     v_new = dev_rows(np.concatenate([x[1] for x in last]), device)

@@ -132,3 +132,20 @@ def test_windowed_prefill_wide_workgroups(gpu):
     for window in (200, 1500):
         got, ref = _prefill_case(gpu, rng, Hkv, Hkv, D, lens_k, n_q, window, sample=6)
         _check(got, ref, P.BF16, f"wide, window {window}")
+
+
+@pytest.mark.parametrize("name,window", [("long_decode", 1024), ("qwen3_decode", 512), ("int8_decode", 700)])
+def test_windowed_decode_full_size_sampled(gpu, name, window):
+    """The full-size workloads with the window the bench measures, in its launch configuration
+    (automatic split plan over the window's span): eight sampled sequences against the plain
+    definition over their own last ``window`` rows."""
+    from oracle import steps as OS
+    from tests.gpu_cases import check_tol, gpu_decode, host_out
+    cfg = W.config(name)
+    wl = W.decode_workload(cfg, 0)
+    say(f"full-size {name}, window {window}: B={len(wl['lens'])}")
+    out, _, _ = gpu_decode(wl, gpu, max_context_len=max(wl["lens"]) + 23, window=window)
+    got = host_out(out)
+    sample = np.random.default_rng(11).choice(len(wl["lens"]), size=8, replace=False)
+    ref = np.stack([OS.decode_one_sequence(cfg, wl["seqs"][b], wl["lens"][b], window) for b in sample])
+    check_tol(got[sample], ref, cfg["dtype"], f"{name} window {window}, 8 sampled sequences")
