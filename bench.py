@@ -581,7 +581,7 @@ def bench_beam(args, cfg):
         batch.upload_step_metadata(slots, (src, dst, rows))
         if timed_idx is not None:
             ev_copy[timed_idx][0].record(stream)
-        batch.copy_blocks()
+        batch.copy_on_write()
         if timed_idx is not None:
             ev_copy[timed_idx][1].record(stream)
         kv.store(batch.slots, st["k"], st["v"])

@@ -136,7 +136,7 @@ class DecodeBatch:
         if self.cow:
             slots, src, dst, rows = self.kv.alloc.append_batch_cow(self.ids, tokens)
             self.upload_step_metadata(slots, (src, dst, rows))
-            self.copy_blocks()
+            self.copy_on_write()
         else:
             self.upload_step_metadata(self.kv.alloc.append_batch(self.ids, tokens))
         if self.fused:
@@ -144,7 +144,7 @@ class DecodeBatch:
         self.kv.store(self.slots, k_new, v_new, k_scale_new, v_scale_new)
         return self.attend(q, softmax_scale, out)
 
-    def copy_blocks(self):
+    def copy_on_write(self):
         """The uploaded step's copy-on-write block copies (must precede the store)."""
         n, B, kv = self.n_copies, self.B, self.kv
         if n:
