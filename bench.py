@@ -17,7 +17,9 @@ whole workload -- every chunk's store and prefill attention.
 Reported beside the throughput:
 * ``roofline`` -- the dominant kernel's algorithmic traffic (decode: KV bytes of the valid tokens;
   prefill: causal flops) divided by its average duration, timed with HIP events on the launch
-  stream, against MI355X's published peak (8 TB/s HBM3E; 2.5 PFLOP/s dense bf16);
+  stream, against MI355X's published peak (8 TB/s HBM3E; 2.5 PFLOP/s dense bf16).  The events
+  bracket the kernel in a second pass of K steps: recording them costs the stream a few
+  microseconds per step, which the throughput pass (``value``, ``ms_per_step``) leaves out;
 * ``cpu_baseline`` -- the fp64 oracle timed on the host on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--seed S]
@@ -47,6 +49,8 @@ def parse():
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window attention: each query attends its last W keys (0: every key)")
+    ap.add_argument("--fused", action="store_true",
+                    help="decode: store the new tokens inside the attention launch (pkv_decode_store_attend)")
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's upload, store and attention from HIP graphs")
     ap.add_argument("--flush-mb", type=int, default=0,
@@ -146,7 +150,10 @@ def bench_decode(args, cfg):
     dtype = cfg["dtype"]
     kvdt = {"f32": F32, "bf16": BF16, "i8": I8}[dtype]
     B, Hq, Hkv, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"]
-    nsteps = args.warmup + args.steps
+    # warm-up, K steps timed by the wall clock (the throughput), then K steps with HIP events around
+    # the attention launch (its duration); the events cost the stream several microseconds per step,
+    # so they stay out of the throughput pass
+    nsteps = args.warmup + 2 * args.steps
     t0 = time.time()
     wl = W.decode_workload(cfg, args.seed)
     lens = wl["lens"]
@@ -167,8 +174,8 @@ def bench_decode(args, cfg):
                       [None if p[2] is None else p[2][:-1] for p in parts],
                       [None if p[3] is None else p[3][:-1] for p in parts])
     max_ctx = max(lens) + nsteps
-    if args.graph and args.window:
-        raise SystemExit("--graph has no sliding window")
+    if (args.graph or args.fused) and args.window:
+        raise SystemExit("--graph and --fused have no sliding window")
     batch = R.DecodeBatch(kv, Hq, ids, max_ctx, args.max_splits, window=args.window)
     # the plan the kernel uses: a window of W keys spans at most ceil((W + 255) / 256) blocks
     span = min(max_ctx, args.window + 255) if args.window > 0 else max_ctx
@@ -230,10 +237,15 @@ def bench_decode(args, cfg):
             flush.fill_(i & 0xFF)
         slots = kv.alloc.append_batch(batch.ids, st["tokens"])
         batch.upload_step_metadata(slots)
-        kv.store(batch.slots, st["k"], st["v"], st["ks"], st["vs"])
-        if timed_idx is not None:
-            ev[timed_idx][0].record(stream)
-        batch.attend(st["q"], scale, out)
+        if args.fused:
+            if timed_idx is not None:
+                ev[timed_idx][0].record(stream)
+            batch.store_attend(st["q"], st["k"], st["v"], scale, out, st["ks"], st["vs"])
+        else:
+            kv.store(batch.slots, st["k"], st["v"], st["ks"], st["vs"])
+            if timed_idx is not None:
+                ev[timed_idx][0].record(stream)
+            batch.attend(st["q"], scale, out)
         if timed_idx is not None:
             ev[timed_idx][1].record(stream)
 
@@ -258,13 +270,17 @@ def bench_decode(args, cfg):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
-        run(args.warmup + j, j)
+        run(args.warmup + j)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    ev_steps = [args.warmup + args.steps + j for j in range(args.steps)]
+    for j, i in enumerate(ev_steps):
+        run(i, j)
+    torch.cuda.synchronize()
     gc.enable()
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
-    bytes_per_launch = sum(kv_bytes(steps[args.warmup + j]["ctx"]) for j in range(args.steps)) / args.steps
+    bytes_per_launch = sum(kv_bytes(steps[i]["ctx"]) for i in ev_steps) / args.steps
     achieved = bytes_per_launch / avg_kern_s / 1e9
     log(f"[bench] splits={splits} blocks/split={bps}; decode kernel avg {avg_kern_s * 1e6:.1f} us, "
         f"{achieved:.0f} GB/s; step {elapsed / args.steps * 1e3:.3f} ms")
@@ -277,7 +293,7 @@ def bench_decode(args, cfg):
         config=dict(workload=cfg["name"], batch=B, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]" if isinstance(
             cfg["ctx"], tuple) else str(cfg["ctx"]), q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256,
             splits=splits, blocks_per_split=bps, window=args.window, hip_graph=bool(args.graph),
-            flush_mb=args.flush_mb, seed=args.seed),
+            flush_mb=args.flush_mb, fused_store=bool(args.fused), seed=args.seed),
         decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
         kv_gbs=achieved,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
@@ -389,11 +405,16 @@ def bench_prefill(args, cfg):
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
+    # K steps timed by the wall clock (the throughput), then K steps with events around each chunk's
+    # attention launch (their durations), as in the decode line
     t0 = time.perf_counter()
+    for j in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     for j in range(args.steps):
         run(j)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     gc.enable()
     kern_s = sum(a.elapsed_time(b) for row in ev for a, b in row) / args.steps / 1e3
     tflops = flops / kern_s / 1e12
@@ -471,9 +492,12 @@ def bench_int8_store(args, cfg):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
-        run(j)
+        run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    for j in range(args.steps):  # the event pass: store durations, kept out of the wall clock
+        run(j)
+    torch.cuda.synchronize()
     gc.enable()
     kern_s = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 1e3
     gbs = step_bytes / kern_s / 1e9
@@ -531,7 +555,7 @@ def bench_beam(args, cfg):
     dev = torch.device("cuda:0")
     NR, NBM, Hq, Hkv, D = cfg["B"], cfg["beams"], cfg["Hq"], cfg["Hkv"], cfg["D"]
     B = NR * NBM
-    nsteps = args.warmup + args.steps
+    nsteps = args.warmup + 2 * args.steps  # warm-up, the wall-clock pass, the event pass
     wl = W.decode_workload(cfg, args.seed)
     lens = wl["lens"]
     # prompts, plus per beam a private partial block and the blocks its appends open
@@ -601,9 +625,12 @@ def bench_beam(args, cfg):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
-        run(args.warmup + j, j)
+        run(args.warmup + j)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    for j in range(args.steps):  # the event pass: kernel durations and byte counts
+        run(args.warmup + args.steps + j, j)
+    torch.cuda.synchronize()
     gc.enable()
     dec_s = sum(a.elapsed_time(b) for a, b in ev_dec) / args.steps / 1e3
     copy_s = sum(a.elapsed_time(b) for a, b in ev_copy) / args.steps / 1e3
