@@ -26,7 +26,9 @@
  *     never allocates device memory.
  *   - Arguments that can be checked on the host are checked before anything
  *     is enqueued; a rejected call enqueues nothing.  Device data (slots, block
- *     ids, lengths) is trusted: out-of-range values there are undefined.
+ *     ids, lengths) is trusted: out-of-range values there are undefined, unless
+ *     device-data checks are on (pkv_set_device_checks, PKV_CHECK=1), which turn
+ *     them into an entry in a device error word instead.
  *
  * Cache layout (all dtypes): K and V are each
  *     [num_blocks][num_kv_heads][256][head_dim]
@@ -75,6 +77,20 @@ typedef struct {
 /* Text of the last failure on the calling thread ("" if none).  Owned by the library. */
 const char* pkv_last_error(void);
 const char* pkv_version(void);
+
+/* Device-data checks.  Kernels normally trust the indices they read from device memory (slots,
+ * block ids, context and key lengths, launch order, run lists, cu_seqlens_q): an out-of-range
+ * value there is undefined.  With checks on (pkv_set_device_checks(1), or PKV_CHECK=1 in the
+ * environment when the library first launches a kernel), each kernel validates those values
+ * before using them and records the first bad one in a device error word instead: a bad slot's
+ * row is skipped; a workgroup whose sequence, run or block pair is bad computes nothing and leaves
+ * its outputs unwritten.  Checks cost one test per workgroup (per row for stores).
+ * pkv_device_error reads and clears the error word on `stream` and waits for the stream:
+ * *code = 0 (no error) or 1 slot, 2 block id, 3 length, 4 launch-order entry, 5 run, 6
+ * cu_seqlens_q, 7 copy row count; *where = the batch row, sequence or pair; *value = the bad
+ * value (where and value may be NULL).  The word is per device and shared by every caller. */
+int pkv_set_device_checks(int32_t enable);
+int pkv_device_error(int32_t* code, int32_t* where, int32_t* value, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Host block manager.

@@ -46,6 +46,8 @@ _pdesc = ctypes.POINTER(CacheDesc)
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
+    "pkv_set_device_checks": (_i32, [_i32]),
+    "pkv_device_error": (_i32, [_p32, _p32, _p32, _vp]),
     "pkv_alloc_create": (_i32, [_i32, _i32, _p32, _i32, ctypes.POINTER(_vp)]),
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_add_seq": (_i32, [_vp, _i64, _p32, _i32, _p32]),
@@ -284,6 +286,21 @@ def kv_store(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale_new=None, v_s
     _check(lib().pkv_kv_store(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_scale_new), _ptr(v_scale_new),
                               _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                               _stream(stream)), "pkv_kv_store")
+
+
+def set_device_checks(enable):
+    """Device-data checks on or off: with them on, kernels validate the slots, block ids, lengths,
+    launch order and run lists they read and report the first bad one (see :func:`device_error`)."""
+    _check(lib().pkv_set_device_checks(1 if enable else 0), "pkv_set_device_checks")
+
+
+def device_error(stream=None):
+    """(code, where, value) of the first bad index the kernels met since the last call (code 0: none);
+    clears it.  Waits for ``stream``."""
+    code, where, value = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pkv_device_error(ctypes.byref(code), ctypes.byref(where), ctypes.byref(value), _stream(stream)),
+           "pkv_device_error")
+    return code.value, where.value, value.value
 
 
 def copy_blocks(src, dst, k_cache, v_cache, rows=None, k_scale=None, v_scale=None, stream=None):

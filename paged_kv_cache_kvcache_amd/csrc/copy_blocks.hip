@@ -10,6 +10,7 @@
 // 43 us), since a step's copies are few and the launch must spread them over every CU.
 #include <hip/hip_runtime.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -24,6 +25,8 @@ struct CopyArgs {
     float* v_scale;
     int32_t row_pieces;  // 16-byte pieces per row
     int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t check;       // validate block ids and row counts (device-data checks)
 };
 
 constexpr int kCopyThreads = 256, kCopyUnroll = 1;
@@ -33,6 +36,17 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
     const int32_t pair = int32_t(blockIdx.x) / a.num_kv_heads;
     const int32_t h = int32_t(blockIdx.x) - pair * a.num_kv_heads;
     const int64_t s = a.src[pair], d = a.dst[pair];
+    if (a.check) {  // the same in every thread: a bad pair's workgroups copy nothing
+        const int32_t r = a.rows != nullptr ? a.rows[pair] : pkv::kBlock;
+        const bool s_bad = s < 0 || s >= a.num_blocks, d_bad = d < 0 || d >= a.num_blocks;
+        const bool r_bad = r < 0 || r > pkv::kBlock;
+        if (s_bad || d_bad || r_bad) {
+            if (threadIdx.x == 0 && h == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+                record_error(s_bad || d_bad ? pkv::kErrBlock : pkv::kErrRows, pair,
+                             s_bad ? int32_t(s) : d_bad ? int32_t(d) : r);
+            return;
+        }
+    }
     if (a.k_scale != nullptr && blockIdx.y == 0 && threadIdx.x == 0) {
         float* sc = is_v ? a.v_scale : a.k_scale;
         sc[d * a.num_kv_heads + h] = sc[s * a.num_kv_heads + h];
@@ -81,6 +95,8 @@ extern "C" int pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t* src, c
     a.v_scale = v_scale;
     a.row_pieces = desc->head_dim * pkv::dtype_bytes(desc->kv_dtype) / 16;
     a.num_kv_heads = desc->num_kv_heads;
+    a.num_blocks = desc->num_blocks;
+    a.check = pkv::device_checks();
     const int per_wg = kCopyThreads * kCopyUnroll;
     const int chunks = (pkv::kBlock * a.row_pieces + per_wg - 1) / per_wg;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(n) * unsigned(desc->num_kv_heads), unsigned(chunks), 2),
@@ -89,3 +105,5 @@ extern "C" int pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t* src, c
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "copy_blocks launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+int pkv::read_error_copy_blocks(void* stream, int32_t* out) { return read_clear_error(stream, out); }

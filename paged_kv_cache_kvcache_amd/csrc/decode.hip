@@ -35,6 +35,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -242,23 +243,65 @@ struct DecodeArgs {
     int32_t blocks_per_split;
     int32_t window;    // > 0: sliding window, the last `window` keys of each sequence
     float scale_log2;  // softmax_scale * log2(e)
+    int32_t B;
+    int32_t num_blocks;
+    int64_t pool_slots;  // num_blocks * 256
+    int32_t check;       // launch the instantiation that validates order, lengths, block ids, new slots
 };
 
+// Device-data checks of one (sequence, split): every block id it reads is in the pool, and so is
+// the new token's slot when this split stores it.  Wavefront-uniform (every wavefront of the
+// workgroup computes the same), so a workgroup that fails leaves as a whole.
+__device__ bool decode_split_inputs_ok(const DecodeArgs& a, int b, int blk0, int blk1, int ctx) {
+    const int lane = threadIdx.x & 63;
+    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    for (int e0 = blk0; e0 < blk1; e0 += 64) {
+        const int e = e0 + lane;
+        const int v = bt[min(e, blk1 - 1)];  // clamped, so the load needs no exec mask
+        const uint64_t bad = __ballot(e < blk1 && (v < 0 || v >= a.num_blocks));
+        if (bad != 0) {
+            const int first = __shfl(v, __ffsll(static_cast<unsigned long long>(bad)) - 1, 64);
+            if (threadIdx.x == 0) record_error(pkv::kErrBlock, b, first);
+            return false;
+        }
+    }
+    if (a.new_slots != nullptr && ctx > 0) {
+        const int bn = (ctx - 1) / pkv::kBlock;
+        if (bn >= blk0 && bn < blk1) {
+            const int32_t slot = a.new_slots[b];
+            if (slot >= a.pool_slots) {
+                if (threadIdx.x == 0) record_error(pkv::kErrSlot, b, slot);
+                return false;
+            }
+        }
+    }
+    return true;
+}
+
 // --------------------------------------------------------------------------- split kernel
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool CHECK>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     using T = Traits<DT, D>;
     constexpr int E = T::E, W = T::W, RB = T::kRowBytes, PB = W * 4;
 
     const int s = blockIdx.x, g = blockIdx.y;
     const int b = a.seq_order != nullptr ? a.seq_order[blockIdx.z] : int(blockIdx.z);
+    if (CHECK && (b < 0 || b >= a.B)) {  // uniform in the workgroup
+        if (threadIdx.x == 0 && s == 0 && g == 0) record_error(pkv::kErrSequence, int(blockIdx.z), b);
+        return;
+    }
     const int ctx = a.context_lens[b];
+    if (CHECK && (ctx < 0 || ctx > int64_t(a.max_blocks) * pkv::kBlock)) {
+        if (threadIdx.x == 0 && s == 0 && g == 0) record_error(pkv::kErrLength, b, ctx);
+        return;
+    }
     const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
     // keys lo..ctx-1 are attended: all of them, or the last `window` (splits start at lo's block)
     const int lo = a.window > 0 ? max(0, ctx - a.window) : 0;
     const int blk0 = lo / pkv::kBlock + s * a.blocks_per_split;
     const int blk1 = min(nblk, blk0 + a.blocks_per_split);
     if (a.splits > 1 && blk0 >= blk1) return;  // empty split: the reduce kernel skips it
+    if (CHECK && !decode_split_inputs_ok(a, b, blk0, blk1, ctx)) return;
 
     // ---- the new token of this sequence (position ctx - 1), stored by the workgroup whose split
     // holds its block before any wavefront reads that block; no other workgroup reads it
@@ -515,8 +558,10 @@ void plan(int B, int Hkv, int max_ctx, int max_splits, int* splits, int* bps) {
 
 template <int DT, int D, int G>
 hipError_t launch(const DecodeArgs& a, int B, hipStream_t st) {
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, G>), dim3(a.splits, a.num_kv_heads, B), dim3(kThreads), 0,
-                       st, a);
+    // device-data checks run in their own instantiation, so the production one is unchanged by them
+    const dim3 grid(a.splits, a.num_kv_heads, B);
+    if (a.check) hipLaunchKernelGGL((decode_split_kernel<DT, D, G, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((decode_split_kernel<DT, D, G, false>), grid, dim3(kThreads), 0, st, a);
     if (a.splits > 1)
         hipLaunchKernelGGL((decode_reduce_kernel<D, DT == PKV_F32>), dim3(a.num_q_heads, B), dim3(D), 0, st, a);
     return hipGetLastError();
@@ -625,6 +670,10 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
     a.num_q_heads = Hq;
     a.scale_log2 = softmax_scale * kLog2e;
     a.window = window;
+    a.B = B;
+    a.num_blocks = desc->num_blocks;
+    a.pool_slots = int64_t(desc->num_blocks) * pkv::kBlock;
+    a.check = pkv::device_checks();
     if (nt != nullptr) {
         a.new_slots = nt->slot_mapping;
         a.k_new = static_cast<const char*>(nt->k_new);
@@ -705,3 +754,5 @@ extern "C" int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q
                        seq_order, max_context_len, max_splits, softmax_scale, out, workspace, workspace_bytes, &nt,
                        0, stream);
 }
+
+int pkv::read_error_decode(void* stream, int32_t* out) { return read_clear_error(stream, out); }

@@ -7,6 +7,7 @@
 // coalesced.  K and V pieces share one launch.  The copy is bit-exact: no arithmetic.
 #include <hip/hip_runtime.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -24,6 +25,8 @@ struct StoreArgs {
     int32_t pieces;          // n * Hkv * pieces_per_row, per tensor
     int32_t row_shift;       // log2(pieces_per_row); rows are 64..512 bytes, a power of two
     int32_t num_kv_heads;
+    int64_t pool_slots;      // num_blocks * 256
+    int32_t check;           // validate slots (device-data checks)
 };
 
 // grid.y selects K (0) or V (1).
@@ -37,6 +40,10 @@ __global__ __launch_bounds__(256) void kv_store_kernel(StoreArgs a) {
     const int32_t h = row - t * a.num_kv_heads;
     const int32_t slot = a.slots[t];
     if (slot < 0) return;
+    if (a.check && slot >= a.pool_slots) {  // a row outside the pool is skipped and reported
+        if (h == 0 && piece == 0 && !is_v) record_error(pkv::kErrSlot, t, slot);
+        return;
+    }
     const int64_t blk = slot / pkv::kBlock, off = slot % pkv::kBlock;
     const int64_t dst_row = (blk * a.num_kv_heads + h) * pkv::kBlock + off;
     const uint4 val = (is_v ? a.v_new : a.k_new)[p];
@@ -84,6 +91,8 @@ extern "C" int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const
     a.row_shift = 0;
     while ((1 << a.row_shift) < ppr) ++a.row_shift;
     a.num_kv_heads = desc->num_kv_heads;
+    a.pool_slots = int64_t(desc->num_blocks) * pkv::kBlock;
+    a.check = pkv::device_checks();
     const int64_t pieces = int64_t(n) * desc->num_kv_heads * ppr;
     PKV_REQUIRE(pieces <= INT32_MAX - 256, PKV_ERR_INVALID, "n = %d too large for one launch", n);
     a.pieces = int32_t(pieces);
@@ -125,6 +134,9 @@ struct QuantArgs {
     float* k_scale;
     float* v_scale;
     int32_t num_kv_heads;
+    int32_t n;            // batch rows
+    int64_t pool_slots;   // num_blocks * 256
+    int32_t check;        // validate the run list and slots (device-data checks)
 };
 
 // The fp32 estimate q = x * fl(1/s) of x / s has relative error below 2^-23 + 2^-48 (below
@@ -178,6 +190,17 @@ __global__ __launch_bounds__(NT) void kv_store_quant_kernel(QuantArgs a) {
     const int h = blockIdx.y;
     const bool is_v = blockIdx.z != 0;
     const int t0 = a.runs[2 * blockIdx.x], len = a.runs[2 * blockIdx.x + 1];
+    if (a.check) {  // the run must lie in the batch, and its rows in one block of the pool
+        const bool run_ok = t0 >= 0 && len >= 1 && len <= pkv::kBlock && t0 <= a.n - len;
+        const int32_t sc = run_ok ? a.slots[t0] : 0;
+        const bool slot_ok = sc >= 0 && sc < a.pool_slots && sc % pkv::kBlock + len <= pkv::kBlock;
+        if (!run_ok || !slot_ok) {  // the same in every thread: the workgroup leaves together
+            if (threadIdx.x == 0 && h == 0 && !is_v)
+                record_error(run_ok ? pkv::kErrSlot : pkv::kErrRun, run_ok ? t0 : int32_t(blockIdx.x),
+                             run_ok ? sc : t0);
+            return;
+        }
+    }
     const int32_t s0 = a.slots[t0];
     const int64_t blk = s0 / pkv::kBlock;
     const int o0 = s0 % pkv::kBlock;
@@ -299,6 +322,9 @@ extern "C" int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new,
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     a.num_kv_heads = desc->num_kv_heads;
+    a.n = n;
+    a.pool_slots = int64_t(desc->num_blocks) * pkv::kBlock;
+    a.check = pkv::device_checks();
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool f32 = new_dtype == PKV_F32;
     const bool wide = max_run > 16;  // eight wavefronts per run once a run has more than 16 rows
@@ -308,3 +334,5 @@ extern "C" int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new,
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "quantising store launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
+
+int pkv::read_error_kv_store(void* stream, int32_t* out) { return read_clear_error(stream, out); }

@@ -34,6 +34,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -63,7 +64,41 @@ struct PrefillArgs {
     int32_t causal;
     int32_t window;  // > 0 (causal only): a query at position P sees keys P - window + 1 .. P
     float scale_log2;
+    int32_t total_q;
+    int32_t num_blocks;
+    int32_t check;   // launch the instantiation that validates cu_seqlens_q, key lengths and block ids
 };
+
+// Device-data checks (uniform in the workgroup, so a workgroup that fails leaves as a whole).
+// cu_seqlens_q non-decreasing within 0..total_q:
+__device__ bool prefill_cu_ok(const PrefillArgs& a) {
+    bool ok = a.cu_seqlens_q[0] >= 0 && a.cu_seqlens_q[a.B] <= a.total_q;
+    int bad = ok ? 0 : (a.cu_seqlens_q[0] < 0 ? 0 : a.B);
+    for (int s = 0; ok && s < a.B; ++s)
+        if (a.cu_seqlens_q[s + 1] < a.cu_seqlens_q[s]) {
+            ok = false;
+            bad = s + 1;
+        }
+    if (!ok && threadIdx.x == 0 && blockIdx.x == 0) record_error(pkv::kErrCuSeqlens, bad, a.cu_seqlens_q[bad]);
+    return ok;
+}
+// every block id of keys key0..key1-1 of sequence b is in the pool:
+__device__ bool prefill_blocks_ok(const PrefillArgs& a, int b, int key0, int key1) {
+    const int lane = threadIdx.x & 63;
+    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    const int e_end = (key1 + pkv::kBlock - 1) / pkv::kBlock;
+    for (int e0 = key0 / pkv::kBlock; e0 < e_end; e0 += 64) {
+        const int e = e0 + lane;
+        const int v = bt[min(e, e_end - 1)];  // clamped, so the load needs no exec mask
+        const uint64_t bad = __ballot(e < e_end && (v < 0 || v >= a.num_blocks));
+        if (bad != 0) {
+            const int first = __shfl(v, __ffsll(static_cast<unsigned long long>(bad)) - 1, 64);
+            if (threadIdx.x == 0) record_error(pkv::kErrBlock, b, first);
+            return false;
+        }
+    }
+    return true;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -103,7 +138,7 @@ __device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // NW = wavefronts per workgroup (4 or 8): all of them share each staged K/V tile.
-template <int D, int G, int NW>
+template <int D, int G, int NW, bool CHECK>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
     constexpr int kThreads = 64 * NW;
     constexpr int kRows = kWaveRows * NW;  // MFMA query rows per workgroup
@@ -125,6 +160,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     // distance from the end of their sequence (every sequence's last tile first, then every
     // second-to-last tile, ...), so the tiles with the longest causal rows start first; the KV
     // head varies fastest.
+    if (CHECK && !prefill_cu_ok(a)) return;
     const int g = blockIdx.x % a.num_kv_heads;
     int item = blockIdx.x / a.num_kv_heads;
     int b = -1, tile = 0, nq = 0;
@@ -149,12 +185,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     if (b < 0) return;
 
     const int Lk = a.seqlens_k[b];
+    if (CHECK && (Lk < 0 || Lk > int64_t(a.max_blocks) * pkv::kBlock || (a.causal && Lk < nq))) {
+        if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrLength, b, Lk);
+        return;
+    }
     const int qrow0 = a.cu_seqlens_q[b];
     const int q0 = tile * QT;
     const int nqt = min(QT, nq - q0);
     const int pos0 = Lk - nq + q0;  // absolute position of token q0
     const int kv_len = a.causal ? min(Lk, pos0 + nqt) : Lk;
     const int ntiles = (kv_len + kKT - 1) / kKT;
+    if (CHECK && !prefill_blocks_ok(a, b, a.window > 0 ? max(0, pos0 - a.window + 1) / kKT * kKT : 0, kv_len))
+        return;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
@@ -418,7 +460,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
 
 template <int D, int G, int NW>
 hipError_t launch_nw(const PrefillArgs& a, long items, hipStream_t st) {
-    hipLaunchKernelGGL((prefill_kernel<D, G, NW>), dim3(unsigned(items)), dim3(64 * NW), 0, st, a);
+    // device-data checks run in their own instantiation, so the production one is unchanged by them
+    if (a.check) hipLaunchKernelGGL((prefill_kernel<D, G, NW, true>), dim3(unsigned(items)), dim3(64 * NW), 0, st, a);
+    else hipLaunchKernelGGL((prefill_kernel<D, G, NW, false>), dim3(unsigned(items)), dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
 
@@ -506,6 +550,9 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
     a.causal = causal != 0;
     a.window = window;
     a.scale_log2 = softmax_scale * kLog2e;
+    a.total_q = total_q;
+    a.num_blocks = desc->num_blocks;
+    a.check = pkv::device_checks();
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int cus = current_num_cus();
     const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, st) : launch_g<128>(a, total_q, G, cus, st);
@@ -534,3 +581,5 @@ extern "C" int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const v
     return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
                         v_cache, block_tables, max_blocks, softmax_scale, 1, window, out, stream);
 }
+
+int pkv::read_error_prefill(void* stream, int32_t* out) { return read_clear_error(stream, out); }

@@ -187,3 +187,9 @@ def test_copy_blocks_rejects_bad_arguments():
     assert call(_desc(kv_dtype=P.I8), scales=(FAKE, None)) == P.ERR_INVALID
     assert call(_desc(head_dim=80)) == P.ERR_UNSUPPORTED
     assert call(_desc(), n=0, ptr=None) == P.OK                         # nothing to copy
+
+
+def test_device_check_switch_and_error_word_arguments():
+    assert P.lib().pkv_set_device_checks(1) == P.OK
+    assert P.lib().pkv_set_device_checks(0) == P.OK
+    assert P.lib().pkv_device_error(None, None, None, None) == P.ERR_INVALID  # code is required

@@ -1,0 +1,174 @@
+"""Device-data checks on the GPU: with checks on, every kernel turns an out-of-range index it reads
+from device memory into an entry in the error word instead of using it.
+
+Every bad value here is chosen so that even an unchecked kernel would stay inside memory the test
+owns: caches, tables, lengths, queries and outputs are views of buffers one block, row or entry
+larger than the view the kernel is told about.  Each case checks the reported (code, where, value),
+that the word is cleared by reading it, and that the valid part of the call still did its work.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_kvcache_amd as P
+from tests.gpu_cases import say
+
+pytestmark = pytest.mark.gpu
+NB, HKV, HQ, D = 6, 2, 4, 128
+SLOT, BLOCK_ID, LENGTH, SEQUENCE, RUN, CU_SEQLENS, ROWS = 1, 2, 3, 4, 5, 6, 7
+
+
+@pytest.fixture
+def checks(gpu):
+    P.set_device_checks(True)
+    assert P.device_error() == (0, 0, 0)
+    yield gpu
+    P.set_device_checks(False)
+    P.device_error()
+
+
+def _caches(dev, dtype=torch.bfloat16, fill=0):
+    """K and V caches of NB blocks as views of NB + 1 blocks (an unchecked access to block NB stays
+    inside the allocation)."""
+    full = [torch.full((NB + 1, HKV, 256, D), fill, dtype=dtype, device=dev) for _ in range(2)]
+    return full, [f[:NB] for f in full]
+
+
+def _i32(x, dev):
+    return torch.tensor(x, dtype=torch.int32, device=dev)
+
+
+def _expect(code, where, value):
+    got = P.device_error()
+    say(f"  device error {got}")
+    assert got == (code, where, value)
+    assert P.device_error() == (0, 0, 0)  # reading cleared it
+
+
+def test_no_error_with_valid_inputs(checks):
+    dev = checks
+    _, (kc, vc) = _caches(dev)
+    rows = torch.randn(3, HKV, D, device=dev).to(torch.bfloat16)
+    P.kv_store(rows, rows, _i32([0, 300, NB * 256 - 1], dev), kc, vc)
+    _expect(0, 0, 0)
+
+
+def test_store_skips_a_slot_outside_the_pool(checks):
+    dev = checks
+    full, (kc, vc) = _caches(dev)
+    rows = torch.randn(3, HKV, D, device=dev).to(torch.bfloat16)
+    P.kv_store(rows, rows, _i32([5, NB * 256 + 7, 600], dev), kc, vc)
+    _expect(SLOT, 1, NB * 256 + 7)
+    assert torch.equal(kc[0, :, 5], rows[0]) and torch.equal(kc[2, :, 600 - 512], rows[2])
+    assert not full[0][NB].any()  # the block past the pool was not written
+
+
+def test_quantising_store_rejects_a_bad_run(checks):
+    dev = checks
+    full, (kc, vc) = _caches(dev, torch.int8)
+    ks = torch.zeros((NB, HKV), device=dev)
+    vs = torch.zeros_like(ks)
+    rows = torch.randn(4, HKV, D, device=dev).to(torch.bfloat16)
+    slots = _i32([256, 257, 258, 259], dev)
+    # run 1 claims no rows (length 0); run 0 is valid and still stored
+    runs = (_i32([0, 1, 1, 0], dev), 2, 1)
+    P.kv_store_quant(rows, rows, slots, kc, vc, ks, vs, runs=runs)
+    _expect(RUN, 1, 1)
+    assert ks[1].abs().sum() > 0 and kc[1, :, 0].abs().sum() > 0
+
+
+def test_quantising_store_rejects_a_run_leaving_its_block(checks):
+    dev = checks
+    _, (kc, vc) = _caches(dev, torch.int8)
+    ks = torch.zeros((NB, HKV), device=dev)
+    rows = torch.randn(3, HKV, D, device=dev).to(torch.bfloat16)
+    slots = _i32([254, 255, 256], dev)  # three rows from offset 254 would cross into the next block
+    P.kv_store_quant(rows, rows, slots, kc, vc, ks, ks.clone(), runs=(_i32([0, 3], dev), 1, 3))
+    _expect(SLOT, 0, 254)
+    assert not kc.any()
+
+
+def test_block_copy_rejects_bad_pairs(checks):
+    dev = checks
+    full, (kc, vc) = _caches(dev, fill=1)
+    kc[3].fill_(2)
+    P.copy_blocks(_i32([3, NB], dev), _i32([4, 5], dev), kc, vc, _i32([256, 10], dev))
+    _expect(BLOCK_ID, 1, NB)
+    assert torch.equal(kc[4], kc[3]) and bool((kc[5] == 1).all())
+    P.copy_blocks(_i32([3], dev), _i32([4], dev), kc, vc, _i32([300], dev))
+    _expect(ROWS, 0, 300)
+
+
+def _decode(dev, tables, lens, order=None, B=2, max_ctx=512, rows=3):
+    """Decode over views: q/out/lens/order/tables one row or entry larger than the kernel is told."""
+    _, (kc, vc) = _caches(dev)
+    kc.normal_()
+    vc.normal_()
+    q_full = torch.randn(B + 1, HQ, D, device=dev).to(torch.bfloat16)
+    out_full = torch.zeros_like(q_full)
+    tab_full = _i32(tables, dev)
+    lens_full = _i32(lens, dev)
+    order_t = None if order is None else _i32(order, dev)[:B]
+    P.paged_attn_decode(q_full[:B], kc, vc, tab_full[:B], lens_full[:B], max_ctx, 0.088, out=out_full[:B],
+                        seq_order=order_t)
+    return out_full
+
+
+def test_decode_rejects_a_block_id_outside_the_pool(checks):
+    out = _decode(checks, [[0, NB], [2, 3], [1, 1]], [300, 400, 1])
+    _expect(BLOCK_ID, 0, NB)
+    assert out[1].abs().sum() > 0  # the valid sequence was attended
+
+
+def test_decode_rejects_a_length_the_table_cannot_hold(checks):
+    out = _decode(checks, [[0, 1], [2, 3], [4, 5]], [513, 200, 1])
+    _expect(LENGTH, 0, 513)
+    assert out[1].abs().sum() > 0
+
+
+def test_decode_rejects_a_launch_order_entry_outside_the_batch(checks):
+    out = _decode(checks, [[0, 1], [2, 3], [4, 5]], [100, 200, 1], order=[2, 1, 0])
+    _expect(SEQUENCE, 0, 2)
+    assert out[1].abs().sum() > 0
+
+
+def test_fused_store_rejects_a_slot_outside_the_pool(checks):
+    dev = checks
+    _, (kc, vc) = _caches(dev)
+    q = torch.randn(2, HQ, D, device=dev).to(torch.bfloat16)
+    new = torch.randn(2, HKV, D, device=dev).to(torch.bfloat16)
+    tab = _i32([[0, 1], [2, 3]], dev)
+    P.decode_store_attend(q, new, new, _i32([NB * 256 + 3, 2 * 256 + 9], dev), kc, vc, tab, _i32([300, 10], dev),
+                          512, 0.088)
+    _expect(SLOT, 0, NB * 256 + 3)
+    assert torch.equal(kc[2, :, 9], new[1])
+
+
+def _prefill(dev, cu, lk, tables, total_q=96, max_q=64, max_k=512):
+    _, (kc, vc) = _caches(dev)
+    kc.normal_()
+    vc.normal_()
+    q = torch.randn(total_q, HQ, D, device=dev).to(torch.bfloat16)
+    out = torch.zeros_like(q)
+    P.paged_attn_prefill(q, _i32(cu, dev), _i32(lk, dev), max_q, max_k, kc, vc, _i32(tables, dev), 0.088, True,
+                         out=out)
+    return out
+
+
+def test_prefill_rejects_a_block_id_outside_the_pool(checks):
+    out = _prefill(checks, [0, 64, 96], [300, 32], [[0, NB], [2, 3]])
+    _expect(BLOCK_ID, 0, NB)
+    assert out[64:].abs().sum() > 0 and not out[:64].any()
+
+
+def test_prefill_rejects_a_key_length_the_table_cannot_hold(checks):
+    out = _prefill(checks, [0, 64, 96], [64, 600], [[0, 1], [2, 3]])
+    _expect(LENGTH, 1, 600)
+    assert out[:64].abs().sum() > 0
+
+
+def test_prefill_rejects_decreasing_cu_seqlens(checks):
+    _prefill(checks, [0, 64, 32], [64, 64], [[0, 1], [2, 3]])
+    code, where, value = P.device_error()
+    assert (code, where, value) == (CU_SEQLENS, 2, 32)
