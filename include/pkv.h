@@ -287,13 +287,35 @@ int pkv_decode_plan(int32_t B, int32_t num_kv_heads, int32_t max_context_len, in
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t num_kv_heads,
                                   int32_t max_context_len, int32_t max_splits);
 
+/* pkv_decode_launch_order: a seq_order (below) for a decode call of this shape.
+ * context_lens: host int32[B], each >= 0; with window > 0 a sequence's work is
+ * min(context_lens[b], window) keys, as in pkv_paged_attn_decode_window.  order: host
+ * int32[B], written with a permutation of 0..B-1.  Host-only; nothing is launched.
+ * Ordering is by work, longest first, with ties kept in sequence order.
+ * When every workgroup of the launch fits on the device at once (B x num_kv_heads x splits
+ * <= compute_units x workgroups_per_cu), workgroup i shares its CU with workgroups
+ * i + compute_units, i + 2 compute_units, ...  The longest-first order is then cut into rounds
+ * of compute_units / (num_kv_heads x splits) sequences, and every odd round is reversed.  The
+ * longest contexts of one round thus share CUs with the shortest of the next, which evens out
+ * the per-CU work.  Otherwise workgroups wait for free slots, and longest-first keeps the
+ * launch's tail short.
+ * compute_units <= 0 takes the current device's CU count (256 without a device, as in
+ * pkv_decode_plan).  workgroups_per_cu <= 0 asks the current device for the occupancy of the
+ * decode kernel of this dtype, head_dim and group size.  Without a device that query fails
+ * with PKV_ERR_HIP.  Bad shapes, a negative length, NULL pointers (B > 0) or an unsupported
+ * group size are PKV_ERR_INVALID / PKV_ERR_UNSUPPORTED. */
+int pkv_decode_launch_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                            const int32_t* context_lens, int32_t max_context_len,
+                            int32_t max_splits, int32_t window, int32_t compute_units,
+                            int32_t workgroups_per_cu, int32_t* order);
+
 /* q: device [B][Hq][head_dim], f32 when the cache is f32, bf16 otherwise.
  * k_cache, v_cache: device, layout above.  k_scale, v_scale: int8 caches only, else NULL.
  * block_tables: device int32[B][max_blocks]; context_lens: device int32[B] -- the number
  * of tokens to attend, including the one just stored; 0 gives a zero output.
  * seq_order: NULL, or device int32[B], a permutation of 0..B-1 giving the order in which the
- * sequences' workgroups are launched (longest context first shortens the tail of the launch);
- * the output stays indexed by sequence.
+ * sequences' workgroups are launched (pkv_decode_launch_order computes a good one); the output
+ * stays indexed by sequence.
  * max_context_len: host upper bound of context_lens (sizes the split plan).
  * out: device [B][Hq][head_dim] in the dtype of q.  workspace: device, at least
  * pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0). */

@@ -70,6 +70,7 @@ SIGNATURES = {
     "pkv_store_runs": (_i32, [_p32, _i32, _p32, _i32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
     "pkv_decode_plan": (_i32, [_i32, _i32, _i32, _i32, _p32, _p32]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_launch_order": (_i32, [_pdesc, _i32, _i32, _p32, _i32, _i32, _i32, _i32, _i32, _p32]),
     "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attn_decode_window": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
@@ -352,6 +353,24 @@ def decode_plan(B, num_kv_heads, max_context_len, max_splits=0):
     _check(lib().pkv_decode_plan(int(B), int(num_kv_heads), int(max_context_len), int(max_splits),
                                  ctypes.byref(s), ctypes.byref(b)), "pkv_decode_plan")
     return s.value, b.value
+
+
+def decode_launch_order(desc, Hq, context_lens, max_context_len, max_splits=0, window=0, compute_units=0,
+                        workgroups_per_cu=0, out=None):
+    """pkv_decode_launch_order: a launch order (host int32 [B]) for a decode call of this shape.
+    ``desc``: a cache descriptor (:func:`cache_desc` / :func:`desc_of`); ``context_lens``: host
+    int32 [B]; ``out``: optional host int32 [B] array to fill (e.g. a view of pinned staging)."""
+    import numpy as np
+    lens, plens = _host_i32(context_lens)
+    B = len(lens)
+    if out is None:
+        out = np.empty(B, dtype=np.int32)
+    if out.dtype != np.int32 or out.shape != (B,) or not out.flags.c_contiguous:
+        raise ValueError("out must be a contiguous int32 array of B entries")
+    _check(lib().pkv_decode_launch_order(ctypes.byref(desc), int(Hq), B, plens, int(max_context_len),
+                                         int(max_splits), int(window), int(compute_units), int(workgroups_per_cu),
+                                         out.ctypes.data_as(_p32)), "pkv_decode_launch_order")
+    return out
 
 
 def decode_workspace_bytes(B, Hq, head_dim, num_kv_heads, max_context_len, max_splits=0):

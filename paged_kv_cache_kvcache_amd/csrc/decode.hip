@@ -7,7 +7,8 @@
 //
 // Work decomposition
 //   One workgroup (4 wavefronts of 64 lanes) per (sequence, KV head, split), launched in the
-//   caller's sequence order (longest contexts first keeps the tail short).  A split is a run of
+//   caller's sequence order (pkv_decode_launch_order: longest contexts first, or balanced per CU
+//   when the whole launch is resident at once).  A split is a run of
 //   blocks_per_split 256-token blocks.  Inside a block, wavefront w owns tokens 64w..64w+63 (a
 //   "tile"), so every wavefront walks the split's blocks with its own independent online-softmax
 //   state and no barrier until the end.
@@ -33,7 +34,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <vector>
 
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -533,12 +536,19 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
 // unsplit: splits add partial-state traffic and a second launch, and the longest-first order
 // already balances the tail.
 int num_cus() {
+    constexpr int kDevices = 16;
+    static std::atomic<int> cache[kDevices];  // per device, filled on first use
     int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();  // no device here: plan for MI355X's 256 CUs
         return 256;
     }
+    if (dev < kDevices && (n = cache[dev].load(std::memory_order_relaxed)) > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -583,7 +593,97 @@ hipError_t launch_d(const DecodeArgs& a, int B, int G, int D, hipStream_t st) {
     return D == 64 ? launch_g<DT, 64>(a, B, G, st) : launch_g<DT, 128>(a, B, G, st);
 }
 
+// ------------------------------------------------------------------------------ launch order
+template <int DT, int D>
+const void* split_kernel_g(int G) {
+    switch (G) {
+        case 1: return reinterpret_cast<const void*>(&decode_split_kernel<DT, D, 1, false>);
+        case 2: return reinterpret_cast<const void*>(&decode_split_kernel<DT, D, 2, false>);
+        case 4: return reinterpret_cast<const void*>(&decode_split_kernel<DT, D, 4, false>);
+        default: return reinterpret_cast<const void*>(&decode_split_kernel<DT, D, 8, false>);
+    }
+}
+
+template <int DT>
+const void* split_kernel_d(int D, int G) {
+    return D == 64 ? split_kernel_g<DT, 64>(G) : split_kernel_g<DT, 128>(G);
+}
+
+// Workgroups of the production split kernel for (dtype, D, G) that one CU of the current device
+// holds at once; 0 when there is no device to ask.  Cached per (device, instantiation).
+int resident_per_cu(int dt, int D, int G) {
+    constexpr int kDevices = 16;
+    static std::atomic<int> cache[kDevices][3][2][4];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+    std::atomic<int>* slot = dev < kDevices ? &cache[dev][dt][D == 128][gi] : nullptr;
+    if (slot != nullptr && slot->load() > 0) return slot->load();
+    const void* k = dt == PKV_F32 ? split_kernel_d<PKV_F32>(D, G)
+                  : dt == PKV_BF16 ? split_kernel_d<PKV_BF16>(D, G) : split_kernel_d<PKV_I8>(D, G);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (slot != nullptr) slot->store(n);
+    return n;
+}
+
 }  // namespace
+
+extern "C" int pkv_decode_launch_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                                       const int32_t* context_lens, int32_t max_context_len, int32_t max_splits,
+                                       int32_t window, int32_t compute_units, int32_t workgroups_per_cu,
+                                       int32_t* order) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    const int Hkv = desc->num_kv_heads, D = desc->head_dim;
+    PKV_REQUIRE(B >= 0 && Hq > 0 && max_context_len >= 0 && max_splits >= 0 && window >= 0, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hq=%d, max_context_len=%d, max_splits=%d, window=%d)", B, Hq, max_context_len,
+                max_splits, window);
+    PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+    const int G = Hq / Hkv;
+    PKV_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, PKV_ERR_UNSUPPORTED,
+                "query group size %d (Hq/Hkv): supported 1, 2, 4, 8", G);
+    if (B == 0) return PKV_OK;
+    PKV_REQUIRE(context_lens && order, PKV_ERR_INVALID, "NULL pointer");
+    // one sort key per sequence: work descending in the high half, the index ascending in the low
+    // half (so ties keep sequence order)
+    std::vector<uint64_t> key(B);
+    for (int b = 0; b < B; ++b) {
+        PKV_REQUIRE(context_lens[b] >= 0, PKV_ERR_INVALID, "context_lens[%d] = %d", b, context_lens[b]);
+        const uint32_t work = uint32_t(window > 0 ? std::min(context_lens[b], window) : context_lens[b]);
+        key[b] = (uint64_t(~work) << 32) | uint32_t(b);
+    }
+    std::sort(key.begin(), key.end());
+    std::vector<int32_t> d(B);
+    for (int b = 0; b < B; ++b) d[b] = int32_t(key[b] & 0xffffffffu);
+
+    const int cus = compute_units > 0 ? compute_units : num_cus();
+    const int per_cu = workgroups_per_cu > 0 ? workgroups_per_cu : resident_per_cu(desc->kv_dtype, D, G);
+    PKV_REQUIRE(per_cu > 0, PKV_ERR_HIP, "no device to query the decode kernel's occupancy on");
+    const int span = window > 0 ? int(std::min<int64_t>(max_context_len, int64_t(window) + pkv::kBlock - 1))
+                                : max_context_len;
+    int S, bps;
+    plan(B, Hkv, span, max_splits, &S, &bps);
+    const int64_t per_seq = int64_t(Hkv) * S;  // a sequence's workgroups are consecutive in the launch
+    const int64_t round = std::max<int64_t>(1, cus / per_seq);  // sequences per round of one workgroup per CU
+    if (int64_t(B) * per_seq <= int64_t(cus) * per_cu && B > round) {
+        // every workgroup is resident from the start, and workgroup i shares its CU with i + cus,
+        // i + 2 cus, ...: alternate the direction of successive rounds so that the long contexts of
+        // one round share CUs with the short ones of the next
+        for (int64_t r = 0; r * round < B; ++r) {
+            const int64_t lo = r * round, hi = std::min<int64_t>(B, lo + round);
+            if (r & 1) std::reverse(d.begin() + lo, d.begin() + hi);
+        }
+    }
+    std::copy(d.begin(), d.end(), order);
+    return PKV_OK;
+}
 
 extern "C" int pkv_decode_plan(int32_t B, int32_t num_kv_heads, int32_t max_context_len, int32_t max_splits,
                                int32_t* splits, int32_t* blocks_per_split) {

@@ -6,11 +6,13 @@ store kernel writes the new K/V rows, then the attention kernel runs.  Every com
 libpkv; this module only moves arrays.
 """
 
+import ctypes
+
 import numpy as np
 import torch
 
-from . import (BF16, BLOCK, F32, I8, Allocator, copy_blocks, decode_store_attend, decode_workspace_bytes, kv_store,
-               kv_store_quant, paged_attn_decode, paged_attn_prefill)
+from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_store_attend, decode_workspace_bytes,
+               desc_of, kv_store, kv_store_quant, lib, paged_attn_decode, paged_attn_prefill)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 
@@ -84,6 +86,7 @@ class DecodeBatch:
         if self.fused and self.window:
             raise ValueError("the fused store+attend step has no sliding window")
         dev = kv.device
+        self._desc = desc_of(kv.k_cache)
         # pinned staging for the per-step metadata: slots[B] | lens[B] | order[B] | tables[B][max_blocks]
         # and, with cow, the step's block copies: src[B] | dst[B] | rows[B]
         nmeta = 3 * self.B + self.B * self.max_blocks
@@ -95,6 +98,11 @@ class DecodeBatch:
         self.context_lens = self._meta[self.B:2 * self.B]
         self.seq_order = self._meta[2 * self.B:3 * self.B]
         self.block_tables = self._meta[3 * self.B:nmeta].view(self.B, self.max_blocks)
+        pin = self._pin.numpy()
+        p32 = ctypes.POINTER(ctypes.c_int32)
+        self._order_args = (ctypes.byref(self._desc), self.Hq, self.B, pin[self.B:].ctypes.data_as(p32),
+                            self.max_context_len, int(max_splits), self.window, 0, 0,
+                            pin[2 * self.B:].ctypes.data_as(p32))
         self._cow = self._meta[nmeta:]
         self.n_copies = 0
         nbytes = decode_workspace_bytes(self.B, self.Hq, kv.D, kv.Hkv, self.max_context_len, max_splits)
@@ -129,7 +137,9 @@ class DecodeBatch:
         lens = pin[B:2 * B]
         self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=lens)
         self.host_context_lens, self.host_block_tables = lens, tab  # valid until the next upload
-        pin[2 * B:3 * B] = np.argsort(-lens, kind="stable")  # longest contexts launch first
+        # longest contexts first; when the whole launch is resident at once, balanced per CU
+        # (pkv_decode_launch_order, called with pointers bound once: it runs every step)
+        _check(lib().pkv_decode_launch_order(*self._order_args), "pkv_decode_launch_order")
 
     def step(self, tokens, q, k_new, v_new, softmax_scale, out=None, k_scale_new=None, v_scale_new=None):
         """One decode step: append one token per sequence, store its K/V, attend.  Returns out [B][Hq][D]."""

@@ -169,6 +169,75 @@ def test_decode_plan():
     assert P.decode_workspace_bytes(256, 16, 128, 8, 2048, 0) == 0
 
 
+def _cu_work(order, lens, per_seq, cus):
+    """Keys per CU when workgroup i of the launch (sequence order[i // per_seq]) runs on CU i % cus."""
+    work = np.zeros(cus, dtype=np.int64)
+    for i in range(len(order) * per_seq):
+        work[i % cus] += lens[order[i // per_seq]]
+    return work
+
+
+def test_decode_launch_order_longest_first_when_workgroups_queue():
+    rng = np.random.default_rng(3)
+    d = _desc(num_kv_heads=8, head_dim=128, kv_dtype=P.BF16)
+    lens = rng.integers(100, 2049, size=256).astype(np.int32)
+    lens[10] = lens[11] = lens[200]  # ties keep sequence order
+    # 256 x 8 workgroups, 2 per CU of 256 CUs: they queue, so longest context first
+    order = P.decode_launch_order(d, 16, lens, 2048, compute_units=256, workgroups_per_cu=2)
+    assert sorted(order) == list(range(256))
+    assert np.all(np.diff(lens[order]) <= 0)
+    for i, j in zip(order, order[1:]):
+        assert lens[i] != lens[j] or i < j
+    assert list(P.decode_launch_order(d, 16, np.full(300, 7), 7, compute_units=256, workgroups_per_cu=2)) == \
+        list(range(300))
+
+
+def test_decode_launch_order_balances_a_resident_launch():
+    d = _desc(num_kv_heads=8, head_dim=128, kv_dtype=P.BF16)
+    # 64 sequences x 8 KV heads = 512 workgroups, exactly 2 per CU: the two sequences on each CU
+    # of an evenly spaced length mix sum to the same number of keys
+    lens = (8192 - 64 * np.random.default_rng(0).permutation(64)).astype(np.int32)
+    order = P.decode_launch_order(d, 32, lens, 8192, compute_units=256, workgroups_per_cu=2)
+    assert sorted(order) == list(range(64))
+    work = _cu_work(order, lens, 8, 256)
+    assert work.min() == work.max() == 8192 + 8192 - 63 * 64
+    first = _cu_work(np.argsort(-lens, kind="stable"), lens, 8, 256)
+    assert first.max() > work.max()
+    # random lengths, a partial last round and three workgroups per CU: never worse than longest first
+    rng = np.random.default_rng(5)
+    for B, per_cu in ((48, 2), (64, 2), (80, 3), (96, 3)):
+        lens = rng.integers(4096, 8193, size=B).astype(np.int32)
+        order = P.decode_launch_order(d, 32, lens, 8192, compute_units=256, workgroups_per_cu=per_cu)
+        assert sorted(order) == list(range(B))
+        assert _cu_work(order, lens, 8, 256).max() <= _cu_work(np.argsort(-lens, kind="stable"), lens, 8, 256).max()
+    # a window caps each sequence's work: every context longer than the window is a tie
+    lens = np.array([9000, 300, 5000, 700, 8000], dtype=np.int32)
+    order = P.decode_launch_order(d, 16, lens, 9000, window=1000, compute_units=256, workgroups_per_cu=1)
+    assert list(order) == [0, 2, 4, 3, 1]
+
+
+def test_decode_launch_order_errors():
+    d = _desc()
+    assert list(P.decode_launch_order(d, 4, np.zeros(0, np.int32), 0, compute_units=4, workgroups_per_cu=1)) == []
+    with pytest.raises(RuntimeError):
+        P.decode_launch_order(d, 4, [5, -1], 5, compute_units=4, workgroups_per_cu=1)
+    with pytest.raises(RuntimeError):
+        P.decode_launch_order(d, 3, [5, 1], 5, compute_units=4, workgroups_per_cu=1)  # Hq not a multiple of Hkv
+    lens = np.array([5, 1], dtype=np.int32)
+    out = np.empty(2, dtype=np.int32)
+    rc = P.lib().pkv_decode_launch_order(ctypes.byref(d), 4, 2, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         5, 0, 0, 4, 1, None)
+    assert rc == P.ERR_INVALID
+    rc = P.lib().pkv_decode_launch_order(ctypes.byref(d), 32, 2, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         5, 0, 0, 4, 1, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    assert rc == P.ERR_UNSUPPORTED  # group size 16
+    if not torch.cuda.is_available():
+        # the occupancy query needs a device
+        rc = P.lib().pkv_decode_launch_order(ctypes.byref(d), 4, 2, lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                             5, 0, 0, 4, 0, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        assert rc == P.ERR_HIP
+
+
 def test_prefill_rejects_bad_descriptor():
     d = _desc(head_dim=80)
     rc = P.lib().pkv_paged_attn_prefill(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE, 1,

@@ -211,3 +211,19 @@ def test_decode_full_size_sampled(gpu, name):
         if cfg["dtype"] == "i8":
             ks = kv.k_scale[idx[::256].long()].cpu().numpy()
             assert np.array_equal(ks, wl["seqs"][b]["k_blk_scale"])
+
+
+def test_launch_order_from_the_device(gpu):
+    """pkv_decode_launch_order with the device's CU count and the decode kernel's occupancy: a
+    permutation; longest first when the workgroups queue (B=256 x 8 KV heads), balanced rounds when
+    every workgroup is resident at once (B=64 x 8 KV heads, G=4)."""
+    rng = np.random.default_rng(2)
+    d = P.cache_desc(16, 8, 128, P.BF16)
+    lens = rng.integers(100, 2049, size=256).astype(np.int32)
+    order = P.decode_launch_order(d, 16, lens, 2048)
+    assert sorted(order) == list(range(256)) and np.all(np.diff(lens[order]) <= 0)
+    lens = rng.integers(4096, 8193, size=64).astype(np.int32)
+    order = P.decode_launch_order(d, 32, lens, 8192)
+    say(f"  B=64 G=4 order head {list(order[:4])} ... tail {list(order[-4:])}")
+    assert sorted(order) == list(range(64))
+    assert not np.all(np.diff(lens[order]) <= 0)  # 512 workgroups fit the device at once
