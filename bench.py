@@ -345,7 +345,7 @@ def cpu_baseline_decode(wl, first=8, window=0):
 def bench_prefill(args, cfg):
     import torch
     import workloads as W
-    from paged_kv_cache_kvcache_amd import BF16, kv_store, paged_attn_prefill
+    from paged_kv_cache_kvcache_amd import BF16, desc_of, kv_store, paged_attn_prefill_ordered, prefill_work_order
     from paged_kv_cache_kvcache_amd import runner as R
 
     dev = torch.device("cuda:0")
@@ -368,17 +368,20 @@ def bench_prefill(args, cfg):
         tab, lens = kv.alloc.block_tables(ids, wl["num_blocks"])  # whole sequences, later segments included
         mb = max(1, -(-int(lens.max()) // 256))
         tab = np.ascontiguousarray(tab[:, :mb])
-        metas.append((cu, lk, slots, tab, mb))
+        # the chunk's work items, heaviest first in CU-balanced rounds (pkv_prefill_work_order)
+        items = prefill_work_order(desc_of(kv.k_cache), Hq, cu, lk, True, args.window)
+        metas.append((cu, lk, slots, tab, mb, items))
     host_s = time.perf_counter() - t0
     # device-resident inputs of every chunk
     dchunks, flops = [], 0
-    for ch, (cu, lk, slots, tab, mb) in zip(chunks, metas):
+    for ch, (cu, lk, slots, tab, mb, items) in zip(chunks, metas):
         dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i] + a:ncached[i] + b]
                                                        for i, a, b in ch]), dev)
         q, k, v = dv("q"), dv("k"), dv("v")
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         dchunks.append(dict(q=q, k=k, v=v, cu=to(cu), lk=to(lk), slots=to(slots), tab=to(tab).view(len(ch), mb),
-                            max_q=int(np.diff(cu).max()), max_k=int(lk.max()), out=torch.empty_like(q)))
+                            items=to(items), max_q=int(np.diff(cu).max()), max_k=int(lk.max()),
+                            out=torch.empty_like(q)))
         for b in range(len(ch)):
             nq, L = int(cu[b + 1] - cu[b]), int(lk[b])
             # causal pairs (within the window when there is one)
@@ -395,8 +398,8 @@ def bench_prefill(args, cfg):
             kv_store(d["k"], d["v"], d["slots"], kv.k_cache, kv.v_cache)
             if timed is not None:
                 ev[timed][c][0].record(stream)
-            paged_attn_prefill(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache, d["tab"],
-                               scale, True, out=d["out"], window=args.window)
+            paged_attn_prefill_ordered(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache,
+                                       d["tab"], scale, d["items"], True, args.window, out=d["out"])
             if timed is not None:
                 ev[timed][c][1].record(stream)
 
@@ -421,6 +424,11 @@ def bench_prefill(args, cfg):
     total_new = sum(n_new)
     log(f"[bench] prefill {nch} chunks, {total_new} new tokens, {flops / 1e9:.2f} GFLOP; prefill kernels "
         f"{kern_s * 1e6:.1f} us/step -> {tflops:.1f} TFLOP/s; step {elapsed / args.steps * 1e3:.3f} ms")
+    # counter traffic of one step (mean per dispatch x chunks), when taken on this workload and the
+    # current kernel source
+    traffic = stored_traffic("prefill_kernel") if (cfg["name"] == "prefill_prefix" and args.seed == 0 and
+                                                  args.window == 0) else None
+    traffic = None if traffic is None else traffic * nch
     res = dict(
         metric="paged decode tokens/s + KV HBM GB/s (% of peak); prefill TFLOP/s",
         value=total_new * args.steps / elapsed, unit="prefill tokens/s", n_gpus=1, steps=args.steps,
@@ -433,7 +441,7 @@ def bench_prefill(args, cfg):
                     cached_tokens=sum(ncached), seed=args.seed),
         prefill_kernel_us=kern_s * 1e6, prefill_tflops=tflops, host_admit_us=host_s * 1e6,
         roofline=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=tflops / BF16_PEAK_TFLOPS, traffic=None, kernel="prefill (all chunks of one step)",
+                      frac=tflops / BF16_PEAK_TFLOPS, traffic=traffic, kernel="prefill (all chunks of one step)",
                       flops_per_step=flops),
     )
     if not args.no_cpu_baseline and args.window == 0:

@@ -391,6 +391,49 @@ int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const void* q, int
                                   const int32_t* block_tables, int32_t max_blocks,
                                   float softmax_scale, int32_t window, void* out, void* stream);
 
+/* Prefill in a caller-given work order.  A work item is one (sequence, query tile) of a launch;
+ * its workgroups cover every KV head.  Items run in the order they are listed.
+ * pkv_paged_attn_prefill finds each workgroup's item on the device instead: every sequence's last
+ * tile first, then every second-to-last, and so on.
+ *
+ * pkv_prefill_work_order: host-only, nothing is launched.  It writes the launch's items into
+ * work_items (host int32[capacity]), each (sequence << 16) | query tile, and their count into
+ * *n_items.  cu_seqlens_q (host int32[B+1], starting at 0) and seqlens_k (host int32[B]) are
+ * those of the call; causal and window are as in that call.  Order:
+ *   - by work, heaviest first: key tiles of 64 keys the item attends, plus one;
+ *   - cut into rounds of (CUs of the current device) / num_kv_heads items;
+ *   - every odd round reversed, so the heavy items of one round share CUs with the light items of
+ *     the next.
+ * Ties keep sequence and tile order.  Query tiles hold pkv_prefill_tile_rows tokens, which
+ * depends on total_q = cu_seqlens_q[B], B, the group size and the device.
+ * Errors:
+ *   - more items than capacity: PKV_ERR_SMALL_BUFFER;
+ *   - B above 32767: PKV_ERR_INVALID;
+ *   - decreasing cu_seqlens_q, or seqlens_k shorter than the new tokens of a causal call:
+ *     PKV_ERR_INVALID.
+ *
+ * pkv_paged_attn_prefill_ordered: pkv_paged_attn_prefill / _window (window = 0: every key) with
+ * work_items (device int32[n_items]).  work_items must hold every item of the call exactly once,
+ * as pkv_prefill_work_order gives them for the same cu_seqlens_q, seqlens_k, shapes and device.
+ * Outputs are bitwise those of the unordered call.  n_items = 0 does nothing.  The items are
+ * device data: with device-data checks on, an item whose sequence or tile does not exist is
+ * recorded as error 5 (where = its index, value = the item).
+ *
+ * pkv_prefill_tile_rows: query tokens per work item of a launch of this shape. */
+int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                           const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
+                           int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items);
+int pkv_paged_attn_prefill_ordered(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                   const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                   int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, int32_t max_blocks,
+                                   float softmax_scale, int32_t causal, int32_t window,
+                                   const int32_t* work_items, int32_t n_items, void* out,
+                                   void* stream);
+int pkv_prefill_tile_rows(const pkv_cache_desc* desc, int32_t Hq, int32_t B, int32_t total_q,
+                          int32_t* tile_rows);
+
 #ifdef __cplusplus
 }
 #endif

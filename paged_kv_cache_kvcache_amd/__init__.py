@@ -81,6 +81,10 @@ SIGNATURES = {
                                       _f32, _i32, _vp, _vp]),
     "pkv_paged_attn_prefill_window": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                              _i32, _f32, _i32, _vp, _vp]),
+    "pkv_paged_attn_prefill_ordered": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                              _i32, _f32, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "pkv_prefill_tile_rows": (_i32, [_pdesc, _i32, _i32, _i32, _p32]),
+    "pkv_prefill_work_order": (_i32, [_pdesc, _i32, _i32, _p32, _p32, _i32, _i32, _p32, _i32, _p32]),
 }
 
 _lib = None
@@ -427,6 +431,47 @@ def decode_store_attend(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_t
                                          int(max_context_len), int(max_splits), float(softmax_scale), _ptr(out),
                                          _ptr(workspace), ws_bytes, _stream(stream)),
            "pkv_decode_store_attend")
+    return out
+
+
+def prefill_tile_rows(desc, Hq, B, total_q):
+    """pkv_prefill_tile_rows: query tokens per work item of a prefill launch of this shape."""
+    t = ctypes.c_int32()
+    _check(lib().pkv_prefill_tile_rows(ctypes.byref(desc), int(Hq), int(B), int(total_q), ctypes.byref(t)),
+           "pkv_prefill_tile_rows")
+    return t.value
+
+
+def prefill_work_order(desc, Hq, cu_seqlens_q, seqlens_k, causal=True, window=0):
+    """pkv_prefill_work_order: the work items of a prefill call (host int32 array)."""
+    import numpy as np
+    cu, pcu = _host_i32(cu_seqlens_q)
+    lk, plk = _host_i32(seqlens_k)
+    B = len(lk)
+    if len(cu) != B + 1:
+        raise ValueError("cu_seqlens_q must have B + 1 entries")
+    cap = int(cu[-1]) + B if B else 0  # at least one query token per item
+    items = np.empty(max(cap, 1), dtype=np.int32)
+    n = ctypes.c_int32()
+    _check(lib().pkv_prefill_work_order(ctypes.byref(desc), int(Hq), B, pcu, plk, int(bool(causal)), int(window),
+                                        items.ctypes.data_as(_p32), cap, ctypes.byref(n)), "pkv_prefill_work_order")
+    return items[:n.value]
+
+
+def paged_attn_prefill_ordered(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache,
+                               block_tables, softmax_scale, work_items, causal=True, window=0, out=None, stream=None):
+    """Varlen prefill whose work items run in the order of ``work_items`` (device int32, each
+    ``(sequence << 16) | query tile``, every item of the launch exactly once)."""
+    desc = desc_of(k_cache)
+    total_q, Hq, _ = q.shape
+    B = int(seqlens_k.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().pkv_paged_attn_prefill_ordered(
+        ctypes.byref(desc), _ptr(q), int(Hq), _ptr(cu_seqlens_q), _ptr(seqlens_k), B, int(total_q),
+        int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), float(softmax_scale), int(bool(causal)), int(window), _ptr(work_items),
+        int(work_items.shape[0]), _ptr(out), _stream(stream)), "pkv_paged_attn_prefill_ordered")
     return out
 
 

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <cmath>
 #include <type_traits>
 
@@ -67,6 +68,8 @@ struct PrefillArgs {
     int32_t total_q;
     int32_t num_blocks;
     int32_t check;   // launch the instantiation that validates cu_seqlens_q, key lengths and block ids
+    const int32_t* items;  // NULL: the built-in order; else item i = (sequence << 16) | query tile
+    int32_t n_items;
 };
 
 // Device-data checks (uniform in the workgroup, so a workgroup that fails leaves as a whole).
@@ -164,6 +167,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     const int g = blockIdx.x % a.num_kv_heads;
     int item = blockIdx.x / a.num_kv_heads;
     int b = -1, tile = 0, nq = 0;
+    if (a.items != nullptr) {  // the caller's order (the grid has exactly n_items x Hkv workgroups)
+        const int it = a.items[item];
+        b = it >> 16;
+        tile = it & 0xffff;
+        if (CHECK) {
+            const bool seq_ok = it >= 0 && b < a.B;
+            const int n = seq_ok ? a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b] : 0;
+            if (!seq_ok || tile >= (n + QT - 1) / QT) {
+                if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrRun, item, it);
+                return;
+            }
+        }
+        nq = a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b];
+    }
     for (int r = 0; b < 0; ++r) {
         int live = 0;
         for (int s = 0; s < a.B; ++s) {
@@ -469,13 +486,20 @@ hipError_t launch_nw(const PrefillArgs& a, long items, hipStream_t st) {
 // Eight-wavefront workgroups halve the K/V staging per query row; four-wavefront ones give twice as
 // many workgroups, which shortens the tail of a small launch (its longest causal rows).  Eight are
 // used once a launch has at least two workgroups per CU of them.
+int choose_nw(long total_q, int B, int Hkv, int G, int num_cus) {
+    const int QT8 = 8 * kWaveRows / G;
+    const long items8 = ((total_q + QT8 - 1) / QT8 + B) * long(Hkv);
+    return items8 >= 2L * num_cus ? 8 : 4;
+}
+
 template <int D, int G>
 hipError_t launch(const PrefillArgs& a, int total_q, int num_cus, hipStream_t st) {
-    constexpr int QT8 = 8 * kWaveRows / G, QT4 = 4 * kWaveRows / G;
-    const long items8 = ((long(total_q) + QT8 - 1) / QT8 + a.B) * a.num_kv_heads;
-    const long items4 = ((long(total_q) + QT4 - 1) / QT4 + a.B) * a.num_kv_heads;
-    if (items4 > INT32_MAX) return hipErrorInvalidValue;
-    return items8 >= 2L * num_cus ? launch_nw<D, G, 8>(a, items8, st) : launch_nw<D, G, 4>(a, items4, st);
+    const int nw = choose_nw(total_q, a.B, a.num_kv_heads, G, num_cus);
+    const int QT = nw * kWaveRows / G;
+    const long items = a.items != nullptr ? long(a.n_items) * a.num_kv_heads
+                                          : ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
+    if (items > INT32_MAX) return hipErrorInvalidValue;
+    return nw == 8 ? launch_nw<D, G, 8>(a, items, st) : launch_nw<D, G, 4>(a, items, st);
 }
 
 template <int D>
@@ -509,7 +533,8 @@ namespace {
 int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const int32_t* cu_seqlens_q,
                  const int32_t* seqlens_k, int32_t B, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
                  const void* k_cache, const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
-                 float softmax_scale, int32_t causal, int32_t window, void* out, void* stream) {
+                 float softmax_scale, int32_t causal, int32_t window, void* out, void* stream,
+                 const int32_t* items = nullptr, int32_t n_items = 0) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     PKV_REQUIRE(desc->kv_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED, "prefill supports bf16 caches only");
@@ -553,6 +578,8 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
     a.total_q = total_q;
     a.num_blocks = desc->num_blocks;
     a.check = pkv::device_checks();
+    a.items = items;
+    a.n_items = n_items;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int cus = current_num_cus();
     const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, st) : launch_g<128>(a, total_q, G, cus, st);
@@ -580,6 +607,89 @@ extern "C" int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const v
                                              float softmax_scale, int32_t window, void* out, void* stream) {
     return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
                         v_cache, block_tables, max_blocks, softmax_scale, 1, window, out, stream);
+}
+
+extern "C" int pkv_paged_attn_prefill_ordered(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                              const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                              int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                              const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, int32_t max_blocks,
+                                              float softmax_scale, int32_t causal, int32_t window,
+                                              const int32_t* work_items, int32_t n_items, void* out,
+                                              void* stream) {
+    PKV_REQUIRE(n_items >= 0, PKV_ERR_INVALID, "n_items = %d", n_items);
+    PKV_REQUIRE(work_items != nullptr || n_items == 0, PKV_ERR_INVALID, "NULL work_items");
+    if (n_items == 0) return PKV_OK;
+    return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
+                        v_cache, block_tables, max_blocks, softmax_scale, causal, window, out, stream, work_items,
+                        n_items);
+}
+
+extern "C" int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
+                                      int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    PKV_REQUIRE(n_items != nullptr, PKV_ERR_INVALID, "NULL n_items");
+    *n_items = 0;
+    PKV_REQUIRE(B >= 0 && B <= 32767 && Hq > 0 && capacity >= 0 && window >= 0, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hq=%d, capacity=%d, window=%d)", B, Hq, capacity, window);
+    PKV_REQUIRE(Hq % desc->num_kv_heads == 0, PKV_ERR_INVALID, "Hq %d is not a multiple of Hkv %d", Hq,
+                desc->num_kv_heads);
+    const int G = Hq / desc->num_kv_heads;
+    PKV_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, PKV_ERR_UNSUPPORTED, "query group size %d", G);
+    if (B == 0) return PKV_OK;
+    PKV_REQUIRE(cu_seqlens_q && seqlens_k, PKV_ERR_INVALID, "NULL pointer");
+    PKV_REQUIRE(cu_seqlens_q[0] == 0, PKV_ERR_INVALID, "cu_seqlens_q[0] = %d", cu_seqlens_q[0]);
+    for (int b = 0; b < B; ++b) {
+        const int nq = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        PKV_REQUIRE(nq >= 0, PKV_ERR_INVALID, "cu_seqlens_q decreases at %d", b + 1);
+        PKV_REQUIRE(seqlens_k[b] >= 0 && (!causal || seqlens_k[b] >= nq), PKV_ERR_INVALID,
+                    "seqlens_k[%d] = %d for %d new tokens", b, seqlens_k[b], nq);
+    }
+    const int cus = current_num_cus();
+    const int QT = choose_nw(cu_seqlens_q[B], B, desc->num_kv_heads, G, cus) * kWaveRows / G;
+    // the items with their key tiles (+1 for a workgroup's fixed cost): heaviest first, ties in
+    // sequence and tile order
+    std::vector<uint64_t> key;
+    std::vector<int32_t> item;
+    for (int b = 0; b < B; ++b) {
+        const int nq = cu_seqlens_q[b + 1] - cu_seqlens_q[b], L = seqlens_k[b];
+        for (int t = 0; t * QT < nq; ++t) {
+            PKV_REQUIRE(t <= 0xffff, PKV_ERR_UNSUPPORTED, "sequence %d has more than 65536 query tiles", b);
+            const int pos0 = L - nq + t * QT, nqt = std::min(QT, nq - t * QT);
+            const int kv_len = causal ? std::min(L, pos0 + nqt) : L;
+            const int kt0 = window > 0 ? std::max(0, pos0 - window + 1) / kKT : 0;
+            const uint32_t w = uint32_t((kv_len + kKT - 1) / kKT - kt0 + 1);
+            key.push_back((uint64_t(~w) << 32) | uint32_t(item.size()));
+            item.push_back((b << 16) | t);
+        }
+    }
+    const int n = int(item.size());
+    PKV_REQUIRE(n <= capacity && (work_items != nullptr || n == 0), PKV_ERR_SMALL_BUFFER,
+                "%d work items, capacity %d", n, capacity);
+    std::sort(key.begin(), key.end());
+    // rounds of one workgroup per CU: every odd round runs lightest first, so the heavy items of
+    // one round share CUs with the light ones of the next
+    const int round = std::max(1, cus / desc->num_kv_heads);
+    for (int r0 = round; r0 < n; r0 += 2 * round)
+        std::reverse(key.begin() + r0, key.begin() + std::min(n, r0 + round));
+    for (int i = 0; i < n; ++i) work_items[i] = item[key[i] & 0xffffffffu];
+    *n_items = n;
+    return PKV_OK;
+}
+
+extern "C" int pkv_prefill_tile_rows(const pkv_cache_desc* desc, int32_t Hq, int32_t B, int32_t total_q,
+                                     int32_t* tile_rows) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    PKV_REQUIRE(tile_rows != nullptr, PKV_ERR_INVALID, "NULL tile_rows");
+    PKV_REQUIRE(B >= 0 && Hq > 0 && total_q >= 0 && Hq % desc->num_kv_heads == 0, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hq=%d, total_q=%d)", B, Hq, total_q);
+    const int G = Hq / desc->num_kv_heads;
+    PKV_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, PKV_ERR_UNSUPPORTED, "query group size %d", G);
+    *tile_rows = choose_nw(total_q, B, desc->num_kv_heads, G, current_num_cus()) * kWaveRows / G;
+    return PKV_OK;
 }
 
 int pkv::read_error_prefill(void* stream, int32_t* out) { return read_clear_error(stream, out); }

@@ -12,7 +12,8 @@ import numpy as np
 import torch
 
 from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_store_attend, decode_workspace_bytes,
-               desc_of, kv_store, kv_store_quant, lib, paged_attn_decode, paged_attn_prefill)
+               desc_of, kv_store, kv_store_quant, lib, paged_attn_decode, paged_attn_prefill_ordered,
+               prefill_work_order)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 
@@ -303,6 +304,23 @@ def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None,
     return ncached
 
 
+def _attend_chunk(kv, q_new, k_new, v_new, cu, lk, slots, tab, softmax_scale, causal, out):
+    """Upload a chunk's metadata and its work order (pkv_prefill_work_order) in one copy, store the
+    new rows, and attend in that order."""
+    dev = kv.device
+    B, n_new, mb = len(lk), len(slots), tab.shape[1]
+    items = prefill_work_order(desc_of(kv.k_cache), q_new.shape[1], cu, lk, causal)
+    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel(), items]).astype(np.int32), dev)
+    d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
+    d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
+    d_tab = meta[2 * B + 1 + n_new:2 * B + 1 + n_new + B * mb].view(B, mb)
+    d_items = meta[2 * B + 1 + n_new + B * mb:]
+    kv.store(d_slots, k_new, v_new)
+    n_q = np.diff(cu)
+    return paged_attn_prefill_ordered(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache,
+                                      d_tab, softmax_scale, d_items, causal, out=out)
+
+
 def prefill_segments(kv, segments, q_new, k_new, v_new, softmax_scale, causal=True, out=None):
     """One prefill chunk made of segments (seq_id, start, end) of admitted sequences' new tokens, so
     that a prompt longer than the chunk's token budget is computed over several chunks: store the
@@ -310,7 +328,6 @@ def prefill_segments(kv, segments, q_new, k_new, v_new, softmax_scale, causal=Tr
 
     q_new [n][Hq][D], k_new/v_new [n][Hkv][D] (device bf16, segments in order).
     """
-    dev = kv.device
     n_new = int(q_new.shape[0])
     ids = [s[0] for s in segments]
     cu, lk, slots = kv.alloc.prefill_segment_slots(ids, [s[1] for s in segments], [s[2] for s in segments], n_new)
@@ -318,15 +335,7 @@ def prefill_segments(kv, segments, q_new, k_new, v_new, softmax_scale, causal=Tr
     tab, lens = kv.alloc.block_tables(ids, kv.num_blocks)
     mb = max(1, -(-int(lens.max()) // BLOCK))
     tab = np.ascontiguousarray(tab[:, :mb])
-    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel()]).astype(np.int32), dev)
-    B = len(ids)
-    d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
-    d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
-    d_tab = meta[2 * B + 1 + n_new:].view(B, mb)
-    kv.store(d_slots, k_new, v_new)
-    n_q = np.diff(cu)
-    return paged_attn_prefill(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache, d_tab,
-                              softmax_scale, causal, out=out)
+    return _attend_chunk(kv, q_new, k_new, v_new, cu, lk, slots, tab, softmax_scale, causal, out)
 
 
 def prefill_chunk(kv, seq_ids, q_new, k_new, v_new, softmax_scale, causal=True, out=None):
@@ -334,17 +343,8 @@ def prefill_chunk(kv, seq_ids, q_new, k_new, v_new, softmax_scale, causal=True, 
 
     q_new [n_new][Hq][D], k_new/v_new [n_new][Hkv][D] (device bf16, in sequence order).
     """
-    dev = kv.device
     n_new = int(q_new.shape[0])
     cu, lk, slots = kv.alloc.prefill_slots(seq_ids, n_new)
     mb = max(1, -(-int(lk.max()) // BLOCK))
     tab, _ = kv.alloc.block_tables(seq_ids, mb)
-    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel()]).astype(np.int32), dev)
-    B = len(seq_ids)
-    d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
-    d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
-    d_tab = meta[2 * B + 1 + n_new:].view(B, mb)
-    kv.store(d_slots, k_new, v_new)
-    n_q = np.diff(cu)
-    return paged_attn_prefill(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache, d_tab,
-                              softmax_scale, causal, out=out)
+    return _attend_chunk(kv, q_new, k_new, v_new, cu, lk, slots, tab, softmax_scale, causal, out)

@@ -238,6 +238,61 @@ def test_decode_launch_order_errors():
         assert rc == P.ERR_HIP
 
 
+def _item_work(it, cu, lk, qt, causal=True, window=0):
+    """Key tiles (of 64) a prefill work item attends, from the kernel's causal rule."""
+    b, t = it >> 16, it & 0xFFFF
+    nq, L = int(cu[b + 1] - cu[b]), int(lk[b])
+    pos0 = L - nq + t * qt
+    kv_len = min(L, pos0 + min(qt, nq - t * qt)) if causal else L
+    first = max(0, pos0 - window + 1) // 64 if window else 0
+    return -(-kv_len // 64) - first
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 200)])
+def test_prefill_work_order(causal, window):
+    rng = np.random.default_rng(11)
+    d = _desc(num_kv_heads=8, head_dim=128, kv_dtype=P.BF16)
+    nq = rng.integers(1, 900, size=13)
+    nq[3] = 64  # exactly one tile
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    lk = (nq + rng.integers(0, 600, size=13)).astype(np.int32)
+    qt = P.prefill_tile_rows(d, 16, 13, int(cu[-1]))
+    assert qt in (64, 128)
+    items = P.prefill_work_order(d, 16, cu, lk, causal, window)
+    # every (sequence, tile) of the call exactly once
+    assert sorted(items.tolist()) == sorted((b << 16) | t for b in range(13) for t in range(-(-int(nq[b]) // qt)))
+    work = [_item_work(int(i), cu, lk, qt, causal, window) for i in items]
+    R = 256 // 8  # items per round of one workgroup per CU (256 CUs without a device)
+    rounds = [work[r:r + R] for r in range(0, len(work), R)]
+    assert len(rounds) >= 3
+    assert min(rounds[0]) >= max(w for r in rounds[1:] for w in r)  # the heaviest items first
+    for i, r in enumerate(rounds):
+        assert r == sorted(r, reverse=(i % 2 == 0))  # heaviest first, lightest first, ...
+    # rounds hold consecutive ranks of the heaviest-first order
+    assert sorted(work, reverse=True) == [w for i, r in enumerate(rounds) for w in (r if i % 2 == 0 else r[::-1])]
+
+
+def test_prefill_work_order_errors():
+    d = _desc(num_kv_heads=2, head_dim=64, kv_dtype=P.BF16)
+    assert len(P.prefill_work_order(d, 4, [0], [])) == 0
+    with pytest.raises(RuntimeError):
+        P.prefill_work_order(d, 4, [0, 10, 5], [10, 10])  # decreasing cu_seqlens_q
+    with pytest.raises(RuntimeError):
+        P.prefill_work_order(d, 4, [0, 10], [9])  # causal: fewer keys than new tokens
+    assert len(P.prefill_work_order(d, 4, [0, 10], [9], causal=False)) == 1
+    with pytest.raises(RuntimeError):
+        P.prefill_work_order(d, 3, [0, 10], [10])  # Hq not a multiple of Hkv
+    cu, lk = np.array([0, 200], np.int32), np.array([200], np.int32)
+    out, n = np.empty(2, np.int32), ctypes.c_int32()
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    rc = P.lib().pkv_prefill_work_order(ctypes.byref(d), 4, 1, cu.ctypes.data_as(p32), lk.ctypes.data_as(p32), 1, 0,
+                                        out.ctypes.data_as(p32), 2, ctypes.byref(n))
+    assert rc == P.ERR_SMALL_BUFFER and n.value == 0  # 200 tokens in tiles of 64: four items
+    rc = P.lib().pkv_paged_attn_prefill_ordered(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE,
+                                                1, 0.1, 1, 0, None, 1, FAKE, None)
+    assert rc == P.ERR_INVALID  # items missing
+
+
 def test_prefill_rejects_bad_descriptor():
     d = _desc(head_dim=80)
     rc = P.lib().pkv_paged_attn_prefill(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE, 1,

@@ -172,3 +172,18 @@ def test_prefill_rejects_decreasing_cu_seqlens(checks):
     _prefill(checks, [0, 64, 32], [64, 64], [[0, 1], [2, 3]])
     code, where, value = P.device_error()
     assert (code, where, value) == (CU_SEQLENS, 2, 32)
+
+
+def test_ordered_prefill_rejects_an_item_outside_the_call(checks):
+    dev = checks
+    _, (kc, vc) = _caches(dev)
+    kc.normal_()
+    vc.normal_()
+    q = torch.randn(96, HQ, D, device=dev).to(torch.bfloat16)
+    out = torch.zeros_like(q)
+    # items of sequence 0 (tile 0) and sequence 1 (tile 0), then a sequence that does not exist
+    items = _i32([0, 1 << 16, 2 << 16], dev)
+    P.paged_attn_prefill_ordered(q, _i32([0, 64, 96], dev), _i32([64, 32], dev), 64, 64, kc, vc,
+                                 _i32([[0, 1], [2, 3]], dev), 0.088, items, True, out=out)
+    _expect(RUN, 2, 2 << 16)
+    assert out[:64].abs().sum() > 0 and out[64:].abs().sum() > 0

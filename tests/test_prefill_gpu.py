@@ -92,3 +92,44 @@ def test_prefill_is_deterministic_and_placement_invariant():
     c = gpu_prefill(other, "cuda")
     assert np.array_equal(a, b)
     assert np.array_equal(a, c)
+
+
+@pytest.mark.parametrize("name,over,causal,window", [
+    ("prefill_prefix", {}, True, 0),
+    ("prefill_prefix", dict(B=8, ctx=[1000, 1100, 900, 1050, 1023, 977, 1100, 1040], group=1, shared=0, chunk=9000),
+     True, 0),
+    ("prefill_prefix", dict(B=5, group=2, chunk=2000), False, 0),
+    ("prefill_prefix", dict(B=9, group=3, chunk=3000), True, 300),
+])
+def test_work_order_gives_bitwise_the_built_in_order(name, over, causal, window):
+    """pkv_paged_attn_prefill_ordered with pkv_prefill_work_order's items against the built-in
+    order of pkv_paged_attn_prefill(_window): the same outputs bit for bit, chunk by chunk."""
+    import math
+    import torch
+    import paged_kv_cache_kvcache_amd as P
+    from paged_kv_cache_kvcache_amd import runner as R
+    from tests.gpu_cases import dev_rows
+    cfg = W.config(name, **over)
+    wl = W.prefill_workload(cfg, 0)
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    prompts = wl["prompts"]
+    kv = R.PagedKV(wl["num_blocks"], Hkv, D, P.BF16, wl["free_order"], device="cuda", fill=0)
+    ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+    n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    for ch in W.pack_chunks(n_new, cfg["chunk"]):
+        rows = lambda key: dev_rows(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), "cuda")
+        q, k, v = rows("q"), rows("k"), rows("v")
+        cu, lk, slots = kv.alloc.prefill_slots(ch, int(q.shape[0]))
+        tab, _ = kv.alloc.block_tables(ch, max(1, -(-int(lk.max()) // 256)))
+        kv.store(to(slots), k, v)
+        items = P.prefill_work_order(P.desc_of(kv.k_cache), Hq, cu, lk, causal, window)
+        qt = P.prefill_tile_rows(P.desc_of(kv.k_cache), Hq, len(ch), int(cu[-1]))
+        assert len(items) == sum(-(-int(n) // qt) for n in np.diff(cu))
+        args = (q, to(cu), to(lk), int(np.diff(cu).max()), int(lk.max()), kv.k_cache, kv.v_cache, to(tab),
+                1.0 / math.sqrt(D))
+        ref = P.paged_attn_prefill(*args, causal, window=window)
+        got = P.paged_attn_prefill_ordered(*args, to(items), causal, window)
+        torch.cuda.synchronize()
+        say(f"  chunk of {len(ch)} prompts: {len(items)} items of {qt} tokens")
+        assert torch.equal(ref, got)
