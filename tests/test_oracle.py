@@ -815,3 +815,151 @@ def test_int8_encoding_rules():
 
 def test_pack_chunks_greedy():
     assert W.pack_chunks([1000, 3000, 200, 4096, 1], 4096) == [[0, 1], [2], [3], [4]]
+
+
+# ------------------------------------------------------ the oracle's whole-step glue (steps.py)
+# These pin oracle/steps.py and Allocator.prefill_segment_slots against things that do not come
+# from the oracle: torch's fp64 SDPA over each sequence's *contiguous* rows as drawn by workloads
+# (no block manager, no cache, no table), hand-derived prefix-cache counts and hand-worked slots.
+from oracle import steps as OS  # noqa: E402
+
+
+def _seq_rows_f64(cfg, seq, lo, hi):
+    """K, V rows lo..hi-1 of one drawn sequence as float64 [Hkv][n][D] (int8: codes x token scale)."""
+    if cfg["dtype"] == "i8":
+        k = seq["kq"][lo:hi].astype(np.float64) * seq["k_tok_scale"][lo:hi, :, None].astype(np.float64)
+        v = seq["vq"][lo:hi].astype(np.float64) * seq["v_tok_scale"][lo:hi, :, None].astype(np.float64)
+    elif cfg["dtype"] == "bf16":
+        k = W.bf16_bits_to_f32(seq["k"][lo:hi]).astype(np.float64)
+        v = W.bf16_bits_to_f32(seq["v"][lo:hi]).astype(np.float64)
+    else:
+        k, v = seq["k"][lo:hi].astype(np.float64), seq["v"][lo:hi].astype(np.float64)
+    return k.transpose(1, 0, 2), v.transpose(1, 0, 2)
+
+
+def _q_f64(cfg, x):
+    return x.astype(np.float64) if cfg["dtype"] == "f32" else W.bf16_bits_to_f32(x).astype(np.float64)
+
+
+def _sdpa_decode_ref(cfg, seq, L, window=0):
+    """One decode query per head over the sequence's last min(L, window) contiguous rows."""
+    G, D = cfg["Hq"] // cfg["Hkv"], cfg["D"]
+    lo = max(0, L - window) if window > 0 else 0
+    k, v = _seq_rows_f64(cfg, seq, lo, L)
+    q = _q_f64(cfg, seq["q"])
+    return _sdpa(q[:, None, :], np.repeat(k, G, axis=0), np.repeat(v, G, axis=0), 1.0 / math.sqrt(D))[:, 0]
+
+
+DECODE_GLUE_CASES = [
+    ("tiny_fp32", {}),
+    ("qwen3_decode", dict(B=3, ctx=[1, 257, 700], Hq=4, Hkv=2, D=16)),
+    ("int8_decode", dict(B=3, ctx=[255, 256, 530], Hq=4, Hkv=4, D=16)),
+    ("long_decode", dict(B=2, ctx=[513, 300], Hq=8, Hkv=1, D=8)),
+]
+
+
+@pytest.mark.parametrize("name,over", DECODE_GLUE_CASES, ids=[c[0] for c in DECODE_GLUE_CASES])
+def test_decode_step_equals_sdpa_on_the_drawn_rows(name, over):
+    """decode_step (admit the history, store it, append and store the new token, attend) gives, for
+    every sequence, attention of its query over all of its drawn rows, the new one included: the
+    store-then-attend order of "Nano-vLLM性能调优实战" §2.2 缓存复用策略, context counting the
+    token just stored."""
+    cfg = W.config(name, **over)
+    wl = W.decode_workload(cfg, 0)
+    out = OS.decode_step(wl)
+    for b, (seq, L) in enumerate(zip(wl["seqs"], wl["lens"])):
+        ref = _sdpa_decode_ref(cfg, seq, L)
+        assert np.max(np.abs(out[b] - ref)) < 1e-12, (name, b)
+        one = OS.decode_one_sequence(cfg, seq, L)
+        assert np.max(np.abs(one - ref)) < 1e-12, (name, b)
+
+
+@pytest.mark.parametrize("window", [1, 2, 255, 256, 257, 600])
+def test_windowed_decode_step_equals_sdpa_on_the_last_rows(window):
+    cfg = W.config("qwen3_decode", B=3, ctx=[1, 300, 700], Hq=4, Hkv=2, D=8)
+    wl = W.decode_workload(cfg, 1)
+    out = OS.decode_step(wl, window=window)
+    for b, (seq, L) in enumerate(zip(wl["seqs"], wl["lens"])):
+        ref = _sdpa_decode_ref(cfg, seq, L, window)
+        assert np.max(np.abs(out[b] - ref)) < 1e-12, b
+        assert np.max(np.abs(OS.decode_one_sequence(cfg, seq, L, window) - ref)) < 1e-12, b
+
+
+def _expected_n_cached(lens, group, shared):
+    """Tokens each prompt finds cached, derived by hand from the prefix-cache rules: only full
+    blocks inside the group's shared tokens can match; the block holding a prompt's last token never
+    hits; a block hits only if an earlier prompt of the group held it in full (it was registered
+    then) and every earlier block hit too.  Nothing is freed during admission, so nothing registered
+    is lost."""
+    out = []
+    for i, n in enumerate(lens):
+        earlier = lens[(i // group) * group:i]
+        k = 0
+        while ((k + 1) * BLOCK <= shared and (k + 1) * BLOCK < n
+               and any(m >= (k + 1) * BLOCK for m in earlier)):
+            k += 1
+        out.append(k * BLOCK)
+    return out
+
+
+PREFILL_GLUE_CASES = [
+    # lengths chosen so prefixes of 0, 1 and 2 blocks hit, with prompts shorter than the shared part
+    dict(B=10, ctx=[300, 700, 512, 513, 257, 256, 900, 520, 600, 1000], group=4, chunk=1500),
+    dict(B=6, ctx=[1000, 100, 530, 515, 1024, 260], group=8, chunk=4096),
+]
+
+
+@pytest.mark.parametrize("over", PREFILL_GLUE_CASES, ids=["several_chunks", "one_chunk"])
+def test_prefill_run_equals_sdpa_per_prompt(over):
+    """prefill_run: every prompt's new tokens attend its whole drawn prefix with a bottom-right
+    causal mask ("Nano-vLLM性能调优实战" §2.2: the cache is written, then read), whatever the
+    prefix cache hit and however the prompts were packed into chunks of at most ``chunk`` new
+    tokens (§3.2 关键调度参数: whole prompts, in order, each chunk filled greedily)."""
+    cfg = W.config("prefill_prefix", Hq=4, Hkv=2, D=8, **over)
+    wl = W.prefill_workload(cfg, 0)
+    out, ncached, chunks = OS.prefill_run(wl)
+    assert ncached == _expected_n_cached(wl["lens"], cfg["group"], cfg["shared"])
+    n_new = [L - c for L, c in zip(wl["lens"], ncached)]
+    assert [i for ch in chunks for i in ch] == list(range(len(n_new)))
+    for c, ch in enumerate(chunks):
+        assert sum(n_new[i] for i in ch) <= cfg["chunk"]
+        if c + 1 < len(chunks):  # greedy: the next prompt did not fit
+            assert sum(n_new[i] for i in ch) + n_new[chunks[c + 1][0]] > cfg["chunk"]
+    assert out.shape == (sum(n_new), cfg["Hq"], cfg["D"])
+    G, r = cfg["Hq"] // cfg["Hkv"], 0
+    for p, L, nc in zip(wl["prompts"], wl["lens"], ncached):
+        k, v = _seq_rows_f64(cfg, p, 0, L)
+        q = _q_f64(cfg, p["q"][nc:L]).transpose(1, 0, 2)
+        ref = _sdpa(q, np.repeat(k, G, axis=0), np.repeat(v, G, axis=0), 1.0 / math.sqrt(cfg["D"]),
+                    _bottom_right_mask(L - nc, L)).transpose(1, 0, 2)
+        assert np.max(np.abs(out[r:r + L - nc] - ref)) < 1e-12
+        r += L - nc
+    assert r == out.shape[0]
+    # with the prefix cache off every token is new, and the outputs of the shared tokens repeat
+    out0, nc0, _ = OS.prefill_run(wl, prefix_cache=False)
+    assert nc0 == [0] * len(wl["lens"])
+    assert out0.shape[0] == sum(wl["lens"])
+
+
+def test_prefill_segment_slots_hand_worked():
+    """A 556-token prompt whose first block is cached has 300 new tokens, computed as segments
+    [0, 256) and [256, 300) in two steps ("Nano-vLLM性能调优实战" §3.2: at most a fixed number of new
+    tokens per step).  Each segment's keys are the cached prefix plus the new tokens up to its end."""
+    a = _alloc(10)  # FIFO pool 0, 1, 2, ...
+    base = list(range(1000, 1512))
+    assert a.add_seq(0, base + [1, 2, 3]) == 0  # 515 tokens: blocks 0, 1, 2
+    assert a.add_seq(1, base[:256] + list(range(5000, 5300))) == 256  # block 0 hits; pops 3, 4
+    assert a.block_tables([1], 3) == [[0, 3, 4]]
+    cu, lk, slots = a.prefill_segment_slots([1], [0], [256])
+    assert cu == [0, 256] and lk == [512] and slots == list(range(3 * 256, 4 * 256))
+    cu, lk, slots = a.prefill_segment_slots([1], [256], [300])
+    assert cu == [0, 44] and lk == [556] and slots == list(range(4 * 256, 4 * 256 + 44))
+    # several sequences in one call, one of them an empty segment
+    cu, lk, slots = a.prefill_segment_slots([0, 1, 0], [510, 100, 0], [515, 101, 0])
+    assert cu == [0, 5, 6, 6] and lk == [515, 357, 0]
+    assert slots == [1 * 256 + 254, 1 * 256 + 255, 2 * 256 + 0, 2 * 256 + 1, 2 * 256 + 2, 3 * 256 + 100]
+    # the whole new range as one segment is prefill_slots
+    assert a.prefill_segment_slots([0, 1], [0, 0], [515, 300]) == tuple(a.prefill_slots([0, 1]))
+    for bad in ([(-1, 5)], [(5, 4)], [(0, 301)]):
+        with pytest.raises(OA.AllocError):
+            a.prefill_segment_slots([1], [bad[0][0]], [bad[0][1]])

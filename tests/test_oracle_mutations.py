@@ -13,6 +13,7 @@ import pytest
 
 from oracle import allocator as OA
 from oracle import attention as OT
+from oracle import steps as OS
 from tests import test_oracle as P
 
 BLOCK = 256
@@ -268,7 +269,87 @@ def _copy_one_row_short(caches, src, dst, rows=None):
     return OT_copy_blocks_orig(caches, src, dst, None if rows is None else [max(0, int(r) - 1) for r in rows])
 
 
+def _decode_step_new_slot_late(wl, window=0):
+    """decode_step with the new token's row stored one slot past the one the allocator gave it."""
+    orig = OA.Allocator.append
+    OA.Allocator.append = lambda self, sid, tok: orig(self, sid, tok) + 1
+    try:
+        return OS_decode_step_orig(wl, window)
+    finally:
+        OA.Allocator.append = orig
+
+
+def _decode_step_context_short(wl, window=0):
+    """decode_step attending the history only (context not counting the token just stored)."""
+    orig = OT.decode
+    OT.decode = lambda q, kc, vc, bt, lens, *a, **k: orig(q, kc, vc, bt, [max(0, L - 1) for L in lens], *a, **k)
+    try:
+        return OS_decode_step_orig(wl, window)
+    finally:
+        OT.decode = orig
+
+
+def _decode_one_window_long(cfg, seq, L, window=0):
+    return OS_decode_one_orig(cfg, seq, L, window + 1 if window > 0 else 0)
+
+
+def _prefill_run_variant(q_from_start=False, attend_first=False, no_budget=False):
+    """prefill_run with one glue slip: queries taken from the prompt's start instead of its first
+    uncached token, a chunk attended before its rows are stored, or the chunk budget ignored."""
+    def run(wl, causal=True, prefix_cache=True):
+        cfg = wl["cfg"]
+        Hkv, D = cfg["Hkv"], cfg["D"]
+        prompts = wl["prompts"]
+        a = OA.Allocator(wl["num_blocks"], wl["free_order"], prefix_cache=prefix_cache)
+        ncached = [a.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+        n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
+        budget = 1 << 30 if no_budget else cfg["chunk"]
+        chunks, cur, tot = [], [], 0
+        for i, n in enumerate(n_new):
+            if cur and tot + n > budget:
+                chunks.append(cur)
+                cur, tot = [], 0
+            cur.append(i)
+            tot += n
+        if cur:
+            chunks.append(cur)
+        kc = np.zeros((wl["num_blocks"], Hkv, 256, D))
+        vc = np.zeros_like(kc)
+        outs = []
+        for ch in chunks:
+            cu, lk, slots = a.prefill_slots(ch)
+            kn = np.concatenate([OS._f64(prompts[i]["k"][ncached[i]:]) for i in ch])
+            vn = np.concatenate([OS._f64(prompts[i]["v"][ncached[i]:]) for i in ch])
+            qn = np.concatenate([OS._f64(prompts[i]["q"][0 if q_from_start else ncached[i]:]
+                                         [:len(prompts[i]["tokens"]) - ncached[i]]) for i in ch])
+            tables = a.block_tables(ch, max(1, -(-max(lk) // 256)))
+            if attend_first:
+                outs.append(OT.prefill(qn, kc, vc, tables, cu, lk, 1.0 / np.sqrt(D), causal))
+            kc, vc = OT.kv_store(kc, vc, kn, vn, slots)
+            if not attend_first:
+                outs.append(OT.prefill(qn, kc, vc, tables, cu, lk, 1.0 / np.sqrt(D), causal))
+        return np.concatenate(outs), ncached, chunks
+    return run
+
+
+def _segment_keys_without_prefix(self, seq_ids, starts, ends):
+    cu, lk, slots = OA_segment_orig(self, seq_ids, starts, ends)
+    return cu, [L - self.seqs[s].n_cached for L, s in zip(lk, seq_ids)], slots
+
+
+def _segment_slots_from_sequence_start(self, seq_ids, starts, ends):
+    cu, lk, _ = OA_segment_orig(self, seq_ids, starts, ends)
+    slots = []
+    for sid, a, b in zip(seq_ids, starts, ends):
+        s = self.seqs[sid]
+        slots += [s.blocks[p // BLOCK] * BLOCK + p % BLOCK for p in range(a, b)]
+    return cu, lk, slots
+
+
 OT_copy_blocks_orig = OT.copy_blocks
+OS_decode_step_orig = OS.decode_step
+OS_decode_one_orig = OS.decode_one_sequence
+OA_segment_orig = OA.Allocator.prefill_segment_slots
 OT_attend_orig = OT.attend
 OT_gather_orig = OT.gather
 OA_block_hash_orig = OA.block_hash
@@ -315,6 +396,13 @@ FORK_PINS = [
 HASH_PINS = [lambda: [P.test_fnv1a64_published_vectors(d, e) for d, e in P._golden_fnv()],
              P.test_block_hash_closed_forms]
 
+STEP_PINS = [
+    lambda: [P.test_decode_step_equals_sdpa_on_the_drawn_rows(n, o) for n, o in P.DECODE_GLUE_CASES],
+    lambda: [P.test_windowed_decode_step_equals_sdpa_on_the_last_rows(w) for w in (1, 257, 600)],
+    lambda: [P.test_prefill_run_equals_sdpa_per_prompt(o) for o in P.PREFILL_GLUE_CASES],
+    P.test_prefill_segment_slots_hand_worked,
+]
+
 MUTANTS = {
     "attend without the softmax scale": (OT, "attend", _attend_no_scale, ATTN_PINS),
     "attend without normalisation": (OT, "attend", _attend_unnormalised, ATTN_PINS),
@@ -347,6 +435,18 @@ MUTANTS = {
     "prefill window one key short": (OT, "prefill", _prefill_window_variant(shift=1), WINDOW_PINS),
     "prefill window counted from the first key": (OT, "prefill", _prefill_window_variant(from_start=True),
                                                   WINDOW_PINS),
+    "decode step stores the new token one slot late": (OS, "decode_step", _decode_step_new_slot_late, STEP_PINS),
+    "decode step context misses the new token": (OS, "decode_step", _decode_step_context_short, STEP_PINS),
+    "one-sequence decode window one key long": (OS, "decode_one_sequence", _decode_one_window_long, STEP_PINS),
+    "prefill run takes queries from the prompt start": (OS, "prefill_run", _prefill_run_variant(q_from_start=True),
+                                                        STEP_PINS),
+    "prefill run attends before storing the chunk": (OS, "prefill_run", _prefill_run_variant(attend_first=True),
+                                                     STEP_PINS),
+    "prefill run ignores the chunk budget": (OS, "prefill_run", _prefill_run_variant(no_budget=True), STEP_PINS),
+    "segment key count omits the cached prefix": (OA.Allocator, "prefill_segment_slots",
+                                                  _segment_keys_without_prefix, STEP_PINS),
+    "segment slots counted from the sequence start": (OA.Allocator, "prefill_segment_slots",
+                                                      _segment_slots_from_sequence_start, STEP_PINS),
 }
 
 
