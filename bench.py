@@ -36,14 +36,15 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+DEFAULT_STEPS, DEFAULT_WARMUP = 20, 3
 BF16_PEAK_TFLOPS = 2516.6  # dense MFMA, 256 CUs at 2.4 GHz
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--config", default="qwen3_decode")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--max-splits", type=int, default=0)
@@ -140,6 +141,12 @@ def stored_traffic(kernel):
     return None
 
 # ------------------------------------------------------------------------------------ decode
+def decode_max_context(lens, warmup, steps):
+    """The context capacity a decode line plans for: its warm-up, wall-clock and event passes each
+    append one token per step."""
+    return max(lens) + warmup + 2 * steps
+
+
 def bench_decode(args, cfg):
     import torch
     import workloads as W
@@ -173,7 +180,7 @@ def bench_decode(args, cfg):
                       [p[1][:-1] for p in parts],
                       [None if p[2] is None else p[2][:-1] for p in parts],
                       [None if p[3] is None else p[3][:-1] for p in parts])
-    max_ctx = max(lens) + nsteps
+    max_ctx = decode_max_context(lens, args.warmup, args.steps)
     if (args.graph or args.fused) and args.window:
         raise SystemExit("--graph and --fused have no sliding window")
     batch = R.DecodeBatch(kv, Hq, ids, max_ctx, args.max_splits, window=args.window)
@@ -369,8 +376,8 @@ def bench_prefill(args, cfg):
         mb = max(1, -(-int(lens.max()) // 256))
         tab = np.ascontiguousarray(tab[:, :mb])
         # the chunk's work items, heaviest first in CU-balanced rounds (pkv_prefill_work_order)
-        items = prefill_work_order(desc_of(kv.k_cache), Hq, cu, lk, True, args.window)
-        metas.append((cu, lk, slots, tab, mb, items))
+        items, tile_rows = prefill_work_order(desc_of(kv.k_cache), Hq, cu, lk, True, args.window)
+        metas.append((cu, lk, slots, tab, mb, (items, tile_rows)))
     host_s = time.perf_counter() - t0
     # device-resident inputs of every chunk
     dchunks, flops = [], 0
@@ -380,7 +387,7 @@ def bench_prefill(args, cfg):
         q, k, v = dv("q"), dv("k"), dv("v")
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         dchunks.append(dict(q=q, k=k, v=v, cu=to(cu), lk=to(lk), slots=to(slots), tab=to(tab).view(len(ch), mb),
-                            items=to(items), max_q=int(np.diff(cu).max()), max_k=int(lk.max()),
+                            items=to(items[0]), tile_rows=items[1], max_q=int(np.diff(cu).max()), max_k=int(lk.max()),
                             out=torch.empty_like(q)))
         for b in range(len(ch)):
             nq, L = int(cu[b + 1] - cu[b]), int(lk[b])
@@ -399,7 +406,8 @@ def bench_prefill(args, cfg):
             if timed is not None:
                 ev[timed][c][0].record(stream)
             paged_attn_prefill_ordered(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache,
-                                       d["tab"], scale, d["items"], True, args.window, out=d["out"])
+                                       d["tab"], scale, d["items"], d["tile_rows"], True, args.window,
+                                       out=d["out"])
             if timed is not None:
                 ev[timed][c][1].record(stream)
 

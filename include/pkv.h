@@ -316,7 +316,9 @@ int pkv_decode_launch_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
  * seq_order: NULL, or device int32[B], a permutation of 0..B-1 giving the order in which the
  * sequences' workgroups are launched (pkv_decode_launch_order computes a good one); the output
  * stays indexed by sequence.
- * max_context_len: host upper bound of context_lens (sizes the split plan).
+ * max_context_len: host upper bound of context_lens (sizes the split plan).  A larger entry is
+ * undefined (its tail would fall outside the plan); with device-data checks on it is recorded as
+ * error 3 and that sequence's output is left unwritten.
  * out: device [B][Hq][head_dim] in the dtype of q.  workspace: device, at least
  * pkv_decode_workspace_bytes(...) bytes (may be NULL when that is 0). */
 int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
@@ -404,8 +406,9 @@ int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const void* q, int
  *   - cut into rounds of (CUs of the current device) / num_kv_heads items;
  *   - every odd round reversed, so the heavy items of one round share CUs with the light items of
  *     the next.
- * Ties keep sequence and tile order.  Query tiles hold pkv_prefill_tile_rows tokens, which
- * depends on total_q = cu_seqlens_q[B], B, the group size and the device.
+ * Ties keep sequence and tile order.  Query tiles hold *tile_rows tokens (tile_rows may be
+ * NULL), the pkv_prefill_tile_rows of total_q = cu_seqlens_q[B], B, the group size and the
+ * device.
  * Errors:
  *   - more items than capacity: PKV_ERR_SMALL_BUFFER;
  *   - B above 32767: PKV_ERR_INVALID;
@@ -413,24 +416,27 @@ int pkv_paged_attn_prefill_window(const pkv_cache_desc* desc, const void* q, int
  *     PKV_ERR_INVALID.
  *
  * pkv_paged_attn_prefill_ordered: pkv_paged_attn_prefill / _window (window = 0: every key) with
- * work_items (device int32[n_items]).  work_items must hold every item of the call exactly once,
- * as pkv_prefill_work_order gives them for the same cu_seqlens_q, seqlens_k, shapes and device.
- * Outputs are bitwise those of the unordered call.  n_items = 0 does nothing.  The items are
+ * work_items (device int32[n_items]) cut into query tiles of tile_rows tokens.  work_items and
+ * tile_rows must be what pkv_prefill_work_order gave for the same cu_seqlens_q, seqlens_k,
+ * shapes and device, whatever total_q the call passes (it may exceed cu_seqlens_q[B]); a
+ * tile_rows that is not one of this kernel's tiles for the group size is PKV_ERR_INVALID.
+ * Outputs are bitwise those of the unordered call with the same tile.  n_items = 0 does nothing.  The items are
  * device data: with device-data checks on, an item whose sequence or tile does not exist is
  * recorded as error 5 (where = its index, value = the item).
  *
  * pkv_prefill_tile_rows: query tokens per work item of a launch of this shape. */
 int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
                            const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
-                           int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items);
+                           int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items,
+                           int32_t* tile_rows);
 int pkv_paged_attn_prefill_ordered(const pkv_cache_desc* desc, const void* q, int32_t Hq,
                                    const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
                                    int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                    const void* k_cache, const void* v_cache,
                                    const int32_t* block_tables, int32_t max_blocks,
                                    float softmax_scale, int32_t causal, int32_t window,
-                                   const int32_t* work_items, int32_t n_items, void* out,
-                                   void* stream);
+                                   const int32_t* work_items, int32_t n_items, int32_t tile_rows,
+                                   void* out, void* stream);
 int pkv_prefill_tile_rows(const pkv_cache_desc* desc, int32_t Hq, int32_t B, int32_t total_q,
                           int32_t* tile_rows);
 

@@ -82,9 +82,9 @@ SIGNATURES = {
     "pkv_paged_attn_prefill_window": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                              _i32, _f32, _i32, _vp, _vp]),
     "pkv_paged_attn_prefill_ordered": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
-                                              _i32, _f32, _i32, _i32, _vp, _i32, _vp, _vp]),
+                                              _i32, _f32, _i32, _i32, _vp, _i32, _i32, _vp, _vp]),
     "pkv_prefill_tile_rows": (_i32, [_pdesc, _i32, _i32, _i32, _p32]),
-    "pkv_prefill_work_order": (_i32, [_pdesc, _i32, _i32, _p32, _p32, _i32, _i32, _p32, _i32, _p32]),
+    "pkv_prefill_work_order": (_i32, [_pdesc, _i32, _i32, _p32, _p32, _i32, _i32, _p32, _i32, _p32, _p32]),
 }
 
 _lib = None
@@ -443,7 +443,8 @@ def prefill_tile_rows(desc, Hq, B, total_q):
 
 
 def prefill_work_order(desc, Hq, cu_seqlens_q, seqlens_k, causal=True, window=0):
-    """pkv_prefill_work_order: the work items of a prefill call (host int32 array)."""
+    """pkv_prefill_work_order: the work items of a prefill call (host int32 array) and the query
+    tile (tokens per item) they were cut with, which the ordered call must be given."""
     import numpy as np
     cu, pcu = _host_i32(cu_seqlens_q)
     lk, plk = _host_i32(seqlens_k)
@@ -452,16 +453,19 @@ def prefill_work_order(desc, Hq, cu_seqlens_q, seqlens_k, causal=True, window=0)
         raise ValueError("cu_seqlens_q must have B + 1 entries")
     cap = int(cu[-1]) + B if B else 0  # at least one query token per item
     items = np.empty(max(cap, 1), dtype=np.int32)
-    n = ctypes.c_int32()
+    n, rows = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().pkv_prefill_work_order(ctypes.byref(desc), int(Hq), B, pcu, plk, int(bool(causal)), int(window),
-                                        items.ctypes.data_as(_p32), cap, ctypes.byref(n)), "pkv_prefill_work_order")
-    return items[:n.value]
+                                        items.ctypes.data_as(_p32), cap, ctypes.byref(n), ctypes.byref(rows)),
+           "pkv_prefill_work_order")
+    return items[:n.value], rows.value
 
 
 def paged_attn_prefill_ordered(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache,
-                               block_tables, softmax_scale, work_items, causal=True, window=0, out=None, stream=None):
+                               block_tables, softmax_scale, work_items, tile_rows, causal=True, window=0, out=None,
+                               stream=None):
     """Varlen prefill whose work items run in the order of ``work_items`` (device int32, each
-    ``(sequence << 16) | query tile``, every item of the launch exactly once)."""
+    ``(sequence << 16) | query tile``, every item of the launch exactly once), cut into query tiles
+    of ``tile_rows`` tokens (both as :func:`prefill_work_order` returns them)."""
     desc = desc_of(k_cache)
     total_q, Hq, _ = q.shape
     B = int(seqlens_k.shape[0])
@@ -471,7 +475,7 @@ def paged_attn_prefill_ordered(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seq
         ctypes.byref(desc), _ptr(q), int(Hq), _ptr(cu_seqlens_q), _ptr(seqlens_k), B, int(total_q),
         int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), float(softmax_scale), int(bool(causal)), int(window), _ptr(work_items),
-        int(work_items.shape[0]), _ptr(out), _stream(stream)), "pkv_paged_attn_prefill_ordered")
+        int(work_items.shape[0]), int(tile_rows), _ptr(out), _stream(stream)), "pkv_paged_attn_prefill_ordered")
     return out
 
 

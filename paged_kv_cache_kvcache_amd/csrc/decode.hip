@@ -240,6 +240,7 @@ struct DecodeArgs {
     float* k_scale_store;
     float* v_scale_store;
     int32_t max_blocks;
+    int32_t max_context_len;  // the host's bound on every context length (the split plan covers it)
     int32_t num_kv_heads;
     int32_t num_q_heads;
     int32_t splits;
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         return;
     }
     const int ctx = a.context_lens[b];
-    if (CHECK && (ctx < 0 || ctx > int64_t(a.max_blocks) * pkv::kBlock)) {
+    if (CHECK && (ctx < 0 || ctx > a.max_context_len)) {
         if (threadIdx.x == 0 && s == 0 && g == 0) record_error(pkv::kErrLength, b, ctx);
         return;
     }
@@ -304,7 +305,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const int blk0 = lo / pkv::kBlock + s * a.blocks_per_split;
     const int blk1 = min(nblk, blk0 + a.blocks_per_split);
     if (a.splits > 1 && blk0 >= blk1) return;  // empty split: the reduce kernel skips it
-    if (CHECK && !decode_split_inputs_ok(a, b, blk0, blk1, ctx)) return;
+    if (CHECK && !decode_split_inputs_ok(a, b, blk0, blk1, ctx)) {
+        // a rejected split's partial state is marked (denominator -1), so the reduce leaves this
+        // sequence's output unwritten instead of merging whatever the workspace held
+        if (a.splits > 1 && threadIdx.x < G)
+            a.ws_ml[2 * ((size_t(b) * a.num_q_heads + g * G + threadIdx.x) * a.splits + s) + 1] = -1.f;
+        return;
+    }
 
     // ---- the new token of this sequence (position ctx - 1), stored by the workgroup whose split
     // holds its block before any wavefront reads that block; no other workgroup reads it
@@ -508,14 +515,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
 // --------------------------------------------------------------------------- split reduce
 // out[b][h] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the non-empty splits.
-template <int D, bool F32_OUT>
+// CHECK: a sequence whose length the split kernel rejected, or one of whose splits it rejected,
+// keeps its output unwritten (every test below is uniform in the workgroup).
+template <int D, bool F32_OUT, bool CHECK>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int ctx = a.context_lens[b];
+    if (CHECK && (ctx < 0 || ctx > a.max_context_len)) return;
     const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
     const int lo_blk = (a.window > 0 ? max(0, ctx - a.window) : 0) / pkv::kBlock;
     const int active = min(a.splits, (nblk - lo_blk + a.blocks_per_split - 1) / a.blocks_per_split);
     const size_t base = (size_t(b) * a.num_q_heads + h) * a.splits;
+    if constexpr (CHECK) {
+        for (int s = 0; s < active; ++s)
+            if (a.ws_ml[2 * (base + s) + 1] < 0.f) return;
+    }
     float M = kNegInf;
     for (int s = 0; s < active; ++s) M = fmaxf(M, a.ws_ml[2 * (base + s)]);
     float num = 0.f, den = 0.f;
@@ -572,8 +586,13 @@ hipError_t launch(const DecodeArgs& a, int B, hipStream_t st) {
     const dim3 grid(a.splits, a.num_kv_heads, B);
     if (a.check) hipLaunchKernelGGL((decode_split_kernel<DT, D, G, true>), grid, dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL((decode_split_kernel<DT, D, G, false>), grid, dim3(kThreads), 0, st, a);
-    if (a.splits > 1)
-        hipLaunchKernelGGL((decode_reduce_kernel<D, DT == PKV_F32>), dim3(a.num_q_heads, B), dim3(D), 0, st, a);
+    if (a.splits > 1) {
+        if (a.check)
+            hipLaunchKernelGGL((decode_reduce_kernel<D, DT == PKV_F32, true>), dim3(a.num_q_heads, B), dim3(D), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_reduce_kernel<D, DT == PKV_F32, false>), dim3(a.num_q_heads, B), dim3(D), 0, st,
+                               a);
+    }
     return hipGetLastError();
 }
 
@@ -766,6 +785,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
     a.seq_order = seq_order;
     a.out = out;
     a.max_blocks = max_blocks;
+    a.max_context_len = max_context_len;
     a.num_kv_heads = Hkv;
     a.num_q_heads = Hq;
     a.scale_log2 = softmax_scale * kLog2e;

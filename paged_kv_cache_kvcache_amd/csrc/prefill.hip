@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 #include <cmath>
 #include <type_traits>
@@ -493,8 +494,8 @@ int choose_nw(long total_q, int B, int Hkv, int G, int num_cus) {
 }
 
 template <int D, int G>
-hipError_t launch(const PrefillArgs& a, int total_q, int num_cus, hipStream_t st) {
-    const int nw = choose_nw(total_q, a.B, a.num_kv_heads, G, num_cus);
+hipError_t launch(const PrefillArgs& a, int total_q, int num_cus, int nw_given, hipStream_t st) {
+    const int nw = nw_given > 0 ? nw_given : choose_nw(total_q, a.B, a.num_kv_heads, G, num_cus);
     const int QT = nw * kWaveRows / G;
     const long items = a.items != nullptr ? long(a.n_items) * a.num_kv_heads
                                           : ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
@@ -503,27 +504,33 @@ hipError_t launch(const PrefillArgs& a, int total_q, int num_cus, hipStream_t st
 }
 
 template <int D>
-hipError_t launch_g(const PrefillArgs& a, int total_q, int G, int num_cus, hipStream_t st) {
+hipError_t launch_g(const PrefillArgs& a, int total_q, int G, int num_cus, int nw, hipStream_t st) {
     switch (G) {
-        case 1: return launch<D, 1>(a, total_q, num_cus, st);
-        case 2: return launch<D, 2>(a, total_q, num_cus, st);
-        case 4: return launch<D, 4>(a, total_q, num_cus, st);
-        case 8: return launch<D, 8>(a, total_q, num_cus, st);
+        case 1: return launch<D, 1>(a, total_q, num_cus, nw, st);
+        case 2: return launch<D, 2>(a, total_q, num_cus, nw, st);
+        case 4: return launch<D, 4>(a, total_q, num_cus, nw, st);
+        case 8: return launch<D, 8>(a, total_q, num_cus, nw, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-// compute units of the current device (queried once per device)
+// compute units of the current device (queried once per device; callers may be on any thread)
 int current_num_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
     }
-    return cus[dev];
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 }  // namespace
@@ -534,7 +541,7 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
                  const int32_t* seqlens_k, int32_t B, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
                  const void* k_cache, const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
                  float softmax_scale, int32_t causal, int32_t window, void* out, void* stream,
-                 const int32_t* items = nullptr, int32_t n_items = 0) {
+                 const int32_t* items = nullptr, int32_t n_items = 0, int32_t tile_rows = 0) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     PKV_REQUIRE(desc->kv_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED, "prefill supports bf16 caches only");
@@ -555,6 +562,14 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
                 "softmax_scale must be finite and positive");
     PKV_REQUIRE(window >= 0 && (window == 0 || causal), PKV_ERR_INVALID,
                 "window = %d: a sliding window needs causal attention and window >= 0", window);
+    // a work list fixes the query tile: the launch must cut tiles exactly as the list did
+    int nw = 0;
+    if (items != nullptr) {
+        nw = tile_rows > 0 && tile_rows * G % kWaveRows == 0 ? tile_rows * G / kWaveRows : 0;
+        PKV_REQUIRE(nw == 4 || nw == 8, PKV_ERR_INVALID,
+                    "tile_rows %d is not a query tile of this kernel for group size %d (%d or %d)", tile_rows, G,
+                    4 * kWaveRows / G, 8 * kWaveRows / G);
+    }
     if (B == 0 || total_q == 0) return PKV_OK;
     PKV_REQUIRE(q && cu_seqlens_q && seqlens_k && k_cache && v_cache && block_tables && out, PKV_ERR_INVALID,
                 "NULL pointer");
@@ -582,7 +597,7 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
     a.n_items = n_items;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int cus = current_num_cus();
-    const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, st) : launch_g<128>(a, total_q, G, cus, st);
+    const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, nw, st) : launch_g<128>(a, total_q, G, cus, nw, st);
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return PKV_OK;
 }
@@ -615,19 +630,20 @@ extern "C" int pkv_paged_attn_prefill_ordered(const pkv_cache_desc* desc, const 
                                               const void* k_cache, const void* v_cache,
                                               const int32_t* block_tables, int32_t max_blocks,
                                               float softmax_scale, int32_t causal, int32_t window,
-                                              const int32_t* work_items, int32_t n_items, void* out,
-                                              void* stream) {
+                                              const int32_t* work_items, int32_t n_items, int32_t tile_rows,
+                                              void* out, void* stream) {
     PKV_REQUIRE(n_items >= 0, PKV_ERR_INVALID, "n_items = %d", n_items);
     PKV_REQUIRE(work_items != nullptr || n_items == 0, PKV_ERR_INVALID, "NULL work_items");
     if (n_items == 0) return PKV_OK;
     return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
                         v_cache, block_tables, max_blocks, softmax_scale, causal, window, out, stream, work_items,
-                        n_items);
+                        n_items, tile_rows);
 }
 
 extern "C" int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
                                       const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
-                                      int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items) {
+                                      int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items,
+                                      int32_t* tile_rows) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     PKV_REQUIRE(n_items != nullptr, PKV_ERR_INVALID, "NULL n_items");
@@ -649,6 +665,7 @@ extern "C" int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, in
     }
     const int cus = current_num_cus();
     const int QT = choose_nw(cu_seqlens_q[B], B, desc->num_kv_heads, G, cus) * kWaveRows / G;
+    if (tile_rows != nullptr) *tile_rows = QT;
     // the items with their key tiles (+1 for a workgroup's fixed cost): heaviest first, ties in
     // sequence and tile order
     std::vector<uint64_t> key;

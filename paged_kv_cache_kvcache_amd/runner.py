@@ -11,9 +11,9 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_store_attend, decode_workspace_bytes,
-               desc_of, kv_store, kv_store_quant, lib, paged_attn_decode, paged_attn_prefill_ordered,
-               prefill_work_order)
+from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_plan, decode_store_attend,
+               decode_workspace_bytes, desc_of, kv_store, kv_store_quant, lib, paged_attn_decode,
+               paged_attn_prefill_ordered, prefill_work_order)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 
@@ -106,6 +106,9 @@ class DecodeBatch:
                             pin[2 * self.B:].ctypes.data_as(p32))
         self._cow = self._meta[nmeta:]
         self.n_copies = 0
+        # the split plan the library uses: a window of W keys spans at most ceil((W + 255) / 256) blocks
+        span = min(self.max_context_len, self.window + BLOCK - 1) if self.window else self.max_context_len
+        self.splits, self.blocks_per_split = decode_plan(self.B, kv.Hkv, span, max_splits)
         nbytes = decode_workspace_bytes(self.B, self.Hq, kv.D, kv.Hkv, self.max_context_len, max_splits)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
 
@@ -309,7 +312,7 @@ def _attend_chunk(kv, q_new, k_new, v_new, cu, lk, slots, tab, softmax_scale, ca
     new rows, and attend in that order."""
     dev = kv.device
     B, n_new, mb = len(lk), len(slots), tab.shape[1]
-    items = prefill_work_order(desc_of(kv.k_cache), q_new.shape[1], cu, lk, causal)
+    items, tile_rows = prefill_work_order(desc_of(kv.k_cache), q_new.shape[1], cu, lk, causal)
     meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel(), items]).astype(np.int32), dev)
     d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
     d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
@@ -318,7 +321,7 @@ def _attend_chunk(kv, q_new, k_new, v_new, cu, lk, slots, tab, softmax_scale, ca
     kv.store(d_slots, k_new, v_new)
     n_q = np.diff(cu)
     return paged_attn_prefill_ordered(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache,
-                                      d_tab, softmax_scale, d_items, causal, out=out)
+                                      d_tab, softmax_scale, d_items, tile_rows, causal, out=out)
 
 
 def prefill_segments(kv, segments, q_new, k_new, v_new, softmax_scale, causal=True, out=None):

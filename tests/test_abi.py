@@ -258,7 +258,8 @@ def test_prefill_work_order(causal, window):
     lk = (nq + rng.integers(0, 600, size=13)).astype(np.int32)
     qt = P.prefill_tile_rows(d, 16, 13, int(cu[-1]))
     assert qt in (64, 128)
-    items = P.prefill_work_order(d, 16, cu, lk, causal, window)
+    items, rows = P.prefill_work_order(d, 16, cu, lk, causal, window)
+    assert rows == qt
     # every (sequence, tile) of the call exactly once
     assert sorted(items.tolist()) == sorted((b << 16) | t for b in range(13) for t in range(-(-int(nq[b]) // qt)))
     work = [_item_work(int(i), cu, lk, qt, causal, window) for i in items]
@@ -274,23 +275,27 @@ def test_prefill_work_order(causal, window):
 
 def test_prefill_work_order_errors():
     d = _desc(num_kv_heads=2, head_dim=64, kv_dtype=P.BF16)
-    assert len(P.prefill_work_order(d, 4, [0], [])) == 0
+    assert len(P.prefill_work_order(d, 4, [0], [])[0]) == 0
     with pytest.raises(RuntimeError):
         P.prefill_work_order(d, 4, [0, 10, 5], [10, 10])  # decreasing cu_seqlens_q
     with pytest.raises(RuntimeError):
         P.prefill_work_order(d, 4, [0, 10], [9])  # causal: fewer keys than new tokens
-    assert len(P.prefill_work_order(d, 4, [0, 10], [9], causal=False)) == 1
+    assert len(P.prefill_work_order(d, 4, [0, 10], [9], causal=False)[0]) == 1
     with pytest.raises(RuntimeError):
         P.prefill_work_order(d, 3, [0, 10], [10])  # Hq not a multiple of Hkv
     cu, lk = np.array([0, 200], np.int32), np.array([200], np.int32)
     out, n = np.empty(2, np.int32), ctypes.c_int32()
     p32 = ctypes.POINTER(ctypes.c_int32)
     rc = P.lib().pkv_prefill_work_order(ctypes.byref(d), 4, 1, cu.ctypes.data_as(p32), lk.ctypes.data_as(p32), 1, 0,
-                                        out.ctypes.data_as(p32), 2, ctypes.byref(n))
+                                        out.ctypes.data_as(p32), 2, ctypes.byref(n), None)
     assert rc == P.ERR_SMALL_BUFFER and n.value == 0  # 200 tokens in tiles of 64: four items
     rc = P.lib().pkv_paged_attn_prefill_ordered(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE,
-                                                1, 0.1, 1, 0, None, 1, FAKE, None)
+                                                1, 0.1, 1, 0, None, 1, 64, FAKE, None)
     assert rc == P.ERR_INVALID  # items missing
+    for bad in (0, 48, 96, 512):  # G = 2: tiles of 64 or 128 tokens only
+        rc = P.lib().pkv_paged_attn_prefill_ordered(ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 1, 1, 1, FAKE, FAKE,
+                                                    FAKE, 1, 0.1, 1, 0, FAKE, 1, bad, FAKE, None)
+        assert rc == P.ERR_INVALID, bad
 
 
 def test_prefill_rejects_bad_descriptor():

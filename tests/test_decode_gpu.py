@@ -86,6 +86,14 @@ SMALL = {
     "qwen3_decode": dict(B=6),
     "long_decode": dict(B=3),
     "int8_decode": dict(B=3),
+    # every query-group size and head_dim the C ABI accepts, in every cache dtype
+    "g8_bf16": dict(base="qwen3_decode", B=4, Hq=64, Hkv=8),
+    "g8_i8": dict(base="int8_decode", B=3, ctx=(100, 1500), Hq=64, Hkv=8),
+    "g8_f32": dict(base="tiny_fp32", Hq=16, Hkv=2),
+    "g1_f32": dict(base="tiny_fp32", Hq=2, Hkv=2),
+    "bf16_d64": dict(base="qwen3_decode", B=5, D=64),
+    "g8_bf16_d64": dict(base="qwen3_decode", B=3, D=64, Hq=32, Hkv=4),
+    "i8_d64": dict(base="int8_decode", B=3, ctx=(100, 1500), D=64, Hq=8, Hkv=4),
 }
 
 
@@ -175,42 +183,46 @@ def test_decode_zero_context_gives_zero(gpu):
 
 # --------------------------------------------------------------------- full-size workloads
 @pytest.mark.parametrize("name", ["qwen3_decode", "long_decode", "int8_decode"])
-def test_decode_full_size_sampled(gpu, name):
-    """Full-size workload in the launch configuration the bench times (automatic split plan,
-    max_context_len covering its 23 default steps); eight sampled sequences are checked against
-    the oracle one by one, and their stored cache rows bit for bit through the oracle's tables."""
+def test_decode_full_size_every_sequence(gpu, name):
+    """Full-size workload on the path the bench times: kv_store then pkv_paged_attn_decode (not the
+    fused launch), the automatic split plan for the bench's max_context_len, and its launch order.
+    Every sequence and every head is checked element by element against the oracle's attention
+    over that sequence's rows, and every stored cache row bit for bit through the oracle's own
+    block manager."""
+    import bench
     from oracle import allocator as OA
     from oracle import steps as OS
     cfg = W.config(name)
     wl = W.decode_workload(cfg, 0)
     say(f"full-size {name}: B={len(wl['lens'])} sum ctx={sum(wl['lens'])}")
-    out, kv, batch = gpu_decode(wl, gpu, max_context_len=max(wl["lens"]) + 23)
+    max_ctx = bench.decode_max_context(wl["lens"], bench.DEFAULT_WARMUP, bench.DEFAULT_STEPS)
+    out, kv, batch = gpu_decode(wl, gpu, max_context_len=max_ctx, fused=False)
+    say(f"  plan: splits={batch.splits} blocks/split={batch.blocks_per_split}")
     got = host_out(out)
-    sample = np.random.default_rng(7).choice(len(wl["lens"]), size=8, replace=False)
-    ref = np.stack([OS.decode_one_sequence(cfg, wl["seqs"][b], wl["lens"][b]) for b in sample])
-    check_tol(got[sample], ref, cfg["dtype"], f"{name} full size, 8 sampled sequences")
-    # the cache rows of the sampled sequences, located through the oracle's own block manager
+    ref = np.stack([OS.decode_one_sequence(cfg, s, L) for s, L in zip(wl["seqs"], wl["lens"])])
+    check_tol(got, ref, cfg["dtype"], f"{name} full size, all {len(wl['lens'])} sequences")
+    # every sequence's cache rows, located through the oracle's own block manager
     a = OA.Allocator(wl["num_blocks"], wl["free_order"])
     for b, s in enumerate(wl["seqs"]):
         a.add_seq(b, s["tokens"][:-1])
     for b, s in enumerate(wl["seqs"]):
         a.append(b, int(s["tokens"][-1]))
-    key = "kq" if cfg["dtype"] == "i8" else "k"
-    vkey = "vq" if cfg["dtype"] == "i8" else "v"
-    kc = kv.k_cache.view(torch.int8 if cfg["dtype"] == "i8" else torch.int16)
-    vc = kv.v_cache.view(torch.int8 if cfg["dtype"] == "i8" else torch.int16)
-    for b in sample[:3]:
-        L = wl["lens"][b]
-        row = a.block_tables([b], -(-L // 256))[0]
-        idx = torch.tensor([row[j // 256] for j in range(L)], device=gpu)
-        off = torch.tensor([j % 256 for j in range(L)], device=gpu)
-        gk = kc[idx, :, off].cpu().numpy()
-        gv = vc[idx, :, off].cpu().numpy()
-        ek, ev = wl["seqs"][b][key], wl["seqs"][b][vkey]
-        assert np.array_equal(gk.view(ek.dtype), ek) and np.array_equal(gv.view(ev.dtype), ev)
-        if cfg["dtype"] == "i8":
-            ks = kv.k_scale[idx[::256].long()].cpu().numpy()
-            assert np.array_equal(ks, wl["seqs"][b]["k_blk_scale"])
+    i8 = cfg["dtype"] == "i8"
+    view = torch.int8 if i8 else torch.int16
+    kc, vc = kv.k_cache.view(view), kv.v_cache.view(view)
+    mb = max(-(-L // 256) for L in wl["lens"])
+    tables = np.array(a.block_tables(range(len(wl["lens"])), mb), dtype=np.int64)
+    for b, (s, L) in enumerate(zip(wl["seqs"], wl["lens"])):
+        j = np.arange(L)
+        idx = torch.from_numpy(tables[b][j // 256]).to(gpu)
+        off = torch.from_numpy(j % 256).to(gpu)
+        gk, gv = kc[idx, :, off].cpu().numpy(), vc[idx, :, off].cpu().numpy()
+        ek, ev = (s["kq"], s["vq"]) if i8 else (s["k"], s["v"])
+        assert np.array_equal(gk.view(ek.dtype), ek) and np.array_equal(gv.view(ev.dtype), ev), b
+        if i8:
+            blocks = torch.from_numpy(tables[b][:-(-L // 256)]).to(gpu)
+            assert np.array_equal(kv.k_scale[blocks].cpu().numpy(), s["k_blk_scale"]), b
+            assert np.array_equal(kv.v_scale[blocks].cpu().numpy(), s["v_blk_scale"]), b
 
 
 def test_launch_order_from_the_device(gpu):

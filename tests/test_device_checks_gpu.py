@@ -100,7 +100,7 @@ def test_block_copy_rejects_bad_pairs(checks):
     _expect(ROWS, 0, 300)
 
 
-def _decode(dev, tables, lens, order=None, B=2, max_ctx=512, rows=3):
+def _decode(dev, tables, lens, order=None, B=2, max_ctx=512, rows=3, max_splits=0):
     """Decode over views: q/out/lens/order/tables one row or entry larger than the kernel is told."""
     _, (kc, vc) = _caches(dev)
     kc.normal_()
@@ -111,20 +111,32 @@ def _decode(dev, tables, lens, order=None, B=2, max_ctx=512, rows=3):
     lens_full = _i32(lens, dev)
     order_t = None if order is None else _i32(order, dev)[:B]
     P.paged_attn_decode(q_full[:B], kc, vc, tab_full[:B], lens_full[:B], max_ctx, 0.088, out=out_full[:B],
-                        seq_order=order_t)
+                        seq_order=order_t, max_splits=max_splits)
     return out_full
 
 
-def test_decode_rejects_a_block_id_outside_the_pool(checks):
-    out = _decode(checks, [[0, NB], [2, 3], [1, 1]], [300, 400, 1])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_decode_rejects_a_block_id_outside_the_pool(checks, splits):
+    """With one split the rejected workgroup writes nothing; with two, its split is marked and the
+    reduce leaves the sequence's output unwritten rather than merge a stale partial."""
+    out = _decode(checks, [[0, NB], [2, 3], [1, 1]], [300, 400, 1], max_splits=splits)
     _expect(BLOCK_ID, 0, NB)
     assert out[1].abs().sum() > 0  # the valid sequence was attended
+    assert not out[0].any()
 
 
 def test_decode_rejects_a_length_the_table_cannot_hold(checks):
     out = _decode(checks, [[0, 1], [2, 3], [4, 5]], [513, 200, 1])
     _expect(LENGTH, 0, 513)
-    assert out[1].abs().sum() > 0
+    assert out[1].abs().sum() > 0 and not out[0].any()
+
+
+def test_decode_rejects_a_length_above_max_context_len(checks):
+    """The table could hold it, but the split plan covers only max_context_len keys: without the
+    check the tail of the context would be silently left out."""
+    out = _decode(checks, [[0, 1], [2, 3], [4, 5]], [301, 200, 1], max_ctx=300)
+    _expect(LENGTH, 0, 301)
+    assert out[1].abs().sum() > 0 and not out[0].any()
 
 
 def test_decode_rejects_a_launch_order_entry_outside_the_batch(checks):
@@ -184,6 +196,6 @@ def test_ordered_prefill_rejects_an_item_outside_the_call(checks):
     # items of sequence 0 (tile 0) and sequence 1 (tile 0), then a sequence that does not exist
     items = _i32([0, 1 << 16, 2 << 16], dev)
     P.paged_attn_prefill_ordered(q, _i32([0, 64, 96], dev), _i32([64, 32], dev), 64, 64, kc, vc,
-                                 _i32([[0, 1], [2, 3]], dev), 0.088, items, True, out=out)
+                                 _i32([[0, 1], [2, 3]], dev), 0.088, items, 64, True, out=out)
     _expect(RUN, 2, 2 << 16)
     assert out[:64].abs().sum() > 0 and out[64:].abs().sum() > 0

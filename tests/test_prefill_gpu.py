@@ -123,13 +123,55 @@ def test_work_order_gives_bitwise_the_built_in_order(name, over, causal, window)
         cu, lk, slots = kv.alloc.prefill_slots(ch, int(q.shape[0]))
         tab, _ = kv.alloc.block_tables(ch, max(1, -(-int(lk.max()) // 256)))
         kv.store(to(slots), k, v)
-        items = P.prefill_work_order(P.desc_of(kv.k_cache), Hq, cu, lk, causal, window)
-        qt = P.prefill_tile_rows(P.desc_of(kv.k_cache), Hq, len(ch), int(cu[-1]))
+        items, qt = P.prefill_work_order(P.desc_of(kv.k_cache), Hq, cu, lk, causal, window)
+        assert qt == P.prefill_tile_rows(P.desc_of(kv.k_cache), Hq, len(ch), int(cu[-1]))
         assert len(items) == sum(-(-int(n) // qt) for n in np.diff(cu))
         args = (q, to(cu), to(lk), int(np.diff(cu).max()), int(lk.max()), kv.k_cache, kv.v_cache, to(tab),
                 1.0 / math.sqrt(D))
         ref = P.paged_attn_prefill(*args, causal, window=window)
-        got = P.paged_attn_prefill_ordered(*args, to(items), causal, window)
+        got = P.paged_attn_prefill_ordered(*args, to(items), qt, causal, window)
         torch.cuda.synchronize()
         say(f"  chunk of {len(ch)} prompts: {len(items)} items of {qt} tokens")
         assert torch.equal(ref, got)
+
+
+def test_ordered_prefill_with_padded_q_keeps_the_list_tile():
+    """A caller may pass q with more rows than cu_seqlens_q[B] (padding).  The launch then still
+    cuts query tiles as the work list did, even where the padded total_q alone would choose the
+    other workgroup shape: outputs equal the unpadded call bit for bit and the padding rows of out
+    stay untouched."""
+    import math
+    import torch
+    import paged_kv_cache_kvcache_amd as P
+    from paged_kv_cache_kvcache_amd import runner as R
+    from tests.gpu_cases import dev_rows
+    cfg = W.config("prefill_prefix", B=8, group=4)  # small enough for four-wavefront tiles
+    wl = W.prefill_workload(cfg, 1)
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    prompts = wl["prompts"]
+    kv = R.PagedKV(wl["num_blocks"], Hkv, D, P.BF16, wl["free_order"], device="cuda", fill=0)
+    ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+    ch = list(range(len(prompts)))
+    rows = lambda key: dev_rows(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), "cuda")
+    q, k, v = rows("q"), rows("k"), rows("v")
+    n = int(q.shape[0])
+    cu, lk, slots = kv.alloc.prefill_slots(ch, n)
+    tab, _ = kv.alloc.block_tables(ch, max(1, -(-int(lk.max()) // 256)))
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    kv.store(to(slots), k, v)
+    d = P.desc_of(kv.k_cache)
+    items, qt = P.prefill_work_order(d, Hq, cu, lk, True)
+    assert qt == 4 * 32 // (Hq // Hkv)
+    # pad until the padded size alone would pick the other tile
+    pad = next(p for p in range(0, 64 * n, 64) if P.prefill_tile_rows(d, Hq, len(ch), n + p) != qt)
+    say(f"  {n} tokens in tiles of {qt}; {pad} rows of padding would choose "
+        f"{P.prefill_tile_rows(d, Hq, len(ch), n + pad)}")
+    qp = torch.cat([q, torch.zeros((pad, Hq, D), dtype=q.dtype, device=q.device)])
+    out = torch.full_like(qp, 3.0)
+    args = (to(cu), to(lk), int(np.diff(cu).max()), int(lk.max()), kv.k_cache, kv.v_cache, to(tab),
+            1.0 / math.sqrt(D), to(items), qt)
+    ref = P.paged_attn_prefill_ordered(q, *args)
+    P.paged_attn_prefill_ordered(qp, *args, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:n], ref)
+    assert bool((out[n:] == 3.0).all())
