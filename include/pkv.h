@@ -52,6 +52,8 @@ extern "C" {
 #endif
 
 #define PKV_BLOCK_SIZE 256
+/* Size of the split workspace held inside the library for pkv_paged_attn_decode_noalloc. */
+#define PKV_DECODE_SCRATCH_BYTES (16u << 20)
 
 enum pkv_status {
     PKV_OK = 0,
@@ -327,6 +329,25 @@ int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, 
                           const int32_t* context_lens, const int32_t* seq_order,
                           int32_t max_context_len, int32_t max_splits, float softmax_scale,
                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_paged_attn_decode_noalloc: pkv_paged_attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments and results, minus the workspace: when the plan splits contexts, the partial
+ * states go to a split workspace inside the library, one PKV_DECODE_SCRATCH_BYTES (16 MiB) array
+ * per device, kept until the process ends.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call.  A plan needing more than PKV_DECODE_SCRATCH_BYTES
+ * (pkv_decode_workspace_bytes) is refused with PKV_ERR_SMALL_BUFFER before anything is launched;
+ * lower max_splits, or call pkv_paged_attn_decode with a workspace.  Every call on one device
+ * shares that device's array, and each call's partials are written before they are read, so
+ * nothing needs clearing between calls; calls that may overlap on one device (different
+ * streams, or different threads) race on it and must be ordered by the caller. */
+int pkv_paged_attn_decode_noalloc(const pkv_cache_desc* desc, const void* q, int32_t B,
+                                  int32_t Hq, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* block_tables, int32_t max_blocks,
+                                  const int32_t* context_lens, const int32_t* seq_order,
+                                  int32_t max_context_len, int32_t max_splits,
+                                  float softmax_scale, void* out, void* stream);
 
 /* Sliding-window decode (intelliparadigm.com Nano-vLLM article, §7.2 关键优化点 lists sliding-
  * window attention): as pkv_paged_attn_decode, but sequence b attends only its last `window`

@@ -73,6 +73,8 @@ SIGNATURES = {
     "pkv_decode_launch_order": (_i32, [_pdesc, _i32, _i32, _p32, _i32, _i32, _i32, _i32, _i32, _p32]),
     "pkv_paged_attn_decode": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _f32, _vp, _vp, _sz, _vp]),
+    "pkv_paged_attn_decode_noalloc": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                             _i32, _f32, _vp, _vp]),
     "pkv_paged_attn_decode_window": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                             _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
     "pkv_decode_store_attend": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -408,6 +410,19 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
                                        _ptr(context_lens), _ptr(seq_order), int(max_context_len), int(max_splits),
                                        float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "pkv_paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len, softmax_scale, out,
+                              max_splits=0, k_scale=None, v_scale=None, seq_order=None, stream=None):
+    """pkv_paged_attn_decode_noalloc: decode attention with the split partials in the library's own
+    per-device scratch; the caller passes every input and the output ``out`` [B][Hq][D]."""
+    desc = desc_of(k_cache)
+    B, Hq, _ = q.shape
+    _check(lib().pkv_paged_attn_decode_noalloc(
+        ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), _ptr(seq_order), int(max_context_len),
+        int(max_splits), float(softmax_scale), _ptr(out), _stream(stream)), "pkv_paged_attn_decode_noalloc")
     return out
 
 

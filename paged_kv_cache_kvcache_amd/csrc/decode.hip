@@ -875,4 +875,63 @@ extern "C" int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q
                        0, stream);
 }
 
+// ------------------------------------------------------------------ allocation-free decode
+// The split partials of pkv_paged_attn_decode_noalloc live in this file-scope array: one copy per
+// device, held until the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory, so kernels are given the device address that hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept below.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(PKV_DECODE_SCRATCH_BYTES);
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+
+// *out = the device address of `scratch` on the current device; PKV_OK, or the failure recorded.
+int scratch_on_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return pkv::fail(PKV_ERR_HIP, "no current HIP device");
+    }
+    PKV_REQUIRE(dev >= 0 && dev < kScratchDevices, PKV_ERR_UNSUPPORTED,
+                "device %d: the decode scratch is kept for devices 0..%d", dev, kScratchDevices - 1);
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return pkv::fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                             hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // every thread finds the same address
+    }
+    *out = ptr;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attn_decode_noalloc(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                             const void* k_cache, const void* v_cache, const float* k_scale,
+                                             const float* v_scale, const int32_t* block_tables,
+                                             int32_t max_blocks, const int32_t* context_lens,
+                                             const int32_t* seq_order, int32_t max_context_len,
+                                             int32_t max_splits, float softmax_scale, void* out, void* stream) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    PKV_REQUIRE(B >= 0 && Hq > 0 && max_context_len >= 0 && max_splits >= 0, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hq=%d, max_context_len=%d, max_splits=%d)", B, Hq, max_context_len, max_splits);
+    const size_t need = pkv_decode_workspace_bytes(B, Hq, desc->head_dim, desc->num_kv_heads, max_context_len,
+                                                   max_splits);
+    PKV_REQUIRE(need <= kScratchBytes, PKV_ERR_SMALL_BUFFER,
+                "this decode plan needs %zu bytes of split workspace; the library's fixed scratch holds %zu "
+                "(lower max_splits, or call pkv_paged_attn_decode with a workspace)", need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && (rc = scratch_on_current_device(&ws)) != PKV_OK) return rc;
+    return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
+                       seq_order, max_context_len, max_splits, softmax_scale, out, ws, need, nullptr, 0, stream);
+}
+
 int pkv::read_error_decode(void* stream, int32_t* out) { return read_clear_error(stream, out); }
