@@ -1,26 +1,31 @@
 """Throughput of the paged-KV hot path on one MI355X, as one JSON line.
 
-Default workload: the Qwen3-0.6B-shaped decode step -- batch 256, contexts U[100, 2048], 16 query /
-8 KV heads, head_dim 128, bf16 KV, one layer.  One *step* is everything a decode iteration does on
-the path: the block manager appends one token per sequence (host C++), block tables, lengths and
-slots go to the device in one pinned copy, kv_store writes the new K/V rows, and the decode kernels
-attend over the whole paged context.  Contexts therefore grow by one token per step, as in a real
-decode loop.  All inputs are seeded synthetic data and are resident in HBM before timing starts.
+Default run: all five workloads of the path, one after another, reported in one line.
+* ``long_decode`` (the headline, top level): 7B-shaped decode, batch 64, contexts U[4096, 8192],
+  32 query / 8 KV heads, head_dim 128, bf16 KV;
+* nested under ``configs`` with the same fields: ``tiny_fp32`` (4 sequences, contexts
+  {1, 255, 256, 600}, fp32), ``qwen3_decode`` (batch 256, contexts U[100, 2048], 16/8 heads, bf16),
+  ``prefill_prefix`` (32 prompts sharing 512-token prefixes in groups of 8, chunks of at most 4096
+  new tokens, 16/8 heads, bf16) and ``int8_decode`` (batch 128, contexts U[512, 8192], 32/32 heads,
+  int8 KV with per-(block, head) scales), plus ``long_decode`` itself.
 
-``--config beam_decode`` times beam search (64 requests x 4 beams that re-fork every step, with
-copy-on-write of shared partial blocks) over the same context mix.
+A decode *step* is everything a decode iteration does on the path: the block manager appends one
+token per sequence (host C++), block tables, lengths and slots go to the device in one pinned copy,
+kv_store writes the new K/V rows, and the decode kernels attend over the whole paged context, so
+contexts grow by one token per step as in a real decode loop.  A prefill step is the whole chunked
+workload: every chunk's store and prefill attention.  All inputs are seeded synthetic data and are
+resident in HBM before timing starts.
 
-``--config prefill_prefix`` times the chunked varlen prefill workload instead (32 prompts with a
-shared 512-token prefix per group of 8, chunks of at most 4096 new tokens): one step is the
-whole workload -- every chunk's store and prefill attention.
+``--config NAME`` runs one workload alone (also ``beam_decode``, ``prefill_long``, ``int8_store``).
 
-Reported beside the throughput:
+Reported per workload:
+* ``value`` / ``ms_per_step`` -- whole steps timed by the wall clock (K steps after W warm-up steps);
 * ``roofline`` -- the dominant kernel's algorithmic traffic (decode: KV bytes of the valid tokens;
   prefill: causal flops) divided by its average duration, timed with HIP events on the launch
-  stream, against MI355X's published peak (8 TB/s HBM3E; 2.5 PFLOP/s dense bf16).  The events
-  bracket the kernel in a second pass of K steps: recording them costs the stream a few
-  microseconds per step, which the throughput pass (``value``, ``ms_per_step``) leaves out;
-* ``cpu_baseline`` -- the fp64 oracle timed on the host on a bounded sample of the same workload.
+  stream in a second pass of K steps, each preceded by a 512 MiB write that evicts L2 and the
+  MALL (``--flush-mb``), against MI355X's published peak (8 TB/s HBM3E; 2.5 PFLOP/s dense bf16);
+* ``cpu_baseline`` -- the fp64 oracle on a bounded sample of the same workload, split over
+  worker processes on the host's cores (one thread each), timed before the GPU is touched.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--seed S]
 """
@@ -45,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
     ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
-    ap.add_argument("--config", default="qwen3_decode")
+    ap.add_argument("--config", default=None, help="one workload alone (default: every workload of the path)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--max-splits", type=int, default=0)
     ap.add_argument("--window", type=int, default=0,
@@ -54,17 +59,19 @@ def parse():
                     help="decode: store the new tokens inside the attention launch (pkv_decode_store_attend)")
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's upload, store and attention from HIP graphs")
-    ap.add_argument("--flush-mb", type=int, default=0,
-                    help="decode: write this many MiB of scratch before every step (evicts L2 and MALL; the "
-                         "kernel time then reads a cold cache, the step time includes the write)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="write this many MiB of scratch before every step of the event pass, so the timed "
+                         "kernels read a cold L2 and MALL (0: no flush); the wall-clock pass never flushes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=0, help="sequences (decode) or prompts (prefill) timed on the CPU")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU time (summed over the worker processes) the oracle baseline may spend per workload")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (to scale hardware byte counters) and exit")
     ap.add_argument("--summarize", metavar="NAME",
                     help="write profiles/NAME.txt from rocprofv3 CSV output (see --prof-dir) and exit")
     ap.add_argument("--prof-dir", default="gpurun_out/prof")
     ap.add_argument("--prof-cmd", default="", help="the command lines that produced the CSVs (recorded)")
+    ap.add_argument("--prof-workload", default=None, help="the workload whose counters the CSVs hold")
     return ap.parse_args()
 
 
@@ -86,7 +93,7 @@ def source_hash(kernel):
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def summarize(name, prof_dir, cmd):
+def summarize(name, prof_dir, cmd, workload=None):
     """Summarise rocprofv3 CSVs: kernel stats, and FETCH_SIZE / WRITE_SIZE per dispatch scaled by the
     same counters' reading for a plain copy of known size."""
     import csv
@@ -122,22 +129,23 @@ def summarize(name, prof_dir, cmd):
             if f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
                 fb = f[0] * 1024 * scale["FETCH_SIZE"]
                 wb = w[0] * 1024 * scale["WRITE_SIZE"]
-                out.append(f"TRAFFIC {kern} source={source_hash(kern)} fetch_bytes={fb:.6g} write_bytes={wb:.6g} "
-                           f"total_bytes={fb + wb:.6g}")
+                out.append(f"TRAFFIC {kern} workload={workload or name} source={source_hash(kern)} "
+                           f"fetch_bytes={fb:.6g} write_bytes={wb:.6g} total_bytes={fb + wb:.6g}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     path = os.path.join(ROOT, "profiles", name + ".txt")
     open(path, "w").write("\n".join(out) + "\n")
     print(path)
 
 
-def stored_traffic(kernel):
-    """HBM bytes per dispatch from a committed counter summary, if taken on the current kernel source."""
+def stored_traffic(kernel, workload, nch=1):
+    """HBM bytes of one step (counter bytes per dispatch x ``nch`` dispatches) from a committed
+    counter summary of this workload, if taken on the current kernel source."""
     import glob
     h = source_hash(kernel)
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
         for line in open(f):
-            if line.startswith(f"TRAFFIC {kernel} source={h} "):
-                return float(line.split("total_bytes=")[1].split()[0])
+            if line.startswith(f"TRAFFIC {kernel} workload={workload} source={h} "):
+                return float(line.split("total_bytes=")[1].split()[0]) * nch
     return None
 
 # ------------------------------------------------------------------------------------ decode
@@ -147,7 +155,9 @@ def decode_max_context(lens, warmup, steps):
     return max(lens) + warmup + 2 * steps
 
 
-def bench_decode(args, cfg):
+def bench_decode(args, cfg, wl=None, cpu=None):
+    """One decode workload on the GPU; ``wl`` (generated here when None) and ``cpu`` (the oracle
+    baseline, timed here before the GPU is touched when None and not disabled)."""
     import torch
     import workloads as W
     from paged_kv_cache_kvcache_amd import BF16, F32, I8, decode_plan
@@ -162,7 +172,10 @@ def bench_decode(args, cfg):
     # so they stay out of the throughput pass
     nsteps = args.warmup + 2 * args.steps
     t0 = time.time()
-    wl = W.decode_workload(cfg, args.seed)
+    if wl is None:
+        wl = W.decode_workload(cfg, args.seed)
+    if cpu is None and not args.no_cpu_baseline:
+        cpu = cpu_baseline_decode(wl, args.window, args.cpu_seconds)
     lens = wl["lens"]
     # the pool also holds the tokens the timed steps append
     nb = max(wl["num_blocks"], W.pool_blocks(cfg, [L + nsteps for L in lens]))
@@ -240,7 +253,7 @@ def bench_decode(args, cfg):
 
     def run(i, timed_idx=None):
         st = steps[i]
-        if flush is not None:
+        if flush is not None and timed_idx is not None:  # the event pass reads a cold cache
             flush.fill_(i & 0xFF)
         slots = kv.alloc.append_batch(batch.ids, st["tokens"])
         batch.upload_step_metadata(slots)
@@ -265,6 +278,8 @@ def bench_decode(args, cfg):
 
         def run(i, timed_idx=None):  # noqa: F811
             st = steps[i]
+            if flush is not None and timed_idx is not None:
+                flush.fill_(i & 0xFF)
             gb.inputs.copy_(st["blob"])
             gb.step(st["tokens"], None if timed_idx is None else ev[timed_idx])
 
@@ -304,52 +319,98 @@ def bench_decode(args, cfg):
         decode_kernel_us=avg_kern_s * 1e6, decode_tokens_per_s_kernel=B / avg_kern_s,
         kv_gbs=achieved,
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                      traffic=stored_traffic("decode_split_kernel") if cfg["name"] == "qwen3_decode" and splits == 1
-                      and args.seed == 0 and args.window == 0 else None,
+                      traffic=stored_traffic("decode_split_kernel", cfg["name"], nch=1)
+                      if args.seed == 0 and args.window == 0 and not args.graph and not args.fused and
+                      args.max_splits == 0 else None,
                       kernel="decode (split kernel + LSE reduce when splits > 1)",
-                      bytes_per_launch=bytes_per_launch),
+                      bytes_per_launch=bytes_per_launch, cold_cache=args.flush_mb > 0),
     )
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(wl, args.cpu_sample or 8, args.window)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
-def _timed_sample(run, total, first=8, budget_s=10.0):
-    """Time ``run(n)`` on growing prefixes of the workload until one run takes ``budget_s`` or covers it all."""
-    n = min(first, total)
-    while True:
-        t0 = time.perf_counter()
-        run(n)
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or n >= total:
-            return n, dt
-        n = min(total, max(2 * n, int(n * 1.2 * budget_s / max(dt, 1e-3))))
+# ------------------------------------------------------------------------- oracle baselines
+# The oracle, as it stands, on a bounded sample of the workload.  Its items (sequences, prompts,
+# rows, repetitions) are independent, so the sample is cut into contiguous slices that worker
+# processes run at once, one thread each, over the host cores this process may use (at most 16,
+# one GPU's share of the host).  The pool is forked before the GPU is touched, and the workload it
+# reads is shared with the parent, not copied.
+_ORACLE_JOBS = {}
 
 
-def cpu_baseline_decode(wl, first=8, window=0):
-    """The oracle's whole decode step (its block manager, store and attention) on the first n sequences."""
+def host_workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _oracle_noop(_):
+    return os.getpid()
+
+
+def _oracle_slice(task):
+    name, lo, hi = task
     from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        units = _ORACLE_JOBS[name](lo, hi)
+        return units, time.perf_counter() - t0
+
+
+def parallel_oracle(fn, total, cpu_seconds=20.0):
+    """Run ``fn(lo, hi)`` (the oracle on items lo..hi-1, returning the units of work it did) over a
+    sample of the first n items, n sized from one item alone so that the workers spend about
+    ``cpu_seconds`` in total.  Returns (units, wall seconds, workers, CPU seconds, n)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        fn(0, 1)  # calibration: one item alone
+        one = max(time.perf_counter() - t0, 1e-4)
+    workers = host_workers()
+    n = int(min(total, max(1, cpu_seconds / one)))
+    w = min(workers, n)
+    bounds = [n * i // w for i in range(w + 1)]
+    key = f"job{len(_ORACLE_JOBS)}"
+    _ORACLE_JOBS[key] = fn
+    with ProcessPoolExecutor(max_workers=w, mp_context=mp.get_context("fork")) as ex:
+        list(ex.map(_oracle_noop, range(w)))  # every worker is up before the clock starts
+        t0 = time.perf_counter()
+        res = list(ex.map(_oracle_slice, [(key, bounds[i], bounds[i + 1]) for i in range(w)]))
+        wall = time.perf_counter() - t0
+    del _ORACLE_JOBS[key]
+    return sum(r[0] for r in res), wall, w, sum(r[1] for r in res), n
+
+
+def _pool_note(w, cpu_s, wall):
+    return f"{w} worker processes, one thread each: {cpu_s:.1f} s of CPU in {wall:.2f} s"
+
+
+def cpu_baseline_decode(wl, window=0, cpu_seconds=20.0):
+    """The oracle's whole decode step (its block manager, store and attention) on a sample of the
+    sequences, in slices."""
     import workloads as W
     from oracle.steps import decode_step
 
-    def run(n):
+    def run(lo, hi):
         sub = dict(wl)
-        sub["lens"] = wl["lens"][:n]
-        sub["seqs"] = wl["seqs"][:n]
+        sub["lens"] = wl["lens"][lo:hi]
+        sub["seqs"] = wl["seqs"][lo:hi]
         sub["num_blocks"] = W.pool_blocks(wl["cfg"], sub["lens"])
         sub["free_order"] = W.free_order(wl["cfg"], wl["seed"], sub["num_blocks"])
         decode_step(sub, window)
+        return hi - lo
 
-    with threadpool_limits(1):
-        n, dt = _timed_sample(run, len(wl["lens"]), first)
+    units, wall, w, cpu_s, n = parallel_oracle(run, len(wl["lens"]), cpu_seconds)
     win = f" over the last {window} keys" if window > 0 else ""
-    return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
+    return dict(value=units / wall, unit="tokens/s", cores=w, kind="oracle",
                 sample=f"first {n} of {len(wl['lens'])} sequences ({sum(wl['lens'][:n])} context tokens), one decode "
-                       f"step: oracle block manager + store + fp64 attention{win}, {dt:.1f}s on one thread")
+                       f"step: oracle block manager + store + fp64 attention{win}; {_pool_note(w, cpu_s, wall)}")
 
 
 # ------------------------------------------------------------------------------------ prefill
-def bench_prefill(args, cfg):
+def bench_prefill(args, cfg, wl=None, cpu=None):
+    """The chunked prefill workload on the GPU (``wl``, ``cpu`` as in :func:`bench_decode`)."""
     import torch
     import workloads as W
     from paged_kv_cache_kvcache_amd import BF16, desc_of, kv_store, paged_attn_prefill_ordered, prefill_work_order
@@ -357,7 +418,11 @@ def bench_prefill(args, cfg):
 
     dev = torch.device("cuda:0")
     Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
-    wl = W.prefill_workload(cfg, args.seed)
+    if wl is None:
+        wl = W.prefill_workload(cfg, args.seed)
+    if cpu is None and not args.no_cpu_baseline and args.window == 0:
+        cpu = (cpu_baseline_prefill_rows(wl, args.cpu_seconds) if cfg.get("split") else
+               cpu_baseline_prefill(wl, args.cpu_seconds))
     prompts = wl["prompts"]
     kv = R.PagedKV(wl["num_blocks"], Hkv, D, BF16, wl["free_order"], device=dev)
     t0 = time.perf_counter()
@@ -400,7 +465,11 @@ def bench_prefill(args, cfg):
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nch)]
           for _ in range(args.steps)]
 
+    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev) if args.flush_mb > 0 else None
+
     def run(timed=None):
+        if flush is not None and timed is not None:  # the event pass starts each step on a cold cache
+            flush.fill_(timed & 0xFF)
         for c, d in enumerate(dchunks):
             kv_store(d["k"], d["v"], d["slots"], kv.k_cache, kv.v_cache)
             if timed is not None:
@@ -434,9 +503,7 @@ def bench_prefill(args, cfg):
         f"{kern_s * 1e6:.1f} us/step -> {tflops:.1f} TFLOP/s; step {elapsed / args.steps * 1e3:.3f} ms")
     # counter traffic of one step (mean per dispatch x chunks), when taken on this workload and the
     # current kernel source
-    traffic = stored_traffic("prefill_kernel") if (cfg["name"] == "prefill_prefix" and args.seed == 0 and
-                                                  args.window == 0) else None
-    traffic = None if traffic is None else traffic * nch
+    traffic = stored_traffic("prefill_kernel", cfg["name"], nch) if args.seed == 0 and args.window == 0 else None
     res = dict(
         metric="paged decode tokens/s + KV HBM GB/s (% of peak); prefill TFLOP/s",
         value=total_new * args.steps / elapsed, unit="prefill tokens/s", n_gpus=1, steps=args.steps,
@@ -450,11 +517,10 @@ def bench_prefill(args, cfg):
         prefill_kernel_us=kern_s * 1e6, prefill_tflops=tflops, host_admit_us=host_s * 1e6,
         roofline=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=tflops / BF16_PEAK_TFLOPS, traffic=traffic, kernel="prefill (all chunks of one step)",
-                      flops_per_step=flops),
+                      flops_per_step=flops, cold_cache=args.flush_mb > 0),
     )
-    if not args.no_cpu_baseline and args.window == 0:
-        res["cpu_baseline"] = (cpu_baseline_prefill_rows(wl) if cfg.get("split") else
-                               cpu_baseline_prefill(wl, args.cpu_sample or 4))
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
@@ -470,17 +536,15 @@ def bench_int8_store(args, cfg):
     dev = torch.device("cuda:0")
     Hkv, D = cfg["Hkv"], cfg["D"]
     wl = W.prefill_workload(cfg, args.seed)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_int8_store(wl, args.cpu_seconds)
     prompts = wl["prompts"]
     kv = R.PagedKV(wl["num_blocks"], Hkv, D, I8, wl["free_order"], device=dev)
     ncached = [kv.alloc.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
     n_new = [len(p["tokens"]) - c for p, c in zip(prompts, ncached)]
     chunks = W.pack_chunks(n_new, cfg["chunk"])
-    dchunks, blocks, host_first = [], 0, None
+    dchunks, blocks = [], 0
     for ch in chunks:
         _, _, slots = kv.alloc.prefill_slots(ch, sum(n_new[i] for i in ch))
-        if host_first is None:  # the first chunk's rows and slots, for the oracle baseline
-            host_first = (np.concatenate([prompts[i]["k"][ncached[i]:] for i in ch]),
-                          np.concatenate([prompts[i]["v"][ncached[i]:] for i in ch]), slots.copy())
         runs, n_runs, longest = store_runs(slots)
         dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i]:] for i in ch]), dev)
         dchunks.append(dict(k=dv("k"), v=dv("v"), slots=torch.from_numpy(np.ascontiguousarray(slots)).to(dev),
@@ -518,7 +582,7 @@ def bench_int8_store(args, cfg):
     kern_s = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 1e3
     gbs = step_bytes / kern_s / 1e9
     # counter traffic per dispatch (mean over the chunks), when taken on the current kernel source
-    traffic = stored_traffic("kv_store_quant_kernel") if args.seed == 0 else None
+    traffic = stored_traffic("kv_store_quant_kernel", cfg["name"], len(dchunks)) if args.seed == 0 else None
     log(f"[bench] int8 store: {len(dchunks)} chunks, {total_new} new tokens, {step_bytes / 1e6:.1f} MB; "
         f"{kern_s * 1e6:.1f} us/step -> {gbs:.0f} GB/s")
     return dict(
@@ -530,31 +594,37 @@ def bench_int8_store(args, cfg):
                     block_size=256, chunks=len(dchunks), seed=args.seed),
         store_kernel_us=kern_s * 1e6,
         roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                      traffic=None if traffic is None else traffic * len(dchunks),
-                      kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
-        cpu_baseline=None if args.no_cpu_baseline else cpu_baseline_int8_store(host_first, wl["num_blocks"], Hkv, D),
+                      traffic=traffic, kernel="kv_store_quant (all chunks of one step)", bytes_per_step=step_bytes),
+        cpu_baseline=cpu,
     )
 
 
-def cpu_baseline_int8_store(first_chunk, num_blocks, Hkv, D, budget_s=5.0):
-    """The oracle's quantising store of the first chunk's rows, repeated for about ``budget_s``."""
-    from threadpoolctl import threadpool_limits
+def cpu_baseline_int8_store(wl, cpu_seconds=20.0):
+    """The oracle's quantising store of the first chunk's new rows (slots from the oracle's own block
+    manager), repeated; each repetition is one item."""
     import workloads as W
+    from oracle import allocator as OA
     from oracle import attention as OT
-    k_bits, v_bits, slots = first_chunk
-    k, v = W.bf16_bits_to_f32(k_bits), W.bf16_bits_to_f32(v_bits)
-    kc = np.zeros((num_blocks, Hkv, 256, D), np.int8)
-    ks = np.zeros((num_blocks, Hkv), np.float32)
-    reps = 0
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
+    cfg = wl["cfg"]
+    Hkv, D, prompts = cfg["Hkv"], cfg["D"], wl["prompts"]
+    a = OA.Allocator(wl["num_blocks"], wl["free_order"])
+    ncached = [a.add_seq(i, p["tokens"]) for i, p in enumerate(prompts)]
+    first = W.pack_chunks([len(p["tokens"]) - c for p, c in zip(prompts, ncached)], cfg["chunk"])[0]
+    _, _, slots = a.prefill_slots(first)
+    k = W.bf16_bits_to_f32(np.concatenate([prompts[i]["k"][ncached[i]:] for i in first]))
+    v = W.bf16_bits_to_f32(np.concatenate([prompts[i]["v"][ncached[i]:] for i in first]))
+    kc = np.zeros((wl["num_blocks"], Hkv, 256, D), np.int8)
+    ks = np.zeros((wl["num_blocks"], Hkv), np.float32)
+
+    def run(lo, hi):
+        for _ in range(lo, hi):
             OT.kv_store_quant(kc, kc, ks, ks, k, v, slots)
-            reps += 1
-        dt = time.perf_counter() - t0
-    return dict(value=reps * len(slots) / dt, unit="stored tokens/s", cores=1, kind="oracle",
-                sample=f"the first chunk's {len(slots)} new tokens (K and V, {Hkv} heads) stored {reps} times: "
-                       f"oracle quantising store, {dt:.1f}s on one thread")
+        return (hi - lo) * len(slots)
+
+    units, wall, w, cpu_s, n = parallel_oracle(run, 1 << 20, cpu_seconds)
+    return dict(value=units / wall, unit="stored tokens/s", cores=w, kind="oracle",
+                sample=f"the first chunk's {len(slots)} new tokens (K and V, {Hkv} heads) stored {n} times: oracle "
+                       f"quantising store; {_pool_note(w, cpu_s, wall)}")
 
 
 def bench_beam(args, cfg):
@@ -573,6 +643,7 @@ def bench_beam(args, cfg):
     B = NR * NBM
     nsteps = args.warmup + 2 * args.steps  # warm-up, the wall-clock pass, the event pass
     wl = W.decode_workload(cfg, args.seed)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_beam(wl, args.seed, args.cpu_seconds)
     lens = wl["lens"]
     # prompts, plus per beam a private partial block and the blocks its appends open
     nb = W.pool_blocks(cfg, lens) + B * (2 + -(-nsteps // 256))
@@ -675,24 +746,24 @@ def bench_beam(args, cfg):
         roofline=dict(bound="hbm", achieved=uniq_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=uniq_gbs / HBM_PEAK_GBS,
                       traffic=None, kernel="decode over every beam's context (bytes: distinct blocks once)",
                       bytes_per_launch=uniq_bytes),
-        cpu_baseline=None if args.no_cpu_baseline else cpu_baseline_beam(wl, args.seed),
+        cpu_baseline=cpu,
     )
 
 
-def cpu_baseline_beam(wl, seed, first=1):
-    """The oracle's beam step on the first n requests: admit and store the prompts, fork each into
+def cpu_baseline_beam(wl, seed, cpu_seconds=20.0):
+    """The oracle's beam step on slices of the requests: admit and store the prompts, fork each into
     its beams, append one token per beam with copy-on-write (block copies included), store the new
     rows, attend over every beam."""
-    from threadpoolctl import threadpool_limits
     import workloads as W
     from oracle import allocator as OA
     from oracle import attention as OT
     cfg = wl["cfg"]
     NBM, Hkv, D = cfg["beams"], cfg["Hkv"], cfg["D"]
 
-    def run(n):
-        seqs = wl["seqs"][:n]
-        nb = W.pool_blocks(cfg, wl["lens"][:n]) + 2 * n * NBM
+    def run(lo, hi):
+        seqs = wl["seqs"][lo:hi]
+        n = hi - lo
+        nb = W.pool_blocks(cfg, wl["lens"][lo:hi]) + 2 * n * NBM
         a = OA.Allocator(nb, W.free_order(cfg, seed, nb))
         kc = np.zeros((nb, Hkv, 256, D))
         vc = np.zeros_like(kc)
@@ -715,18 +786,17 @@ def cpu_baseline_beam(wl, seed, first=1):
         lens = [a.seq_len(b) for b in beams]
         OT.decode(W.bf16_bits_to_f32(inp["q"]), kc, vc, a.block_tables(beams, -(-max(lens) // 256)), lens,
                   1.0 / math.sqrt(D))
+        return n * NBM
 
-    with threadpool_limits(1):
-        n, dt = _timed_sample(run, len(wl["lens"]), first)
-    return dict(value=n * NBM / dt, unit="tokens/s", cores=1, kind="oracle",
+    units, wall, w, cpu_s, n = parallel_oracle(run, len(wl["lens"]), cpu_seconds)
+    return dict(value=units / wall, unit="tokens/s", cores=w, kind="oracle",
                 sample=f"first {n} of {len(wl['lens'])} requests x {NBM} beams: oracle block manager (forks, "
-                       f"copy-on-write), block copies, store, fp64 attention, {dt:.1f}s on one thread")
+                       f"copy-on-write), block copies, store, fp64 attention; {_pool_note(w, cpu_s, wall)}")
 
 
-def cpu_baseline_prefill_rows(wl, budget_s=10.0):
+def cpu_baseline_prefill_rows(wl, cpu_seconds=20.0):
     """Prompts longer than a chunk: the oracle's causal attention (plain definition, fp64) for the
-    last rows of the longest prompt, one row at a time, for about ``budget_s`` seconds."""
-    from threadpoolctl import threadpool_limits
+    last rows of the longest prompt, all heads, in slices of rows."""
     from oracle import attention as OT
     import workloads as W
     cfg = wl["cfg"]
@@ -735,49 +805,83 @@ def cpu_baseline_prefill_rows(wl, budget_s=10.0):
     L = len(p["tokens"])
     k, v, q = (W.bf16_bits_to_f32(p[x]).astype(np.float64) for x in ("k", "v", "q"))
     scale = 1.0 / math.sqrt(cfg["D"])
-    n = 0
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s and n < L:
+
+    def run(lo, hi):
+        for n in range(lo, hi):
             pos = L - 1 - n
             for h in range(cfg["Hq"]):
                 OT.attend(q[pos, h], k[:pos + 1, h // G], v[:pos + 1, h // G], scale)
-            n += 1
-        dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="prefill tokens/s", cores=1, kind="oracle",
-                sample=f"last {n} rows of the {L}-token prompt, all {cfg['Hq']} heads: fp64 causal attention, "
-                       f"{dt:.1f}s on one thread")
+        return hi - lo
+
+    units, wall, w, cpu_s, n = parallel_oracle(run, L, cpu_seconds)
+    return dict(value=units / wall, unit="prefill tokens/s", cores=w, kind="oracle",
+                sample=f"last {n} rows of the {L}-token prompt, all {cfg['Hq']} heads: fp64 causal attention; "
+                       f"{_pool_note(w, cpu_s, wall)}")
 
 
-def cpu_baseline_prefill(wl, first=4):
-    """The oracle's chunked prefill (its block manager, store, fp64 attention) on the first n prompts."""
-    from threadpoolctl import threadpool_limits
+def cpu_baseline_prefill(wl, cpu_seconds=20.0):
+    """The oracle's chunked prefill (its block manager, store, fp64 attention) on slices of the
+    prompts; a slice's prompts share prefix blocks with each other only, so each slice computes
+    the tokens it finds uncached, and those are what is counted."""
     import workloads as W
     from oracle.steps import prefill_run
     cfg = wl["cfg"]
 
-    def run(n):
+    def run(lo, hi):
         sub = dict(wl)
-        sub["lens"] = wl["lens"][:n]
-        sub["prompts"] = wl["prompts"][:n]
+        sub["lens"] = wl["lens"][lo:hi]
+        sub["prompts"] = wl["prompts"][lo:hi]
         sub["num_blocks"] = W.pool_blocks(cfg, sub["lens"])
         sub["free_order"] = W.free_order(cfg, wl["seed"], sub["num_blocks"])
-        run.out = prefill_run(sub)
+        _, ncached, _ = prefill_run(sub)
+        return sum(L - c for L, c in zip(sub["lens"], ncached))
 
-    with threadpool_limits(1):
-        n, dt = _timed_sample(run, len(wl["lens"]), first)
-    _, ncached, _ = run.out
-    new = sum(L - c for L, c in zip(wl["lens"][:n], ncached))
-    return dict(value=new / dt, unit="prefill tokens/s", cores=1, kind="oracle",
-                sample=f"first {n} of {len(wl['lens'])} prompts ({new} new tokens): oracle block manager + store + "
-                       f"fp64 causal attention, {dt:.1f}s on one thread")
+    units, wall, w, cpu_s, n = parallel_oracle(run, len(wl["lens"]), cpu_seconds)
+    return dict(value=units / wall, unit="prefill tokens/s", cores=w, kind="oracle",
+                sample=f"first {n} of {len(wl['lens'])} prompts in {w} slices ({units} new tokens): oracle block "
+                       f"manager + store + fp64 causal attention; {_pool_note(w, cpu_s, wall)}")
 
 
 # ------------------------------------------------------------------------------------ main
+# The path's five workloads; the first is the headline (top level of the default line).
+ALL_WORKLOADS = ["long_decode", "tiny_fp32", "qwen3_decode", "prefill_prefix", "int8_decode"]
+SUMMARY_KEYS = ("value", "unit", "ms_per_step", "dtype", "config", "roofline", "cpu_baseline", "decode_kernel_us",
+                "decode_tokens_per_s_kernel", "kv_gbs", "prefill_kernel_us", "prefill_tflops", "host_admit_us")
+
+
+def bench_all(args):
+    """Every workload of the path: inputs generated and the oracle baselines timed first (before the
+    GPU is touched), then each workload on the GPU.  Returns one line: the headline workload at the
+    top level, every workload under ``configs``."""
+    import workloads as W
+    cfgs = {n: W.config(n) for n in ALL_WORKLOADS}
+    wls, cpus = {}, {}
+    for n, cfg in cfgs.items():
+        t0 = time.time()
+        wls[n] = (W.prefill_workload if cfg["kind"] == "prefill" else W.decode_workload)(cfg, args.seed)
+        log(f"[bench] generated {n} in {time.time() - t0:.1f}s")
+        if not args.no_cpu_baseline:
+            cpus[n] = (cpu_baseline_prefill(wls[n], args.cpu_seconds) if cfg["kind"] == "prefill" else
+                       cpu_baseline_decode(wls[n], 0, args.cpu_seconds))
+            log(f"[bench] oracle baseline {n}: {cpus[n]['value']:.4g} {cpus[n]['unit']} ({cpus[n]['sample']})")
+    res = {}
+    for n in [x for x in ("tiny_fp32", "qwen3_decode", "prefill_prefix", "long_decode", "int8_decode")]:
+        fn = bench_prefill if cfgs[n]["kind"] == "prefill" else bench_decode
+        res[n] = fn(args, cfgs[n], wls[n], cpus.get(n))
+        wls[n] = None  # free the host copy
+        r = res[n]["roofline"]
+        log(f"[bench] {n}: {res[n]['value']:.4g} {res[n]['unit']}, {r['achieved']:.1f} {r['unit']} "
+            f"({100 * r['frac']:.1f}% of peak)")
+    top = dict(res[ALL_WORKLOADS[0]])
+    top["configs"] = {n: {k: res[n][k] for k in SUMMARY_KEYS if k in res[n]}
+                      for n in ("tiny_fp32", "qwen3_decode", "prefill_prefix", "long_decode", "int8_decode")}
+    return top
+
+
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.prof_dir, args.prof_cmd)
+        summarize(args.summarize, args.prof_dir, args.prof_cmd, args.prof_workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -786,7 +890,8 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import torch
     import workloads as W
-    if not torch.cuda.is_available():
+    # device_count() does not initialise the GPU: the oracle baselines fork worker processes first
+    if torch.cuda.device_count() < 1:
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     if args.copy_calib:
@@ -798,15 +903,18 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": n, "copy_calib_bytes_written": n, "launches": 5}), flush=True)
         return
-    cfg = W.config(args.config)
-    if cfg["kind"] == "decode":
-        res = bench_decode(args, cfg)
-    elif cfg["kind"] == "store":
-        res = bench_int8_store(args, cfg)
-    elif cfg["kind"] == "beam":
-        res = bench_beam(args, cfg)
+    if args.config is None:
+        res = bench_all(args)
     else:
-        res = bench_prefill(args, cfg)
+        cfg = W.config(args.config)
+        if cfg["kind"] == "decode":
+            res = bench_decode(args, cfg)
+        elif cfg["kind"] == "store":
+            res = bench_int8_store(args, cfg)
+        elif cfg["kind"] == "beam":
+            res = bench_beam(args, cfg)
+        else:
+            res = bench_prefill(args, cfg)
     print(json.dumps(res), flush=True)
 
 
