@@ -119,9 +119,11 @@ extern "C" int pkv_kv_store(const pkv_cache_desc* desc, const void* k_new, const
 // the fp64 quotient and rounding the exact quotient agree.
 //
 // One workgroup per (run, KV head, K or V), from a run list the host builds with the slot
-// mapping (pkv_store_runs).  Short runs (decode appends) take one wavefront, long ones eight
-// (measured on the prefill workload's chunks: 42 us per step against 48 with four wavefronts,
-// and no better with sixteen).
+// mapping (pkv_store_runs).  Short runs (decode appends) take one wavefront, long ones eight.
+// Rounding takes one FMA per value (see quant8); on the prefill workload's chunks this took a
+// chunk's store from 13.5 to 12.3 us.  Cutting long runs into 64-row pieces spread over more
+// workgroups did not pay: with a second launch for the absmax (4.7 + 9.3 us) or with every piece
+// reducing its whole run from L2 (14.7 us).
 namespace {
 
 struct QuantArgs {
@@ -135,15 +137,20 @@ struct QuantArgs {
     float* v_scale;
     int32_t num_kv_heads;
     int32_t n;            // batch rows
+    int32_t wide;         // runs of more than 16 rows: eight wavefronts per run
     int64_t pool_slots;   // num_blocks * 256
     int32_t check;        // validate the run list and slots (device-data checks)
 };
 
-// The fp32 estimate q = x * fl(1/s) of x / s has relative error below 2^-23 + 2^-48 (below
-// 3 * 2^-24 when x itself is rounded to fp32 first), so |q - x / s| < 2.3e-5 for |x / s| <= 128:
-// q rounds like x / s unless it lies within kNearHalf of a half-integer.  Only then the exact
-// fp64 residual 2 (x - k s) decides.
+// The fp32 estimate x * fl(1/s) of x / s has relative error below 2^-23 + 2^-48 (below 3 * 2^-24
+// when x itself was rounded to fp32 first), so it is within 2.3e-5 of x / s for |x / s| <= 128:
+// its rounding agrees with that of x / s unless it lies within kNearHalf of a half-integer.  Only
+// then the exact fp64 residual 2 (x - k s) decides.
 constexpr float kNearHalf = 6e-5f;
+// fma(x, rcp, kRound) rounds x * rcp (exact inside the fma) to an integer k, ties to even, and
+// leaves k in the low bits: the bit pattern is that of kRound plus k, whose low byte is k as an
+// int8 for |k| <= 128
+constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
 
 __device__ __forceinline__ int fix_rint(int k, double x, double s) {
     const double r2 = 2.0 * __builtin_fma(-double(k), s, x);  // exact
@@ -151,56 +158,97 @@ __device__ __forceinline__ int fix_rint(int k, double x, double s) {
     return k + int(r2 > s || (r2 == s && odd)) - int(r2 < -s || (r2 == -s && odd));
 }
 
-// rint(x / s), ties to even, clamped to +-127; x, s exact in fp64, s > 0.
-__device__ __forceinline__ int quant_div(double x, double s, float rcp) {
-    const float q = float(x) * rcp;
-    int k = int(__builtin_rintf(q));
-    if (fabsf(q - __builtin_floorf(q) - 0.5f) < kNearHalf) k = fix_rint(k, x, s);
-    return min(max(k, -127), 127);
-}
-
-// Eight codes rint(x[e] / s), clamped, for values exact in fp32 (one branch per 8 values).
-__device__ __forceinline__ uint2 quant8(const float (&x)[8], float s, float rcp) {
-    int k[8];
+// Code bytes of eight values: clamp(rint(x[e] / s), -127, 127) (s > 0, or s = 0 with rcp = 0,
+// which gives zeros), with x[e] * rcp first.  |x[e]| <= 127 s holds for the run's own values (s
+// is at least their absmax / 127, up to fp32 rounding that keeps the quotient below 127.5), so
+// their codes need no clamp; re-quantised rows (CLAMP) are clamped, which matters only when
+// rows 0..o0-1 were not written by this store (c old / s with old <= s is otherwise in range).
+// xd[e] is the exact value when it differs from x[e] (a product code * old); nullptr when x[e]
+// is exact.
+template <bool CLAMP>
+__device__ __forceinline__ uint2 quant8(const float (&x)[8], const double* xd, float s, float rcp) {
+    float t[8];
     bool near = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float q = x[e] * rcp;
-        k[e] = int(__builtin_rintf(q));
-        near |= fabsf(q - __builtin_floorf(q) - 0.5f) < kNearHalf;
+        t[e] = __builtin_fmaf(x[e], rcp, kRound);
+        const float r = __builtin_fmaf(x[e], rcp, -(t[e] - kRound));  // x rcp - k
+        near |= fabsf(r) > 0.5f - kNearHalf;
     }
-    if (near) {
+    uint32_t b[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k[e] = fix_rint(k[e], double(x[e]), double(s));
+    for (int e = 0; e < 8; ++e)
+        b[e] = CLAMP ? uint32_t(min(max(int(t[e] - kRound), -127), 127)) : __float_as_uint(t[e]);
+    if (near) {  // rare: the exact quotient decides
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = fix_rint(int(t[e] - kRound), xd != nullptr ? xd[e] : double(x[e]), double(s));
+            b[e] = uint32_t(min(max(k, -127), 127));
+        }
     }
-    uint32_t w[2] = {0, 0};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e >> 2] |= uint32_t(uint8_t(int8_t(min(max(k[e], -127), 127)))) << (8 * (e & 3));
-    return make_uint2(w[0], w[1]);
+    return make_uint2(__builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u) << 16),
+                      __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16));
 }
 
+// Eight values 8 pc .. 8 pc + 7 of head h of batch row t, as fp32.
+template <int D, bool F32>
+__device__ __forceinline__ void load8(const char* src, size_t row_stride, int t, int h, int pc, float (&x)[8]) {
+    const char* p = src + size_t(t) * row_stride + (size_t(h) * D + 8 * pc) * (F32 ? 4 : 2);
+    if constexpr (F32) {
+        const uint4 u0 = reinterpret_cast<const uint4*>(p)[0], u1 = reinterpret_cast<const uint4*>(p)[1];
+        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+}
+
+// The run's checks (device-data checks on): it lies in the batch and its rows in one block of
+// the pool.  The same in every thread, so a failing workgroup leaves as a whole.
+__device__ __forceinline__ bool run_ok(const QuantArgs& a, int run, int t0, int len, bool report) {
+    const bool in_batch = t0 >= 0 && len >= 1 && len <= pkv::kBlock && t0 <= a.n - len;
+    const int32_t sc = in_batch ? a.slots[t0] : 0;
+    const bool slot_ok = sc >= 0 && sc < a.pool_slots && sc % pkv::kBlock + len <= pkv::kBlock;
+    if ((!in_batch || !slot_ok) && report && threadIdx.x == 0)
+        record_error(in_batch ? pkv::kErrSlot : pkv::kErrRun, in_batch ? t0 : run, in_batch ? sc : t0);
+    return in_batch && slot_ok;
+}
+
+// Re-quantise cache rows r (of D codes) to scale sn from scale old: code -> rint(code old / sn).
+template <int D>
+__device__ __forceinline__ void requant_row_piece(int8_t* cache, int r, int cp, float old, float sn, float rcp) {
+    uint2* p = reinterpret_cast<uint2*>(cache + size_t(r) * D + 8 * cp);
+    const uint2 u = *p;
+    float x[8];
+    double xd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int c = int(int8_t((e < 4 ? u.x : u.y) >> (8 * (e & 3))));
+        xd[e] = double(c) * double(old);  // exact
+        x[e] = float(xd[e]);
+    }
+    *p = quant8<true>(x, xd, sn, rcp);
+}
+
+// ---- one workgroup per run: absmax, re-quantisation, codes and scale.  NT = 64 threads for
+// runs of at most 16 rows (decode appends), 512 for longer ones.
 template <int D, bool F32, int NT>
 __global__ __launch_bounds__(NT) void kv_store_quant_kernel(QuantArgs a) {
-    constexpr int PR = D / 8;      // 8-value pieces per row
-    constexpr int RS = NT / PR;    // rows per pass
-    constexpr int CR = D / 16;     // 16-code pieces per cache row
-    constexpr int CS = NT / CR;    // cache rows per pass
-    constexpr int MR = (NT == 64 ? 16 : pkv::kBlock) / RS;  // rows per thread for the longest run
+    constexpr int PR = D / 8;    // 8-value pieces per row
+    constexpr int RS = NT / PR;  // rows per pass
+    constexpr int MR = (NT == 64 ? 16 : pkv::kBlock) / RS;  // passes for the longest run
     constexpr int NWAVE = NT / 64;
     const int h = blockIdx.y;
     const bool is_v = blockIdx.z != 0;
     const int t0 = a.runs[2 * blockIdx.x], len = a.runs[2 * blockIdx.x + 1];
-    if (a.check) {  // the run must lie in the batch, and its rows in one block of the pool
-        const bool run_ok = t0 >= 0 && len >= 1 && len <= pkv::kBlock && t0 <= a.n - len;
-        const int32_t sc = run_ok ? a.slots[t0] : 0;
-        const bool slot_ok = sc >= 0 && sc < a.pool_slots && sc % pkv::kBlock + len <= pkv::kBlock;
-        if (!run_ok || !slot_ok) {  // the same in every thread: the workgroup leaves together
-            if (threadIdx.x == 0 && h == 0 && !is_v)
-                record_error(run_ok ? pkv::kErrSlot : pkv::kErrRun, run_ok ? t0 : int32_t(blockIdx.x),
-                             run_ok ? sc : t0);
-            return;
-        }
-    }
+    if (a.check && !run_ok(a, int(blockIdx.x), t0, len, h == 0 && !is_v)) return;
     const int32_t s0 = a.slots[t0];
     const int64_t blk = s0 / pkv::kBlock;
     const int o0 = s0 % pkv::kBlock;
@@ -210,30 +258,11 @@ __global__ __launch_bounds__(NT) void kv_store_quant_kernel(QuantArgs a) {
     const char* src = is_v ? a.v_new : a.k_new;
     const size_t row_stride = size_t(a.num_kv_heads) * D * (F32 ? 4 : 2);
     const int pc = threadIdx.x % PR, r0 = threadIdx.x / PR;
-    // batch row t, values 8 pc .. 8 pc + 7 of head h
-    auto load8 = [&](int t, float (&x)[8]) {
-        const char* p = src + size_t(t) * row_stride + (size_t(h) * D + 8 * pc) * (F32 ? 4 : 2);
-        if constexpr (F32) {
-            const uint4 u0 = reinterpret_cast<const uint4*>(p)[0], u1 = reinterpret_cast<const uint4*>(p)[1];
-            const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e]);
-        } else {
-            const uint4 u = *reinterpret_cast<const uint4*>(p);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[2 * e] = __uint_as_float(w[e] << 16);
-                x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-            }
-        }
-    };
-
-    // The run's rows, all loaded at once (a run has at most 256 rows, or 16 for one wavefront):
-    // thread (r0, pc) holds rows r0 + u RS.  Slots past the run re-read its last row.
+    // the run's rows, all loaded at once: thread (r0, pc) holds rows r0 + u RS (slots past the
+    // run re-read its last row)
     float x[MR][8];
 #pragma unroll
-    for (int u = 0; u < MR; ++u) load8(t0 + min(r0 + u * RS, len - 1), x[u]);
+    for (int u = 0; u < MR; ++u) load8<D, F32>(src, row_stride, t0 + min(r0 + u * RS, len - 1), h, pc, x[u]);
     float amax = 0.f;
 #pragma unroll
     for (int u = 0; u < MR; ++u)
@@ -249,48 +278,25 @@ __global__ __launch_bounds__(NT) void kv_store_quant_kernel(QuantArgs a) {
         for (int i = 0; i < NWAVE; ++i) amax = fmaxf(amax, s_red[i]);
     }
     const float sn = fmaxf(old, float(double(amax) / 127.0));  // the same value in every thread
-    int8_t* cache = (is_v ? a.v_cache : a.k_cache) + ((blk * a.num_kv_heads + h) * pkv::kBlock) * D;
-
-    // re-quantise the block's earlier rows when the scale grows
-    if (o0 > 0 && sn > old) {
-        const float rcp = 1.f / sn;
-        const int cp = threadIdx.x % CR;
-        for (int r = threadIdx.x / CR; r < o0; r += CS) {
-            uint4* p = reinterpret_cast<uint4*>(cache + size_t(r) * D + 16 * cp);
-            const uint4 u = *p;
-            uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t o = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int c = int(int8_t(w[e] >> (8 * b)));
-                    const int q = quant_div(double(c) * double(old), double(sn), rcp);
-                    o |= uint32_t(uint8_t(int8_t(q))) << (8 * b);
-                }
-                w[e] = o;
-            }
-            *p = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
-
-    // quantise the run's rows
     const float rcp = sn > 0.f ? 1.f / sn : 0.f;
+    int8_t* cache = (is_v ? a.v_cache : a.k_cache) + ((blk * a.num_kv_heads + h) * pkv::kBlock) * D;
+    if (o0 > 0 && sn > old) {  // re-quantise the block's earlier rows when the scale grows
+        for (int r = r0; r < o0; r += RS) requant_row_piece<D>(cache, r, pc, old, sn, rcp);
+    }
 #pragma unroll
     for (int u = 0; u < MR; ++u) {
         const int r = r0 + u * RS;
-        if (r >= len) break;
-        *reinterpret_cast<uint2*>(cache + size_t(o0 + r) * D + 8 * pc) =
-            sn > 0.f ? quant8(x[u], sn, rcp) : make_uint2(0, 0);
+        if (r < len)
+            *reinterpret_cast<uint2*>(cache + size_t(o0 + r) * D + 8 * pc) = quant8<false>(x[u], nullptr, sn, rcp);
     }
     if (threadIdx.x == 0) *scale = sn;
 }
 
-template <int D, int NT>
-void launch_quant(const QuantArgs& a, int n_runs, bool f32, hipStream_t st) {
+template <int D, bool F32>
+void launch_quant(const QuantArgs& a, int n_runs, hipStream_t st) {
     const dim3 grid(unsigned(n_runs), unsigned(a.num_kv_heads), 2);
-    if (f32) hipLaunchKernelGGL((kv_store_quant_kernel<D, true, NT>), grid, dim3(NT), 0, st, a);
-    else hipLaunchKernelGGL((kv_store_quant_kernel<D, false, NT>), grid, dim3(NT), 0, st, a);
+    if (!a.wide) hipLaunchKernelGGL((kv_store_quant_kernel<D, F32, 64>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((kv_store_quant_kernel<D, F32, 512>), grid, dim3(512), 0, st, a);
 }
 
 }  // namespace
@@ -312,7 +318,8 @@ extern "C" int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new,
                 PKV_ERR_INVALID, "NULL pointer");
     const uintptr_t mis = uintptr_t(k_new) | uintptr_t(v_new) | uintptr_t(k_cache) | uintptr_t(v_cache);
     PKV_REQUIRE((mis & 15) == 0, PKV_ERR_INVALID, "K/V pointers must be 16-byte aligned");
-    QuantArgs a;
+    QuantArgs a{};
+    a.wide = max_run > 16;  // eight wavefronts per run once a run has more than 16 rows
     a.k_new = static_cast<const char*>(k_new);
     a.v_new = static_cast<const char*>(v_new);
     a.slots = slot_mapping;
@@ -327,9 +334,8 @@ extern "C" int pkv_kv_store_quant(const pkv_cache_desc* desc, const void* k_new,
     a.check = pkv::device_checks();
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool f32 = new_dtype == PKV_F32;
-    const bool wide = max_run > 16;  // eight wavefronts per run once a run has more than 16 rows
-    if (desc->head_dim == 64) wide ? launch_quant<64, 512>(a, n_runs, f32, st) : launch_quant<64, 64>(a, n_runs, f32, st);
-    else wide ? launch_quant<128, 512>(a, n_runs, f32, st) : launch_quant<128, 64>(a, n_runs, f32, st);
+    if (desc->head_dim == 64) f32 ? launch_quant<64, true>(a, n_runs, st) : launch_quant<64, false>(a, n_runs, st);
+    else f32 ? launch_quant<128, true>(a, n_runs, st) : launch_quant<128, false>(a, n_runs, st);
     hipError_t e = hipGetLastError();
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "quantising store launch failed: %s", hipGetErrorString(e));
     return PKV_OK;

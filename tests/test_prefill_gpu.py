@@ -162,9 +162,10 @@ def test_ordered_prefill_with_padded_q_keeps_the_list_tile():
     d = P.desc_of(kv.k_cache)
     items, qt = P.prefill_work_order(d, Hq, cu, lk, True)
     assert qt == 4 * 32 // (Hq // Hkv)
-    # pad until the padded size alone would pick the other tile
-    pad = next(p for p in range(0, 64 * n, 64) if P.prefill_tile_rows(d, Hq, len(ch), n + p) != qt)
-    say(f"  {n} tokens in tiles of {qt}; {pad} rows of padding would choose "
+    # pad well past the real rows (where the kernel has a choice of tile, past the size that would
+    # choose the other one)
+    pad = next((p for p in range(0, 64 * n, 64) if P.prefill_tile_rows(d, Hq, len(ch), n + p) != qt), 2 * n)
+    say(f"  {n} tokens in tiles of {qt}; with {pad} rows of padding the size alone gives tiles of "
         f"{P.prefill_tile_rows(d, Hq, len(ch), n + pad)}")
     qp = torch.cat([q, torch.zeros((pad, Hq, D), dtype=q.dtype, device=q.device)])
     out = torch.full_like(qp, 3.0)

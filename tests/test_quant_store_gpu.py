@@ -149,3 +149,34 @@ def test_quantising_store_of_a_prompt_chunk_matches_oracle(gpu):
     torch.cuda.synchronize()
     for got, want in zip((kv.k_cache, kv.v_cache, kv.k_scale, kv.v_scale), ref):
         assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("D,hkv,src", [(128, 8, "bf16"), (64, 3, "f32")])
+def test_long_runs_match_oracle_bitwise(gpu, D, hkv, src):
+    """Runs of 17, 64, 65, 100, 200 and 256 rows (eight-wavefront workgroups), several starting
+    mid-block with a larger absmax than the block's earlier rows (so that rows 0..o0-1 are
+    re-quantised), one starting mid-block in a block never written (its sentinel scale is
+    negative: the re-quantised codes clamp), next to a 16-row run and single rows, must give the
+    oracle's codes and scales bit for bit."""
+    rng = np.random.default_rng(12)
+    nb = 12
+    st = Both(nb, hkv, D, gpu)
+    # call 1: fresh blocks, runs of 64 (block 0), 17 (block 1), 256 (block 2), 16 (block 3) and 1
+    plan1 = [(0, 0, 64), (1, 0, 17), (2, 0, 256), (3, 0, 16), (4, 0, 1)]
+    # call 2: runs continuing blocks mid-way with values 1.5x larger (scales grow: re-quantisation)
+    # or 0.5x smaller (scales stay), and a 200-row run from offset 56
+    plan2 = [(0, 64, 192, 1.5), (1, 17, 65, 0.5), (3, 16, 100, 2.0), (4, 1, 255, 1.0), (5, 0, 100, 1.0)]
+    plan3 = [(5, 100, 156, 3.0), (6, 56, 200, 1.0)]
+    for call, plan in enumerate([[(b, o, n, 1.0) for b, o, n in plan1], plan2, plan3]):
+        slots = []
+        for b, o, n, mul in plan:
+            slots += [b * BLOCK + o + i for i in range(n)]
+        n_rows = len(slots)
+        muls = np.concatenate([np.full(n, mul, np.float32) for _, _, n, mul in plan])[:, None, None]
+        k = _rows(rng, (n_rows, hkv, D), src) * muls
+        v = _rows(rng, (n_rows, hkv, D), src) * muls
+        if src == "bf16":  # keep the scaled values exact in bf16
+            k, v = W.bf16_bits_to_f32(W.f32_to_bf16_bits(k)), W.bf16_bits_to_f32(W.f32_to_bf16_bits(v))
+        runs = P.store_runs(slots)
+        say(f"  call {call}: {runs[1]} runs, longest {runs[2]}")
+        st.store(k, v, slots, src, f"long runs, call {call}")
