@@ -116,6 +116,8 @@ def summarize(name, prof_dir, cmd, workload=None):
         scale = {}
         for (run, kern, ctr), v in sorted(counters.items()):
             avg = sum(v) / len(v)
+            if ctr.startswith(("SQ_", "GRBM_")) and "prefill_kernel" not in kern:
+                continue  # shader-sequencer passes are taken for the prefill kernel
             out.append(f"{run} | {kern[:80]} | {ctr} | n={len(v)} | avg={avg:.6g} | min={min(v):.6g} | max={max(v):.6g}")
             if run == "copy" and "copyBuffer" in kern:
                 scale[ctr] = (1 << 30) / (avg * 1024)
@@ -123,6 +125,24 @@ def summarize(name, prof_dir, cmd, workload=None):
         if scale:
             out.append("copy calibration (bytes of a 1 GiB copy / counter bytes): " +
                        ", ".join(f"{k} x{v:.4f}" for k, v in sorted(scale.items())))
+        # derived shader-sequencer figures (counters are summed over the 8 XCDs; GRBM_GUI_ACTIVE
+        # counts each XCD's busy cycles, the SQ cycle counters each SIMD's or each wave's)
+        for kern in ("prefill_kernel",):
+            avg = {c: sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c.startswith(("SQ_", "GRBM_"))}
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+                simd_cycles = avg["GRBM_GUI_ACTIVE"] / 8 * 1024  # 1024 SIMDs busy for the kernel's cycles
+                out.append(f"DERIVED {kern}: MFMA busy {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f} of SIMD cycles "
+                           f"(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024))")
+                if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+                    out.append(f"DERIVED {kern}: VALU co-issued during {avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}"
+                               f" of MFMA-busy cycles")
+                for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY"):
+                    if c in avg and "SQ_WAVE_CYCLES" in avg:
+                        out.append(f"DERIVED {kern}: {c} {avg[c] / avg['SQ_WAVE_CYCLES']:.3f} of wave cycles")
+            if "SQ_INSTS_MFMA" in avg and "SQ_INSTS_VALU" in avg:
+                out.append(f"DERIVED {kern}: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f} VALU and "
+                           f"{avg.get('SQ_INSTS_LDS', 0) / avg['SQ_INSTS_MFMA']:.2f} LDS instructions per MFMA; "
+                           f"LDS bank conflicts {avg.get('SQ_LDS_BANK_CONFLICT', 0):.0f}")
         for kern in ("decode_split_kernel", "prefill_kernel", "kv_store_quant_kernel"):  # the dominant kernels
             f = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "FETCH_SIZE"]
             w = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "WRITE_SIZE"]

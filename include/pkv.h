@@ -384,7 +384,11 @@ int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q, int32_t B
                             void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
- * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation).
+ * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation): the engine's
+ * full-computation phase, attention over the whole prompt with FlashAttention-2 named as the
+ * kernel for it (intelliparadigm.com Nano-vLLM article, §7.2 关键优化点), reading a cache that
+ * the store has just written ("Nano-vLLM性能调优实战", §2.2 缓存复用策略), for varlen batches of
+ * new tokens whose cached prefix blocks are reused (ocdem.com nano-vllm article, §2.1).
  *
  * q: device bf16 [total_q][Hq][head_dim], the new tokens of B sequences back to back;
  * sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (device int32[B+1]).
