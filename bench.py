@@ -685,7 +685,7 @@ def bench_beam(args, cfg):
     mk = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.steps)]
     ev_copy, ev_dec = mk(), mk()
-    state = dict(beams=[[r] for r in range(NR)], next_id=NR)
+    state = dict(beams=np.arange(NR, dtype=np.int64)[:, None], next_id=NR)  # [request][beam] ids
     log_rows, log_copies, log_tables = [], [], []
 
     def unique_rows(tab, lens):
@@ -701,11 +701,12 @@ def bench_beam(args, cfg):
         st = steps[i]
         alloc = kv.alloc
         nid = state["next_id"]
-        par = [cur[int(p) % len(cur)] for cur, ps in zip(state["beams"], st["parents"]) for p in ps]
-        new = list(range(nid, nid + B))
+        cur = state["beams"]
+        par = np.take_along_axis(cur, st["parents"] % cur.shape[1], axis=1).ravel()
+        new = np.arange(nid, nid + B, dtype=np.int64)
         alloc.fork_batch(par, new)
-        alloc.free_batch([sid for cur in state["beams"] for sid in cur])
-        state["beams"] = [new[r * NBM:(r + 1) * NBM] for r in range(NR)]
+        alloc.free_batch(cur.ravel())
+        state["beams"] = new.reshape(NR, NBM)
         state["next_id"] = nid + B
         slots, src, dst, rows = alloc.append_batch_cow(new, st["tokens"])
         batch.set_sequences(new)
