@@ -16,7 +16,7 @@ contexts grow by one token per step as in a real decode loop.  A prefill step is
 workload: every chunk's store and prefill attention.  All inputs are seeded synthetic data and are
 resident in HBM before timing starts.
 
-``--config NAME`` runs one workload alone (also ``beam_decode``, ``prefill_long``, ``int8_store``).
+``--config NAME`` runs one workload alone (also ``beam_decode``, ``beam_long``, ``prefill_long``, ``int8_store``).
 
 Reported per workload:
 * ``value`` / ``ms_per_step`` -- whole steps timed by the wall clock (K steps after W warm-up steps);
@@ -57,6 +57,12 @@ def parse():
                     help="sliding-window attention: each query attends its last W keys (0: every key)")
     ap.add_argument("--fused", action="store_true",
                     help="decode: store the new tokens inside the attention launch (pkv_decode_store_attend)")
+    ap.add_argument("--ungrouped", action="store_true",
+                    help="beam workloads: attend every beam on its own (pkv_paged_attn_decode); by default a "
+                         "step whose requests share at least runner.GROUP_MIN_SHARED keys on average reads "
+                         "each request's shared blocks once (pkv_paged_attn_decode_grouped)")
+    ap.add_argument("--grouped", action="store_true",
+                    help="beam workloads: always read each request's shared blocks once")
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's upload, store and attention from HIP graphs")
     ap.add_argument("--flush-mb", type=int, default=512,
@@ -671,7 +677,10 @@ def bench_beam(args, cfg):
     R.admit_and_store(kv, list(range(NR)), [s["tokens"] for s in wl["seqs"]], [s["k"] for s in wl["seqs"]],
                       [s["v"] for s in wl["seqs"]])
     max_ctx = max(lens) + nsteps
-    batch = R.DecodeBatch(kv, Hq, list(range(B)), max_ctx, args.max_splits, cow=True)
+    # the beams of a request are consecutive: grouped attention reads their shared blocks once
+    batch = R.DecodeBatch(kv, Hq, list(range(B)), max_ctx, args.max_splits, cow=True,
+                          group_size=0 if args.ungrouped else NBM,
+                          group_min_shared=0 if args.grouped else R.GROUP_MIN_SHARED)
     steps = []
     for s in range(nsteps):
         inp = W.decode_step_inputs(cfg, args.seed, s, B)
@@ -686,7 +695,7 @@ def bench_beam(args, cfg):
                   for _ in range(args.steps)]
     ev_copy, ev_dec = mk(), mk()
     state = dict(beams=np.arange(NR, dtype=np.int64)[:, None], next_id=NR)  # [request][beam] ids
-    log_rows, log_copies, log_tables = [], [], []
+    log_rows, log_copies, log_tables, log_grouped = [], [], [], []
 
     def unique_rows(tab, lens):
         """Rows of the distinct physical blocks the step's beams attend (each block read once)."""
@@ -722,6 +731,7 @@ def bench_beam(args, cfg):
         batch.attend(st["q"], scale, out)
         if timed_idx is not None:
             ev_dec[timed_idx][1].record(stream)
+            log_grouped.append(batch.grouped)
             log_rows.append(int(rows.sum()))
             log_copies.append(len(src))
             log_tables.append((batch.host_block_tables.copy(), batch.host_context_lens.copy()))
@@ -760,12 +770,14 @@ def bench_beam(args, cfg):
         dtype="bf16", data="synthetic",
         config=dict(workload=cfg["name"], requests=NR, beams=NBM, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]",
                     q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256, seed=args.seed),
+        attention=f"grouped by request in {sum(log_grouped)} of {len(log_grouped)} timed steps, per beam otherwise",
         decode_kernel_us=dec_s * 1e6, decode_gbs_all_beam_reads=dec_gbs,
         copies_per_step=sum(log_copies) / args.steps, copy_kernel_us=copy_s * 1e6,
         copy=dict(bound="hbm", achieved=copy_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=copy_gbs / HBM_PEAK_GBS,
                   bytes_per_step=copy_bytes),
         roofline=dict(bound="hbm", achieved=uniq_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=uniq_gbs / HBM_PEAK_GBS,
-                      traffic=None, kernel="decode over every beam's context (bytes: distinct blocks once)",
+                      traffic=None, kernel=("grouped decode over each request's beams" if all(log_grouped) else
+                                            "decode over every beam's context") + " (bytes: distinct blocks once)",
                       bytes_per_launch=uniq_bytes),
         cpu_baseline=cpu,
     )

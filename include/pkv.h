@@ -89,8 +89,10 @@ const char* pkv_version(void);
  * its outputs unwritten.  Checks cost one test per workgroup (per row for stores).
  * pkv_device_error reads and clears the error word on `stream` and waits for the stream:
  * *code = 0 (no error) or 1 slot, 2 block id, 3 length, 4 launch-order entry, 5 run, 6
- * cu_seqlens_q, 7 copy row count; *where = the batch row, sequence or pair; *value = the bad
- * value (where and value may be NULL).  The word is per device and shared by every caller. */
+ * cu_seqlens_q, 7 copy row count, 8 a group member's block table differing within the group's
+ * shared keys; *where = the batch row, sequence or pair; *value = the bad value, or for 8 the
+ * block-table entry (where and value may be NULL).  The word is per device and shared by every
+ * caller. */
 int pkv_set_device_checks(int32_t enable);
 int pkv_device_error(int32_t* code, int32_t* where, int32_t* value, void* stream);
 
@@ -382,6 +384,42 @@ int pkv_decode_store_attend(const pkv_cache_desc* desc, const void* q, int32_t B
                             const int32_t* context_lens, const int32_t* seq_order,
                             int32_t max_context_len, int32_t max_splits, float softmax_scale,
                             void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped decode for forked sequences.  Parallel sampling and beam search keep several
+ * sequences per request that share blocks (ocdem.com nano-vllm article, §2.1; a fork shares every
+ * block of its parent, pkv_alloc_fork).  Group k is the group_size consecutive sequences
+ * k*group_size .. k*group_size + group_size - 1 of the batch; its first shared_lens[k] keys must
+ * sit in the same physical blocks for every member.  The call reads those blocks once per group
+ * and KV head for all members' query heads, then each member's remaining keys for its own heads,
+ * so the shared keys cross HBM once per group instead of once per member.  The output is that of
+ * pkv_paged_attn_decode on the same batch up to fp32 rounding order.
+ *
+ * pkv_decode_group_shared_lens (host-only): shared_lens[k] = min over the members of
+ * context_lens, capped at 256 x the number of leading block-table entries equal across the
+ * members.  block_tables: host int32[B][max_blocks]; context_lens: host int32[B], each within
+ * 0..256 x max_blocks; shared_lens: host int32[B / group_size], written.  B not a multiple of
+ * group_size, group_size < 1, a bad length or a NULL pointer (B > 0) is PKV_ERR_INVALID.
+ *
+ * pkv_paged_attn_decode_grouped: q, k_cache, v_cache, k_scale, v_scale, block_tables,
+ * context_lens, max_context_len, softmax_scale and out as in pkv_paged_attn_decode (no split, no
+ * launch order, no workspace).  shared_lens: device int32[B / group_size], each at most every
+ * member's context length (pkv_decode_group_shared_lens computes them).  group_size x Hq /
+ * num_kv_heads must be 1, 2, 4 or 8 (query rows per KV head and group), else
+ * PKV_ERR_UNSUPPORTED; B must be a multiple of group_size, else PKV_ERR_INVALID.  With
+ * device-data checks on, a shared length above a member's context (or a context above
+ * max_context_len) is recorded as error 3, a block id outside the pool as error 2 and a member
+ * whose table differs within the shared keys as error 8; that group's output is then left
+ * unwritten. */
+int pkv_decode_group_shared_lens(const int32_t* block_tables, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t B, int32_t group_size,
+                                 int32_t* shared_lens);
+int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                  const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, const int32_t* block_tables,
+                                  int32_t max_blocks, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t group_size,
+                                  const int32_t* shared_lens, float softmax_scale, void* out,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation): the engine's

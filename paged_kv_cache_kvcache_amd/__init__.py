@@ -77,6 +77,9 @@ SIGNATURES = {
                                              _i32, _f32, _vp, _vp]),
     "pkv_paged_attn_decode_window": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                             _i32, _f32, _i32, _vp, _vp, _sz, _vp]),
+    "pkv_decode_group_shared_lens": (_i32, [_p32, _i32, _p32, _i32, _i32, _p32]),
+    "pkv_paged_attn_decode_grouped": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                             _i32, _vp, _f32, _vp, _vp]),
     "pkv_decode_store_attend": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i32, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attn_prefill": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
@@ -410,6 +413,35 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, max_conte
                                        _ptr(context_lens), _ptr(seq_order), int(max_context_len), int(max_splits),
                                        float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "pkv_paged_attn_decode")
+    return out
+
+
+def decode_group_shared_lens(block_tables, context_lens, group_size, out=None):
+    """pkv_decode_group_shared_lens on host arrays: for each group of ``group_size`` consecutive
+    sequences, the leading keys every member holds in the same physical blocks (int32 numpy)."""
+    import numpy as np
+    tab, pt = _host_i32(block_tables)
+    lens, pl = _host_i32(context_lens)
+    B = len(lens)
+    mb = int(tab.shape[1]) if tab.ndim == 2 else 0
+    res = np.empty(max(B // max(int(group_size), 1), 1), dtype=np.int32) if out is None else out
+    _check(lib().pkv_decode_group_shared_lens(pt, mb, pl, B, int(group_size), res.ctypes.data_as(_p32)),
+           "pkv_decode_group_shared_lens")
+    return res[:B // max(int(group_size), 1)] if out is None else res
+
+
+def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, max_context_len, softmax_scale,
+                              group_size, shared_lens, out=None, k_scale=None, v_scale=None, stream=None):
+    """pkv_paged_attn_decode_grouped: decode for groups of ``group_size`` consecutive forked sequences
+    that share their first ``shared_lens[k]`` keys (device int32 per group); q [B][Hq][D]."""
+    desc = desc_of(k_cache)
+    B, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().pkv_paged_attn_decode_grouped(
+        ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), int(group_size),
+        _ptr(shared_lens), float(softmax_scale), _ptr(out), _stream(stream)), "pkv_paged_attn_decode_grouped")
     return out
 
 

@@ -251,6 +251,10 @@ struct DecodeArgs {
     int32_t num_blocks;
     int64_t pool_slots;  // num_blocks * 256
     int32_t check;       // launch the instantiation that validates order, lengths, block ids, new slots
+    // grouped decode (decode_group_kernel): groups of group_size consecutive sequences whose first
+    // shared_lens[group] keys sit in the same physical blocks
+    int32_t group_size;
+    const int32_t* shared_lens;
 };
 
 // Device-data checks of one (sequence, split): every block id it reads is in the pool, and so is
@@ -544,6 +548,252 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     else static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
 }
 
+// --------------------------------------------------------------------------- grouped decode
+// Forked sequences (parallel sampling, beam search) share every block of their parent (ocdem.com
+// nano-vllm article, §2.1).  Group k is the group_size consecutive sequences k*M .. k*M + M - 1,
+// whose first shared_lens[k] keys sit in the same physical blocks.  One workgroup per (group, KV
+// head) reads those blocks once for all GM = M x Gq query rows (Gq query heads per KV head), then
+// each member's remaining keys for its own Gq rows only, and writes the members' outputs: the
+// shared keys cross HBM once per group instead of once per member.  The per-block work is that of
+// decode_split_kernel (same lane layout, reductions and online softmax), with rows outside the
+// member skipped while its own keys are read.
+template <int DT, int D, int GM, bool CHECK>
+__global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
+    using T = Traits<DT, D>;
+    constexpr int E = T::E, W = T::W, RB = T::kRowBytes, PB = W * 4;
+
+    const int g = blockIdx.y, grp = blockIdx.z;
+    const int M = a.group_size, gq = a.num_q_heads / a.num_kv_heads;  // GM == M * gq
+    const int b0 = grp * M;
+    const int shared = a.shared_lens[grp];
+    if (CHECK) {  // uniform in the workgroup
+        bool ok = shared >= 0;
+        int bad = 0, val = shared;
+        for (int m = 0; ok && m < M; ++m) {
+            const int ctx = a.context_lens[b0 + m];
+            if (ctx < shared || ctx > a.max_context_len) {
+                ok = false;
+                bad = b0 + m;
+                val = ctx;
+            }
+        }
+        if (!ok) {
+            if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrLength, bad, val);
+            return;
+        }
+        // the shared blocks are one set for every member, and every block read is in the pool
+        const int nsh = (shared + pkv::kBlock - 1) / pkv::kBlock;
+        const int lane = threadIdx.x & 63;
+        for (int m = 0; m < M; ++m) {
+            const int32_t* bt = a.block_tables + size_t(b0 + m) * a.max_blocks;
+            const int32_t* bt0 = a.block_tables + size_t(b0) * a.max_blocks;
+            const int nblk = (a.context_lens[b0 + m] + pkv::kBlock - 1) / pkv::kBlock;
+            for (int e0 = 0; e0 < nblk; e0 += 64) {
+                const int e = min(e0 + lane, nblk - 1);
+                const int v = bt[e];
+                const bool differs = e < nsh && v != bt0[e];
+                const uint64_t bad_blk = __ballot(v < 0 || v >= a.num_blocks);
+                const uint64_t bad_sh = __ballot(differs);
+                if (bad_blk != 0 || bad_sh != 0) {
+                    const bool blk = bad_blk != 0;
+                    const int at = __ffsll(static_cast<unsigned long long>(blk ? bad_blk : bad_sh)) - 1;
+                    const int first = __shfl(v, at, 64);
+                    if (threadIdx.x == 0 && g == 0)
+                        record_error(blk ? pkv::kErrBlock : pkv::kErrShared, b0 + m, blk ? first : e0 + at);
+                    return;
+                }
+            }
+        }
+    }
+
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane >> 4, c = lane & 15;
+
+    // query row j: member j / gq, head g * gq + j % gq
+    typename T::QReg qr[GM];
+#pragma unroll
+    for (int j = 0; j < GM; ++j)
+        T::load_q(qr[j], a.q, (size_t(b0 + j / gq) * a.num_q_heads + g * gq + j % gq) * D + c * E);
+
+    float m[GM], l[GM], acc[GM][E];
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        m[j] = kNegInf;
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[j][e] = 0.f;
+    }
+
+    const size_t lane_off = size_t(r) * RB + size_t(c) * PB;
+    uint32_t kw[16][W], vw[16][W];
+    // One block: this wavefront's quarter of keys blk*256 .. blk*256 + 255 below ctx and from lo on,
+    // for the rows of member `only` (-1: every row).  Rows of other members take the block's work
+    // with every score masked, which leaves their state unchanged: skipping them instead made the
+    // compiler spill at eight rows.
+    auto attend_block = [&](int64_t phys, int blk, int ctx, int lo, int only) __attribute__((always_inline)) {
+        const int valid = min(kTile, ctx - (blk * pkv::kBlock + w * kTile));
+        const char* kp = a.k_cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
+        const char* vp = a.v_cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (4 * i + r < valid) {
+                load_piece<W>(kp + size_t(4 * i) * RB, kw[i]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < W; ++k) kw[i][k] = 0u;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (4 * i + r < valid) {
+                load_piece<W>(vp + size_t(4 * i) * RB, vw[i]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < W; ++k) vw[i][k] = 0u;
+            }
+        }
+        float ks = a.scale_log2, vs = 1.f;
+        if constexpr (DT == PKV_I8) {
+            ks *= a.k_scale[phys * a.num_kv_heads + g];
+            vs = a.v_scale[phys * a.num_kv_heads + g];
+        }
+        const bool row_ok = 4 * c + r < valid && blk * pkv::kBlock + w * kTile + 4 * c + r >= lo;
+        float p[GM];
+#pragma unroll
+        for (int j = 0; j < GM; ++j) {
+            float part[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) part[i] = T::dot(qr[j], kw[i]);
+            const float tot = transpose_reduce16(part, c);
+            const bool mine = only < 0 || j / gq == only;
+            const float sc = row_ok && mine ? tot * ks : kNegInf;
+            const float mn = fmaxf(m[j], row_max16(sc));
+            const bool none = mn == kNegInf;
+            const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
+            p[j] = none ? 0.f : __builtin_amdgcn_exp2f(sc - mn);
+            m[j] = mn;
+            l[j] = l[j] * alpha + p[j];
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[j][e] *= alpha;
+            p[j] *= vs;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float v[E];
+            T::unpack(vw[i], v);
+#pragma unroll
+            for (int j = 0; j < GM; ++j) {
+                float pi;
+                switch (i) {  // DPP lane selects must be immediates
+                    case 0: pi = bcast_row<0>(p[j]); break;
+                    case 1: pi = bcast_row<1>(p[j]); break;
+                    case 2: pi = bcast_row<2>(p[j]); break;
+                    case 3: pi = bcast_row<3>(p[j]); break;
+                    case 4: pi = bcast_row<4>(p[j]); break;
+                    case 5: pi = bcast_row<5>(p[j]); break;
+                    case 6: pi = bcast_row<6>(p[j]); break;
+                    case 7: pi = bcast_row<7>(p[j]); break;
+                    case 8: pi = bcast_row<8>(p[j]); break;
+                    case 9: pi = bcast_row<9>(p[j]); break;
+                    case 10: pi = bcast_row<10>(p[j]); break;
+                    case 11: pi = bcast_row<11>(p[j]); break;
+                    case 12: pi = bcast_row<12>(p[j]); break;
+                    case 13: pi = bcast_row<13>(p[j]); break;
+                    case 14: pi = bcast_row<14>(p[j]); break;
+                    default: pi = bcast_row<15>(p[j]); break;
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[j][e] = fmaf(pi, v[e], acc[j][e]);
+            }
+        }
+    };
+
+    // ---- one walk over this wavefront's blocks (one call site keeps the register allocation that
+    // of one loop): first the shared keys 0 .. shared-1 from member 0's table (64 entries per
+    // VGPR, by readlane), then each member's own keys shared .. ctx-1 (a few blocks, one scalar
+    // load each)
+    const int32_t* bt0 = a.block_tables + size_t(b0) * a.max_blocks;
+    const int nsh = (shared + pkv::kBlock - 1) / pkv::kBlock;
+    const int n_shared = min(nsh, max(0, (shared - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
+    const int first = shared / pkv::kBlock;
+    int bt_win = 0;
+    int btv = lane < nsh ? bt0[lane] : 0;
+    int mm = -1, blk = 0, blk_end = n_shared, ctx = shared, lo = 0;
+    const int32_t* bt = bt0;
+    while (true) {
+        if (blk >= blk_end) {  // next member with blocks for this wavefront
+            if (++mm >= M) break;
+            ctx = a.context_lens[b0 + mm];
+            bt = a.block_tables + size_t(b0 + mm) * a.max_blocks;
+            blk = first;
+            blk_end = min((ctx + pkv::kBlock - 1) / pkv::kBlock, max(first, (ctx - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
+            lo = shared;
+            continue;
+        }
+        int64_t phys;
+        if (mm < 0) {
+            const int win = blk >> 6;
+            if (win != bt_win) {
+                bt_win = win;
+                const int e = 64 * win + lane;
+                btv = e < nsh ? bt0[e] : 0;
+            }
+            phys = __builtin_amdgcn_readlane(btv, blk & 63);
+        } else {
+            phys = __builtin_amdgcn_readfirstlane(bt[blk]);
+        }
+        attend_block(phys, blk, ctx, lo, mm);
+        ++blk;
+    }
+
+    // ---- merge the four lane groups of each wavefront, then the four wavefronts through LDS
+    __shared__ float s_m[kWaves][GM], s_l[kWaves][GM];
+    __shared__ float s_acc[kWaves][GM][D];
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        float Mx = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
+        Mx = fmaxf(Mx, __shfl_xor(Mx, 32, 64));
+        const float f = m[j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m[j] - Mx);
+        const float L = wave_sum(l[j] * f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float x = acc[j][e] * f;
+            x += __shfl_xor(x, 16, 64);
+            x += __shfl_xor(x, 32, 64);
+            acc[j][e] = x;
+        }
+        if (lane == 0) {
+            s_m[w][j] = Mx;
+            s_l[w][j] = L;
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_acc[w][j][c * E + e] = acc[j][e];
+        }
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < GM * D; idx += kThreads) {
+        const int j = idx / D, d = idx - j * D;
+        float Mx = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) Mx = fmaxf(Mx, s_m[ww][j]);
+        float num = 0.f, den = 0.f;
+        if (Mx != kNegInf) {
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = s_m[ww][j] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s_m[ww][j] - Mx);
+                num += f * s_acc[ww][j][d];
+                den += f * s_l[ww][j];
+            }
+        }
+        const float o = den > 0.f ? num / den : 0.f;
+        const size_t oi = (size_t(b0 + j / gq) * a.num_q_heads + g * gq + j % gq) * D + d;
+        if constexpr (DT == PKV_F32) static_cast<float*>(a.out)[oi] = o;
+        else static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(o);
+    }
+}
+
 // ------------------------------------------------------------------------------ planning
 // Automatic plan: split only until the launch has two workgroups per CU.  Measured on MI355X, a
 // launch that already fills the chip twice over (e.g. 64 long sequences x 8 KV heads) runs fastest
@@ -828,6 +1078,30 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
     return PKV_OK;
 }
 
+template <int DT, int D, int GM>
+hipError_t launch_group_gm(const DecodeArgs& a, int n_groups, hipStream_t st) {
+    const dim3 grid(1, unsigned(a.num_kv_heads), unsigned(n_groups));
+    if (a.check) hipLaunchKernelGGL((decode_group_kernel<DT, D, GM, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((decode_group_kernel<DT, D, GM, false>), grid, dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_group_d(const DecodeArgs& a, int n_groups, int GM, hipStream_t st) {
+    switch (GM) {
+        case 1: return launch_group_gm<DT, D, 1>(a, n_groups, st);
+        case 2: return launch_group_gm<DT, D, 2>(a, n_groups, st);
+        case 4: return launch_group_gm<DT, D, 4>(a, n_groups, st);
+        case 8: return launch_group_gm<DT, D, 8>(a, n_groups, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT>
+hipError_t launch_group(const DecodeArgs& a, int n_groups, int GM, int D, hipStream_t st) {
+    return D == 64 ? launch_group_d<DT, 64>(a, n_groups, GM, st) : launch_group_d<DT, 128>(a, n_groups, GM, st);
+}
+
 }  // namespace
 
 extern "C" int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
@@ -932,6 +1206,100 @@ extern "C" int pkv_paged_attn_decode_noalloc(const pkv_cache_desc* desc, const v
     if (need > 0 && (rc = scratch_on_current_device(&ws)) != PKV_OK) return rc;
     return decode_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
                        seq_order, max_context_len, max_splits, softmax_scale, out, ws, need, nullptr, 0, stream);
+}
+
+extern "C" int pkv_decode_group_shared_lens(const int32_t* block_tables, int32_t max_blocks,
+                                            const int32_t* context_lens, int32_t B, int32_t group_size,
+                                            int32_t* shared_lens) {
+    PKV_REQUIRE(B >= 0 && max_blocks >= 0 && group_size >= 1, PKV_ERR_INVALID,
+                "bad shape (B=%d, max_blocks=%d, group_size=%d)", B, max_blocks, group_size);
+    PKV_REQUIRE(B % group_size == 0, PKV_ERR_INVALID, "B %d is not a multiple of group_size %d", B, group_size);
+    if (B == 0) return PKV_OK;
+    PKV_REQUIRE(block_tables && context_lens && shared_lens, PKV_ERR_INVALID, "NULL pointer");
+    for (int b = 0; b < B; ++b)
+        PKV_REQUIRE(context_lens[b] >= 0 && int64_t(context_lens[b]) <= int64_t(max_blocks) * pkv::kBlock,
+                    PKV_ERR_INVALID, "context_lens[%d] = %d outside 0..%lld", b, context_lens[b],
+                    (long long)max_blocks * pkv::kBlock);
+    for (int k = 0; k < B / group_size; ++k) {
+        const int b0 = k * group_size;
+        int len = context_lens[b0];
+        for (int m = 1; m < group_size; ++m) len = std::min(len, context_lens[b0 + m]);
+        // leading blocks of the shortest context that every member holds at the same entry
+        const int nblk = (len + pkv::kBlock - 1) / pkv::kBlock;
+        int n = 0;
+        for (; n < nblk; ++n) {
+            const int32_t blk = block_tables[size_t(b0) * max_blocks + n];
+            bool same = true;
+            for (int m = 1; m < group_size && same; ++m) same = block_tables[size_t(b0 + m) * max_blocks + n] == blk;
+            if (!same) break;
+        }
+        shared_lens[k] = std::min(len, n * pkv::kBlock);
+    }
+    return PKV_OK;
+}
+
+extern "C" int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                             const void* k_cache, const void* v_cache, const float* k_scale,
+                                             const float* v_scale, const int32_t* block_tables,
+                                             int32_t max_blocks, const int32_t* context_lens,
+                                             int32_t max_context_len, int32_t group_size,
+                                             const int32_t* shared_lens, float softmax_scale, void* out,
+                                             void* stream) {
+    int rc = pkv::check_desc(desc);
+    if (rc != PKV_OK) return rc;
+    const int Hkv = desc->num_kv_heads, D = desc->head_dim;
+    PKV_REQUIRE(B >= 0 && Hq > 0 && max_blocks >= 0 && max_context_len >= 0 && group_size >= 1, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hq=%d, max_blocks=%d, max_context_len=%d, group_size=%d)", B, Hq, max_blocks,
+                max_context_len, group_size);
+    PKV_REQUIRE(Hq % Hkv == 0, PKV_ERR_INVALID, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+    PKV_REQUIRE(B % group_size == 0, PKV_ERR_INVALID, "B %d is not a multiple of group_size %d", B, group_size);
+    const int GM = group_size * (Hq / Hkv);
+    PKV_REQUIRE(GM == 1 || GM == 2 || GM == 4 || GM == 8, PKV_ERR_UNSUPPORTED,
+                "group_size x Hq / Hkv = %d query rows per KV head: supported 1, 2, 4, 8", GM);
+    PKV_REQUIRE(int64_t(max_blocks) * pkv::kBlock >= max_context_len, PKV_ERR_INVALID,
+                "max_blocks %d cannot hold max_context_len %d", max_blocks, max_context_len);
+    PKV_REQUIRE(B / group_size <= 65535 && Hkv <= 65535, PKV_ERR_UNSUPPORTED,
+                "at most 65535 groups and 65535 KV heads");
+    PKV_REQUIRE(std::isfinite(softmax_scale), PKV_ERR_INVALID, "softmax_scale is not finite");
+    const bool i8 = desc->kv_dtype == PKV_I8;
+    PKV_REQUIRE(i8 == (k_scale != nullptr) && i8 == (v_scale != nullptr), PKV_ERR_INVALID,
+                "k_scale / v_scale are required for int8 caches and rejected otherwise");
+    if (B == 0) return PKV_OK;
+    PKV_REQUIRE(q && k_cache && v_cache && block_tables && context_lens && shared_lens && out, PKV_ERR_INVALID,
+                "NULL pointer");
+    const uintptr_t mis = uintptr_t(q) | uintptr_t(k_cache) | uintptr_t(v_cache) | uintptr_t(out);
+    PKV_REQUIRE((mis & 15) == 0, PKV_ERR_INVALID, "q, caches and out must be 16-byte aligned");
+    DecodeArgs a{};
+    a.q = q;
+    a.k_cache = static_cast<const char*>(k_cache);
+    a.v_cache = static_cast<const char*>(v_cache);
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.max_blocks = max_blocks;
+    a.max_context_len = max_context_len;
+    a.num_kv_heads = Hkv;
+    a.num_q_heads = Hq;
+    a.splits = 1;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.B = B;
+    a.num_blocks = desc->num_blocks;
+    a.pool_slots = int64_t(desc->num_blocks) * pkv::kBlock;
+    a.check = pkv::device_checks();
+    a.group_size = group_size;
+    a.shared_lens = shared_lens;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int ng = B / group_size;
+    hipError_t e;
+    switch (desc->kv_dtype) {
+        case PKV_F32: e = launch_group<PKV_F32>(a, ng, GM, D, st); break;
+        case PKV_BF16: e = launch_group<PKV_BF16>(a, ng, GM, D, st); break;
+        default: e = launch_group<PKV_I8>(a, ng, GM, D, st); break;
+    }
+    PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "grouped decode launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
 }
 
 int pkv::read_error_decode(void* stream, int32_t* out) { return read_clear_error(stream, out); }

@@ -43,6 +43,7 @@ enum DeviceError : int32_t {
     kErrRun = 5,        // run list entry outside the batch or its block
     kErrCuSeqlens = 6,  // cu_seqlens_q not non-decreasing within 0..total_q
     kErrRows = 7,       // copy row count outside 0..256
+    kErrShared = 8,     // a group member whose block table differs within the group's shared keys
 };
 
 // Each kernel translation unit keeps its own error word (code, where, value) in device memory;

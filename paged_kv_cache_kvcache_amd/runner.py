@@ -11,11 +11,15 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_plan, decode_store_attend,
+from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_group_shared_lens, decode_plan,
+               decode_store_attend, paged_attn_decode_grouped,
                decode_workspace_bytes, desc_of, kv_store, kv_store_quant, lib, paged_attn_decode,
                paged_attn_prefill_ordered, prefill_work_order)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
+# mean shared keys per group from which DecodeBatch reads a group's shared blocks once
+# (pkv_paged_attn_decode_grouped); measured crossover on MI355X, bf16, 16 / 8 heads, D 128
+GROUP_MIN_SHARED = 2048
 
 
 def _to_dev(a, device, dtype=None):
@@ -73,7 +77,8 @@ class DecodeBatch:
     """A batch of sequences in decode: history admitted and stored, then one token per step
     (``fused``: the step's store and attention in one launch, pkv_decode_store_attend)."""
 
-    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False, window=0, cow=False):
+    def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False, window=0, cow=False,
+                 group_size=0, group_min_shared=GROUP_MIN_SHARED):
         self.kv = kv
         self.Hq = int(Hq)
         self.ids = np.asarray(seq_ids, dtype=np.int64)
@@ -84,14 +89,25 @@ class DecodeBatch:
         self.fused = fused
         self.window = int(window)  # > 0: sliding-window attention over the last `window` keys
         self.cow = bool(cow)  # sequences share blocks (forks): appends copy shared partial blocks
+        # > 0: sequences k*group_size .. k*group_size + group_size - 1 are forks of one request.  A step
+        # whose groups share at least group_min_shared keys on average reads them once per group
+        # (pkv_paged_attn_decode_grouped); shorter shared prefixes stay in the caches when every
+        # sequence reads them, and the per-sequence kernel is faster there.
+        self.group_size = int(group_size)
+        self.group_min_shared = int(group_min_shared)
+        self.grouped = False  # the path the last uploaded step takes
         if self.fused and self.window:
             raise ValueError("the fused store+attend step has no sliding window")
+        if self.group_size and (self.fused or self.window or self.B % self.group_size):
+            raise ValueError("grouped attention needs B a multiple of group_size, no window and no fused step")
         dev = kv.device
         self._desc = desc_of(kv.k_cache)
         # pinned staging for the per-step metadata: slots[B] | lens[B] | order[B] | tables[B][max_blocks]
         # and, with cow, the step's block copies: src[B] | dst[B] | rows[B]
         nmeta = 3 * self.B + self.B * self.max_blocks
-        self._pin = torch.empty(nmeta + (3 * self.B if self.cow else 0), dtype=torch.int32).pin_memory()
+        ncow = 3 * self.B if self.cow else 0
+        ngroups = self.B // self.group_size if self.group_size else 0
+        self._pin = torch.empty(nmeta + ncow + ngroups, dtype=torch.int32).pin_memory()
         self._meta = torch.empty_like(self._pin, device=dev)
         self._copied = torch.cuda.Event()
         self._copied.record()
@@ -104,7 +120,9 @@ class DecodeBatch:
         self._order_args = (ctypes.byref(self._desc), self.Hq, self.B, pin[self.B:].ctypes.data_as(p32),
                             self.max_context_len, int(max_splits), self.window, 0, 0,
                             pin[2 * self.B:].ctypes.data_as(p32))
-        self._cow = self._meta[nmeta:]
+        self._cow = self._meta[nmeta:nmeta + ncow]
+        self._groups_at = nmeta + ncow
+        self.shared_lens = self._meta[self._groups_at:self._groups_at + ngroups]  # per group
         self.n_copies = 0
         # the split plan the library uses: a window of W keys spans at most ceil((W + 255) / 256) blocks
         span = min(self.max_context_len, self.window + BLOCK - 1) if self.window else self.max_context_len
@@ -141,6 +159,14 @@ class DecodeBatch:
         lens = pin[B:2 * B]
         self.kv.alloc.block_tables(self.ids, mb, out=tab, context_lens=lens)
         self.host_context_lens, self.host_block_tables = lens, tab  # valid until the next upload
+        if self.group_size:
+            ng = B // self.group_size
+            sh = pin[self._groups_at:self._groups_at + ng]
+            decode_group_shared_lens(tab, lens, self.group_size, out=sh)
+            self.host_shared_lens = sh
+            self.grouped = bool(sh.mean() >= self.group_min_shared)
+            if self.grouped:
+                return
         # longest contexts first; when the whole launch is resident at once, balanced per CU
         # (pkv_decode_launch_order, called with pointers bound once: it runs every step)
         _check(lib().pkv_decode_launch_order(*self._order_args), "pkv_decode_launch_order")
@@ -175,6 +201,11 @@ class DecodeBatch:
                                   seq_order=self.seq_order)
 
     def attend(self, q, softmax_scale, out=None):
+        if self.grouped:
+            return paged_attn_decode_grouped(q, self.kv.k_cache, self.kv.v_cache, self.block_tables,
+                                             self.context_lens, self.max_context_len, softmax_scale, self.group_size,
+                                             self.shared_lens, out=out, k_scale=self.kv.k_scale,
+                                             v_scale=self.kv.v_scale)
         return paged_attn_decode(q, self.kv.k_cache, self.kv.v_cache, self.block_tables, self.context_lens,
                                 self.max_context_len, softmax_scale, out=out, workspace=self.workspace,
                                 max_splits=self.max_splits, k_scale=self.kv.k_scale, v_scale=self.kv.v_scale,

@@ -135,6 +135,80 @@ def test_decode_rejects_bad_arguments():
     assert _decode(d, B=0) == P.OK
 
 
+def _grouped(desc, B=4, Hq=4, group_size=2, max_blocks=3, max_ctx=600, ks=None, vs=None, scale=0.125):
+    return P.lib().pkv_paged_attn_decode_grouped(ctypes.byref(desc), FAKE, B, Hq, FAKE, FAKE, ks, vs, FAKE,
+                                                 max_blocks, FAKE, max_ctx, group_size, FAKE, scale, FAKE, None)
+
+
+def test_grouped_decode_rejects_bad_arguments():
+    d = _desc()  # 2 KV heads: Hq 4 gives two query heads per KV head
+    assert _grouped(d, B=3) == P.ERR_INVALID                       # B % group_size
+    assert _grouped(d, group_size=0) == P.ERR_INVALID
+    assert _grouped(d, group_size=8, B=8) == P.ERR_UNSUPPORTED     # 8 members x 2 heads = 16 rows
+    assert _grouped(d, group_size=3, B=6) == P.ERR_UNSUPPORTED     # 6 rows
+    assert _grouped(d, Hq=3) == P.ERR_INVALID
+    assert _grouped(d, max_blocks=2) == P.ERR_INVALID               # table too narrow
+    assert _grouped(d, ks=FAKE, vs=FAKE) == P.ERR_INVALID
+    assert _grouped(_desc(kv_dtype=P.I8)) == P.ERR_INVALID
+    assert _grouped(d, B=0) == P.OK
+
+
+def _shared_lens_by_definition(tab, lens, m):
+    """Per group: the shortest member's length, cut at 256 x the first block entry where the
+    members' tables differ (only entries below that length count)."""
+    res = []
+    for k in range(len(lens) // m):
+        rows, n = tab[k * m:(k + 1) * m], min(lens[k * m:(k + 1) * m])
+        e = 0
+        while e < -(-n // 256) and len(set(int(x) for x in rows[:, e])) == 1:
+            e += 1
+        res.append(min(n, 256 * e))
+    return res
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_group_shared_lens_match_the_definition(seed):
+    """pkv_decode_group_shared_lens against a brute-force reading of its definition on random
+    fork structures: members copied from one table, then diverging from a random block on."""
+    rng = np.random.default_rng(seed)
+    m = [1, 2, 3, 4, 8, 5][seed]
+    ng, mb = 7, 6
+    tab = np.full((ng * m, mb), -1, dtype=np.int32)
+    lens = np.zeros(ng * m, dtype=np.int32)
+    nxt = 0
+    for k in range(ng):
+        base = rng.integers(0, 1000, size=mb).astype(np.int32)
+        for j in range(m):
+            i = k * m + j
+            n = int(rng.integers(0, mb * 256 + 1)) if k != 0 else 256 * int(rng.integers(0, mb + 1))
+            nb = -(-n // 256)
+            row = base.copy()
+            cut = int(rng.integers(0, mb + 1))  # from this block on the member has its own
+            row[cut:] = 2000 + nxt + np.arange(mb - cut)
+            nxt += mb
+            tab[i, :nb] = row[:nb]
+            lens[i] = n
+    got = P.decode_group_shared_lens(tab, lens, m).tolist()
+    assert got == _shared_lens_by_definition(tab, lens.tolist(), m)
+    # a group whose members are identical shares everything; one whose first entries differ nothing
+    same = np.tile(np.array([[5, 6, -1]], np.int32), (m, 1))
+    assert P.decode_group_shared_lens(same, np.full(m, 300, np.int32), m).tolist() == [300]
+    if m > 1:
+        diff = same.copy()
+        diff[1, 0] = 9
+        assert P.decode_group_shared_lens(diff, np.full(m, 300, np.int32), m).tolist() == [0]
+
+
+def test_group_shared_lens_errors():
+    tab = np.zeros((4, 2), np.int32)
+    with pytest.raises(RuntimeError):
+        P.decode_group_shared_lens(tab, np.full(4, 10, np.int32), 3)      # B % group_size
+    with pytest.raises(RuntimeError):
+        P.decode_group_shared_lens(tab, np.array([10, -1, 5, 5], np.int32), 2)  # negative length
+    with pytest.raises(RuntimeError):
+        P.decode_group_shared_lens(tab, np.array([10, 513, 5, 5], np.int32), 2)  # past the table
+
+
 def test_fused_store_decode_rejects_bad_arguments():
     d = _desc()
     i8 = _desc(kv_dtype=P.I8)

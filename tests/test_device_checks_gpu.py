@@ -199,3 +199,37 @@ def test_ordered_prefill_rejects_an_item_outside_the_call(checks):
                                  _i32([[0, 1], [2, 3]], dev), 0.088, items, 64, True, out=out)
     _expect(RUN, 2, 2 << 16)
     assert out[:64].abs().sum() > 0 and out[64:].abs().sum() > 0
+
+
+SHARED = 8
+
+
+@pytest.mark.parametrize("case", ["tables differ", "shared past a context", "block outside the pool"])
+def test_grouped_decode_rejects_a_bad_group(checks, case):
+    """pkv_paged_attn_decode_grouped, two groups of two sequences: group 0 is bad in one way, group 1
+    is valid.  Group 0's outputs stay unwritten, group 1's match the plain decode."""
+    dev = checks
+    _, (kc, vc) = _caches(dev)
+    kc.copy_(torch.randn_like(kc, dtype=torch.float32).to(kc.dtype))
+    vc.copy_(torch.randn_like(vc, dtype=torch.float32).to(vc.dtype))
+    tab = [[0, 1, -1], [0, 1, -1], [3, 4, -1], [3, 5, -1]]
+    lens, shared = [400, 400, 300, 300], [400, 256]
+    expect = None
+    if case == "tables differ":  # member 1 has its own block at entry 1, inside the claimed 400 keys
+        tab[1][1] = 2
+        expect = (SHARED, 1, 1)
+    elif case == "shared past a context":
+        shared[0] = 500
+        expect = (LENGTH, 0, 400)
+    else:
+        tab[1][1] = tab[0][1] = NB  # shared, but outside the pool
+        expect = (BLOCK_ID, 0, NB)
+    q = torch.randn(4, HQ, D, device=dev).to(torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    t, ln = _i32(tab, dev), _i32(lens, dev)
+    P.paged_attn_decode_grouped(q, kc, vc, t, ln, 400, 0.088, 2, _i32(shared, dev), out=out)
+    _expect(*expect)
+    assert bool((out[:2] == 7.0).all())
+    ref = P.paged_attn_decode(q[2:], kc, vc, t[2:], ln[2:], 400, 0.088)
+    torch.cuda.synchronize()
+    assert (out[2:].float() - ref.float()).abs().max().item() < 2e-2

@@ -37,19 +37,19 @@ class Both:
     mode "bf16": bf16 cache; "i8": int8 cache fed pre-quantised rows with per-token scales;
     "i8q": int8 cache fed bf16 rows through the quantising store."""
 
-    def __init__(self, mode, device, seed):
-        self.mode, self.device = mode, device
+    def __init__(self, mode, device, seed, hkv=HKV, d=D, nb=NB):
+        self.mode, self.device, self.hkv, self.d = mode, device, hkv, d
         self.rng = np.random.default_rng(seed)
-        order = np.random.default_rng(seed + 100).permutation(NB).astype(np.int32)
-        shape = (NB, HKV, 256, D)
+        order = np.random.default_rng(seed + 100).permutation(nb).astype(np.int32)
+        shape = (nb, hkv, 256, d)
         if mode == "bf16":
-            self.kv = R.PagedKV(NB, HKV, D, P.BF16, order, device=device, fill=float("nan"))
+            self.kv = R.PagedKV(nb, hkv, d, P.BF16, order, device=device, fill=float("nan"))
             self.oc = [np.full(shape, np.nan, dtype=np.float32) for _ in range(2)]
         else:
-            self.kv = R.PagedKV(NB, HKV, D, P.I8, order, device=device, fill=CODE_FILL)
+            self.kv = R.PagedKV(nb, hkv, d, P.I8, order, device=device, fill=CODE_FILL)
             self.oc = [np.full(shape, CODE_FILL, dtype=np.int8) for _ in range(2)]
-            self.oc += [np.zeros((NB, HKV), dtype=np.float32) for _ in range(2)]
-        self.oa = OA.Allocator(NB, order, prefix_cache=True)
+            self.oc += [np.zeros((nb, hkv), dtype=np.float32) for _ in range(2)]
+        self.oa = OA.Allocator(nb, order, prefix_cache=True)
 
     # --- both sides --------------------------------------------------------------------------
     def add(self, sid, toks):
@@ -86,12 +86,12 @@ class Both:
         """(oracle rows, device rows, oracle scales, device scales) of new tokens at ``slots``."""
         n = len(slots)
         if self.mode == "i8":
-            codes = self.rng.integers(-127, 128, size=(n, HKV, D)).astype(np.int8)
+            codes = self.rng.integers(-127, 128, size=(n, self.hkv, self.d)).astype(np.int8)
             # a block keeps one scale per KV head: rows bound for one block carry the same one
             blk = np.asarray(slots, dtype=np.float32)[:, None] // 256
-            sc = (0.005 + 0.0003 * blk + 0.002 * np.arange(HKV, dtype=np.float32)).astype(np.float32)
+            sc = (0.005 + 0.0003 * blk + 0.002 * np.arange(self.hkv, dtype=np.float32)).astype(np.float32)
             return codes, _dev(codes, self.device), sc, _dev(sc, self.device)
-        bits = W.f32_to_bf16_bits(self.rng.standard_normal((n, HKV, D)).astype(np.float32))
+        bits = W.f32_to_bf16_bits(self.rng.standard_normal((n, self.hkv, self.d)).astype(np.float32))
         return W.bf16_bits_to_f32(bits), R.bf16_tensor(bits, self.device), None, None
 
     def oracle_append(self, ids, toks):
@@ -137,6 +137,68 @@ class Both:
         ref = OT.decode(W.bf16_bits_to_f32(bits), *self.oc[:2], tab.tolist(), lens, SCALE,
                         *(self.oc[2:] if self.mode != "bf16" else (None, None)))
         check_tol(out.float().cpu().numpy().astype(np.float64), ref, "bf16" if self.mode == "bf16" else "i8", what)
+
+
+    def decode_grouped(self, ids, group_size, hq, what):
+        """pkv_paged_attn_decode_grouped over groups of ``group_size`` consecutive ``ids`` against
+        the oracle's plain decode of every sequence; returns the groups' shared lengths."""
+        lens = [self.oa.seq_len(i) for i in ids]
+        mb = -(-max(lens) // 256)
+        tab, dlens = self.kv.alloc.block_tables(ids, mb)
+        assert dlens.tolist() == lens and tab.tolist() == self.oa.block_tables(ids, mb)
+        shared = P.decode_group_shared_lens(tab, dlens, group_size)
+        # the definition, entry by entry: the shortest member's length, cut at the first block
+        # entry where the members' tables differ
+        for k, sl in enumerate(shared.tolist()):
+            rows = tab[k * group_size:(k + 1) * group_size]
+            n = min(lens[k * group_size:(k + 1) * group_size])
+            first_diff = next((e for e in range(-(-n // 256)) if len(set(rows[:, e].tolist())) > 1), None)
+            assert sl == (n if first_diff is None else min(n, 256 * first_diff)), (k, sl)
+        bits = W.f32_to_bf16_bits(self.rng.standard_normal((len(ids), hq, self.d)).astype(np.float32))
+        q = R.bf16_tensor(bits, self.device)
+        ks, vs = (self.kv.k_scale, self.kv.v_scale) if self.mode != "bf16" else (None, None)
+        out = P.paged_attn_decode_grouped(q, self.kv.k_cache, self.kv.v_cache, _dev(tab, self.device),
+                                          _dev(dlens, self.device), max(lens), 1.0 / math.sqrt(self.d), group_size,
+                                          _dev(shared, self.device), k_scale=ks, v_scale=vs)
+        ref = OT.decode(W.bf16_bits_to_f32(bits), *self.oc[:2], tab.tolist(), lens, 1.0 / math.sqrt(self.d),
+                        *(self.oc[2:] if self.mode != "bf16" else (None, None)))
+        check_tol(out.float().cpu().numpy().astype(np.float64), ref, "bf16" if self.mode == "bf16" else "i8", what)
+        return shared.tolist()
+
+
+@pytest.mark.parametrize("mode,hq,hkv,d,m", [("bf16", 8, 2, 128, 2), ("bf16", 4, 2, 128, 4), ("bf16", 2, 2, 64, 8),
+                                             ("bf16", 2, 2, 128, 1), ("i8", 8, 4, 128, 2), ("i8q", 4, 4, 64, 4)])
+def test_grouped_decode_matches_oracle(gpu, mode, hq, hkv, d, m):
+    """Groups of m forks per request, read through pkv_paged_attn_decode_grouped, against the oracle:
+    prompts ending inside a block, on a block boundary and one token short of one; members whose
+    lengths differ inside a group; a member re-forked from another after a prune; appends that
+    cross into new blocks, so members differ in full blocks too."""
+    both = Both(mode, gpu, seed=20 + m, hkv=hkv, d=d, nb=72)
+    rnd = np.random.default_rng(m)
+    prompts = [300, 512, 255]
+    groups = []
+    for r, n in enumerate(prompts):
+        both.add(100 * r, rnd.integers(0, 1000, size=n).tolist())
+        for k in range(1, m):
+            both.fork(100 * r, 100 * r + k)
+        groups.append([100 * r + k for k in range(m)])
+    flat = lambda: [i for g in groups for i in g]
+    seen_partial = False
+    for step in range(5):
+        if step == 1:  # the first member of every group runs two tokens ahead of the others
+            both.step([g[0] for g in groups])
+            both.step([g[0] for g in groups])
+        if step == 3 and m > 1:  # prune each group's last member, re-fork it from the first
+            for g in groups:
+                both.free(g[-1])
+                both.fork(g[0], g[-1])
+        both.step(flat())
+        shared = both.decode_grouped(flat(), m, hq, f"{mode} m={m} step {step}")
+        lens = [both.oa.seq_len(i) for i in flat()]
+        seen_partial |= any(sl < max(lens[k * m:(k + 1) * m]) for k, sl in enumerate(shared))
+        say(f"  {mode} hq={hq} hkv={hkv} d={d} m={m} step {step}: shared {shared}, lengths {lens}")
+        both.oa.check_invariants()
+    assert seen_partial or m == 1  # some member read keys beyond its group's shared ones
 
 
 @pytest.mark.parametrize("mode", ["bf16", "i8", "i8q"])

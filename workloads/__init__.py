@@ -62,6 +62,9 @@ CONFIGS = {
     # beam search over decode prompts: B requests x `beams` beams that re-fork every step
     "beam_decode": dict(id=8, kind="beam", B=64, beams=4, ctx=(100, 2048), Hq=16, Hkv=8, D=128,
                         dtype="bf16", value_scale=0.5, pool=None),
+    # the same beam search over long prompts, whose shared blocks no cache holds
+    "beam_long": dict(id=9, kind="beam", B=32, beams=4, ctx=(16384, 32768), Hq=16, Hkv=8, D=128,
+                      dtype="bf16", value_scale=0.5, pool=None),
     # the prompts of prefill_prefix (same seeds, same draws), stored by the quantising store into
     # int8 caches; dtype is that of the new rows
     "int8_store": dict(id=3, kind="store", B=32, ctx=(100, 1024), Hq=16, Hkv=8, D=128,
