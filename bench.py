@@ -88,8 +88,8 @@ def log(*a):
 
 # ------------------------------------------------------------------------------------ profiles
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = {"decode_split_kernel": "decode.hip", "prefill_kernel": "prefill.hip", "kv_store_kernel": "kv_store.hip",
-                  "kv_store_quant_kernel": "kv_store.hip"}
+KERNEL_SOURCES = {"decode_split_kernel": "decode.hip", "decode_group_kernel": "decode.hip", "prefill_kernel": "prefill.hip",
+                  "kv_store_kernel": "kv_store.hip", "kv_store_quant_kernel": "kv_store.hip"}
 
 
 def source_hash(kernel):
@@ -149,7 +149,7 @@ def summarize(name, prof_dir, cmd, workload=None):
                 out.append(f"DERIVED {kern}: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f} VALU and "
                            f"{avg.get('SQ_INSTS_LDS', 0) / avg['SQ_INSTS_MFMA']:.2f} LDS instructions per MFMA; "
                            f"LDS bank conflicts {avg.get('SQ_LDS_BANK_CONFLICT', 0):.0f}")
-        for kern in ("decode_split_kernel", "prefill_kernel", "kv_store_quant_kernel"):  # the dominant kernels
+        for kern in ("decode_split_kernel", "decode_group_kernel", "prefill_kernel", "kv_store_quant_kernel"):
             f = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "FETCH_SIZE"]
             w = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "WRITE_SIZE"]
             if f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
@@ -776,8 +776,10 @@ def bench_beam(args, cfg):
         copy=dict(bound="hbm", achieved=copy_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=copy_gbs / HBM_PEAK_GBS,
                   bytes_per_step=copy_bytes),
         roofline=dict(bound="hbm", achieved=uniq_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=uniq_gbs / HBM_PEAK_GBS,
-                      traffic=None, kernel=("grouped decode over each request's beams" if all(log_grouped) else
-                                            "decode over every beam's context") + " (bytes: distinct blocks once)",
+                      traffic=stored_traffic("decode_group_kernel" if all(log_grouped) else "decode_split_kernel",
+                                             cfg["name"]),
+                      kernel=("grouped decode over each request's beams" if all(log_grouped) else
+                              "decode over every beam's context") + " (bytes: distinct blocks once)",
                       bytes_per_launch=uniq_bytes),
         cpu_baseline=cpu,
     )

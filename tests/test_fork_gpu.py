@@ -268,6 +268,38 @@ def test_decode_batch_with_copy_on_write(gpu, fused):
         both.check_caches(f"fused={fused} step {step}")
 
 
+@pytest.mark.parametrize("min_shared", [0, 1 << 30])
+def test_decode_batch_grouped(gpu, min_shared):
+    """DecodeBatch with group_size: two requests of two beams each, steps with copy-on-write and a
+    re-fork; min_shared 0 takes the grouped kernel every step, a huge one the per-sequence one."""
+    both = Both("bf16", gpu, seed=13)
+    rnd = np.random.default_rng(8)
+    both.add(0, rnd.integers(0, 1000, size=700).tolist())
+    both.add(1, rnd.integers(0, 1000, size=511).tolist())
+    both.fork(0, 1000)
+    both.fork(1, 1001)
+    ids = [0, 1000, 1, 1001]
+    batch = R.DecodeBatch(both.kv, HQ, ids, 800, cow=True, group_size=2, group_min_shared=min_shared)
+    for step in range(4):
+        if step == 2:  # the second beam of request 0 is replaced by a fork of the first
+            both.free(1000)
+            both.fork(0, 1002)
+            ids = [0, 1002, 1, 1001]
+            batch.set_sequences(ids)
+        toks = both.rng.integers(0, 1000, size=len(ids)).tolist()
+        slots, src, dst, _ = both.oracle_append(ids, toks)
+        rows = [both._rows(slots) for _ in range(2)]
+        both.oc = list(OT.kv_store(*both.oc, rows[0][0], rows[1][0], slots))
+        bits = W.f32_to_bf16_bits(both.rng.standard_normal((len(ids), HQ, D)).astype(np.float32))
+        out = batch.step(toks, R.bf16_tensor(bits, gpu), rows[0][1], rows[1][1], SCALE)
+        assert batch.grouped == (min_shared == 0)
+        lens = [both.oa.seq_len(i) for i in ids]
+        ref = OT.decode(W.bf16_bits_to_f32(bits), *both.oc[:2], both.oa.block_tables(ids, 4), lens, SCALE)
+        say(f"  min_shared={min_shared} step {step}: shared {batch.host_shared_lens.tolist()}, lengths {lens}")
+        check_tol(out.float().cpu().numpy().astype(np.float64), ref, "bf16", f"grouped batch step {step}")
+        both.check_caches(f"grouped batch step {step}")
+
+
 @pytest.mark.parametrize("dtype,hkv,d", [(P.F32, 1, 64), (P.BF16, 8, 128), (P.BF16, 3, 64), (P.I8, 2, 128),
                                           (P.I8, 5, 64)])
 @pytest.mark.parametrize("with_rows", [True, False])
