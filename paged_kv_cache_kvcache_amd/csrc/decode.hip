@@ -625,19 +625,20 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
     }
 
     const size_t lane_off = size_t(r) * RB + size_t(c) * PB;
-    uint32_t kw[16][W], vw[16][W];
-    // One block: this wavefront's quarter of keys blk*256 .. blk*256 + 255 below ctx and from lo on,
-    // for the rows of member `only` (-1: every row).  Rows of other members take the block's work
-    // with every score masked, which leaves their state unchanged: skipping them instead made the
-    // compiler spill at eight rows.
-    auto attend_block = [&](int64_t phys, int blk, int ctx, int lo, int only) __attribute__((always_inline)) {
-        const int valid = min(kTile, ctx - (blk * pkv::kBlock + w * kTile));
-        const char* kp = a.k_cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
-        const char* vp = a.v_cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
+    // One block of this wavefront's walk: its quarter of keys blk*256 .. blk*256 + 255 below ctx and
+    // from lo on, for the rows of member `only` (-1: every row).
+    struct Unit {
+        int64_t phys;
+        int blk, ctx, lo, only;
+        bool ok;
+    };
+    auto load_unit = [&](const Unit& u, uint32_t (&kw)[16][W], uint32_t (&vw)[16][W]) __attribute__((always_inline)) {
+        const int valid = min(kTile, u.ctx - (u.blk * pkv::kBlock + w * kTile));
+        const size_t tile = ((size_t(u.phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (4 * i + r < valid) {
-                load_piece<W>(kp + size_t(4 * i) * RB, kw[i]);
+                load_piece<W>(a.k_cache + tile + size_t(4 * i) * RB, kw[i]);
             } else {
 #pragma unroll
                 for (int k = 0; k < W; ++k) kw[i][k] = 0u;
@@ -646,18 +647,26 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (4 * i + r < valid) {
-                load_piece<W>(vp + size_t(4 * i) * RB, vw[i]);
+                load_piece<W>(a.v_cache + tile + size_t(4 * i) * RB, vw[i]);
             } else {
 #pragma unroll
                 for (int k = 0; k < W; ++k) vw[i][k] = 0u;
             }
         }
+    };
+    // Rows of other members take the block's work with every score masked, which leaves their state
+    // unchanged: skipping them instead made the compiler spill at eight rows.
+    auto attend_unit = [&](const Unit& u, const uint32_t (&kw)[16][W], const uint32_t (&vw)[16][W])
+        __attribute__((always_inline)) {
+        const int64_t phys = u.phys;
+        const int only = u.only;
+        const int valid = min(kTile, u.ctx - (u.blk * pkv::kBlock + w * kTile));
         float ks = a.scale_log2, vs = 1.f;
         if constexpr (DT == PKV_I8) {
             ks *= a.k_scale[phys * a.num_kv_heads + g];
             vs = a.v_scale[phys * a.num_kv_heads + g];
         }
-        const bool row_ok = 4 * c + r < valid && blk * pkv::kBlock + w * kTile + 4 * c + r >= lo;
+        const bool row_ok = 4 * c + r < valid && u.blk * pkv::kBlock + w * kTile + 4 * c + r >= u.lo;
         float p[GM];
 #pragma unroll
         for (int j = 0; j < GM; ++j) {
@@ -708,42 +717,71 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
         }
     };
 
-    // ---- one walk over this wavefront's blocks (one call site keeps the register allocation that
-    // of one loop): first the shared keys 0 .. shared-1 from member 0's table (64 entries per
-    // VGPR, by readlane), then each member's own keys shared .. ctx-1 (a few blocks, one scalar
-    // load each)
+    // ---- one walk over this wavefront's blocks: first the shared keys 0 .. shared-1 from member
+    // 0's table (64 entries per VGPR, by readlane), then each member's own keys shared .. ctx-1 (a
+    // few blocks, one scalar load each)
     const int32_t* bt0 = a.block_tables + size_t(b0) * a.max_blocks;
     const int nsh = (shared + pkv::kBlock - 1) / pkv::kBlock;
-    const int n_shared = min(nsh, max(0, (shared - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
     const int first = shared / pkv::kBlock;
     int bt_win = 0;
     int btv = lane < nsh ? bt0[lane] : 0;
-    int mm = -1, blk = 0, blk_end = n_shared, ctx = shared, lo = 0;
+    int mm = -1, nblk = 0, blk_end = min(nsh, max(0, (shared - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
+    int wctx = shared, wlo = 0;
     const int32_t* bt = bt0;
-    while (true) {
-        if (blk >= blk_end) {  // next member with blocks for this wavefront
-            if (++mm >= M) break;
-            ctx = a.context_lens[b0 + mm];
+    auto next_unit = [&]() __attribute__((always_inline)) {
+        Unit u{0, 0, 0, 0, 0, false};
+        while (nblk >= blk_end) {  // next member with blocks for this wavefront
+            if (mm + 1 >= M) return u;
+            ++mm;
+            wctx = a.context_lens[b0 + mm];
             bt = a.block_tables + size_t(b0 + mm) * a.max_blocks;
-            blk = first;
-            blk_end = min((ctx + pkv::kBlock - 1) / pkv::kBlock, max(first, (ctx - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
-            lo = shared;
-            continue;
+            nblk = first;
+            blk_end = min((wctx + pkv::kBlock - 1) / pkv::kBlock,
+                          max(first, (wctx - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
+            wlo = shared;
         }
-        int64_t phys;
         if (mm < 0) {
-            const int win = blk >> 6;
+            const int win = nblk >> 6;
             if (win != bt_win) {
                 bt_win = win;
                 const int e = 64 * win + lane;
                 btv = e < nsh ? bt0[e] : 0;
             }
-            phys = __builtin_amdgcn_readlane(btv, blk & 63);
+            u.phys = __builtin_amdgcn_readlane(btv, nblk & 63);
         } else {
-            phys = __builtin_amdgcn_readfirstlane(bt[blk]);
+            u.phys = __builtin_amdgcn_readfirstlane(bt[nblk]);
         }
-        attend_block(phys, blk, ctx, lo, mm);
-        ++blk;
+        u.blk = nblk++;
+        u.ctx = wctx;
+        u.lo = wlo;
+        u.only = mm;
+        u.ok = true;
+        return u;
+    };
+    // The next block's K/V loads are issued before this block's arithmetic, so they overlap it:
+    // with at most eight rows per group, one workgroup per (group, KV head) often leaves a single
+    // wavefront per SIMD, and nothing else would hide the load latency.  Two buffers fit below the
+    // register file when a lane's piece of a row is at most 4 dwords.
+    constexpr bool kDouble = W <= 4;
+    uint32_t ka[16][W], va[16][W];
+    Unit cur = next_unit();
+    if constexpr (kDouble) {
+        uint32_t kb[16][W], vb[16][W];
+        if (cur.ok) load_unit(cur, ka, va);
+        while (cur.ok) {
+            const Unit nxt = next_unit();
+            if (nxt.ok) load_unit(nxt, kb, vb);
+            attend_unit(cur, ka, va);
+            if (!nxt.ok) break;
+            cur = next_unit();
+            if (cur.ok) load_unit(cur, ka, va);
+            attend_unit(nxt, kb, vb);
+        }
+    } else {
+        for (; cur.ok; cur = next_unit()) {
+            load_unit(cur, ka, va);
+            attend_unit(cur, ka, va);
+        }
     }
 
     // ---- merge the four lane groups of each wavefront, then the four wavefronts through LDS
