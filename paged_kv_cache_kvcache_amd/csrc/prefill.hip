@@ -141,6 +141,18 @@ __device__ __forceinline__ void dma16(const char* src, char* lds_dst) {
 // every DMA this wavefront issued has landed in LDS (vmcnt(0); expcnt and lgkmcnt left alone)
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// v_permlane32_swap exchanges the upper half of one operand with the lower half of the other;
+// swapping v with itself leaves every lane holding its own value and that of lane ^ 32.  It does
+// not go through the LDS queue, so (unlike a bpermute) it does not wait for LDS reads in flight.
+__device__ __forceinline__ float max_across_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // NW = wavefronts per workgroup (4 or 8): all of them share each staged K/V tile.
 template <int D, int G, int NW, bool CHECK>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(PrefillArgs a) {
@@ -180,9 +192,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
                 return;
             }
         }
-        nq = a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b];
     }
-    for (int r = 0; b < 0; ++r) {
+    for (int r = 0; b < 0 && a.items == nullptr; ++r) {
         int live = 0;
         for (int s = 0; s < a.B; ++s) {
             const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
@@ -202,12 +213,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     }
     if (b < 0) return;
 
+    // The sequence's lengths and the first window of its block table (below) are requested
+    // together, so that a workgroup's start waits for one memory round trip after its work item.
+    const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    int btv = lane < a.max_blocks ? bt[lane] : 0;
     const int Lk = a.seqlens_k[b];
+    const int qrow0 = a.cu_seqlens_q[b];
+    if (a.items != nullptr) nq = a.cu_seqlens_q[b + 1] - qrow0;
     if (CHECK && (Lk < 0 || Lk > int64_t(a.max_blocks) * pkv::kBlock || (a.causal && Lk < nq))) {
         if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrLength, b, Lk);
         return;
     }
-    const int qrow0 = a.cu_seqlens_q[b];
     const int q0 = tile * QT;
     const int nqt = min(QT, nq - q0);
     const int pos0 = Lk - nq + q0;  // absolute position of token q0
@@ -217,41 +234,30 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         return;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
     const int rho = 32 * w + col;
     const int j = rho / QT, t = rho % QT;
     const bool col_ok = t < nqt;
-    const int P = a.causal ? min(pos0 + t, kv_len - 1) : kv_len - 1;  // last key this column sees
-    // last key any column of this wavefront sees (tiles past it are skipped) and the last key every
-    // column sees (tiles up to it need no mask)
-    int pw = P, pm = P;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        pw = max(pw, __shfl_xor(pw, o, 64));
-        pm = min(pm, __shfl_xor(pm, o, 64));
-    }
-    const int pw_max = __builtin_amdgcn_readfirstlane(pw);
-    const int pw_min = __builtin_amdgcn_readfirstlane(pm);
-    // sliding window: the first key this column sees; over the wavefront the smallest (tiles below
-    // it are skipped) and the largest (tiles from it on need no lower mask).  The workgroup's first
-    // tile holds the first key of its first token.
-    const int Lo = a.window > 0 ? max(0, P - a.window + 1) : 0;
-    int lw = Lo, lm = Lo;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        lw = min(lw, __shfl_xor(lw, o, 64));
-        lm = max(lm, __shfl_xor(lm, o, 64));
-    }
-    const int lw_min = __builtin_amdgcn_readfirstlane(lw);
-    const int lw_max = __builtin_amdgcn_readfirstlane(lm);
+    // last key the column of token t sees (non-decreasing in t)
+    auto last_key = [&](int tt) { return a.causal ? min(pos0 + tt, kv_len - 1) : kv_len - 1; };
+    // first key the column whose last key is p sees, under a sliding window (non-decreasing in p)
+    auto first_key = [&](int p) { return a.window > 0 ? max(0, p - a.window + 1) : 0; };
+    const int P = last_key(t), Lo = first_key(P);
+    // The wavefront's columns hold tokens t_lo..t_hi of the tile: 32 consecutive tokens of one
+    // head when a tile has 32 or more tokens, else every token of the tile.  Both key bounds are
+    // monotone in t, so their extremes over the wavefront come from its end tokens: the last key
+    // any column sees (tiles past it are skipped), the last key every column sees (tiles up to it
+    // need no mask), and the same pair for the first keys of a sliding window (tiles wholly below
+    // the smallest are skipped, tiles from the largest on need no lower mask).
+    const int t_lo = QT >= 32 ? (32 * w) % QT : 0, t_hi = QT >= 32 ? t_lo + 31 : QT - 1;
+    const int pw_max = last_key(t_hi), pw_min = last_key(t_lo);
+    const int lw_min = first_key(pw_min), lw_max = first_key(pw_max);
+    // the workgroup's first tile holds the first key of its first token
     const int kt0 = a.window > 0 ? max(0, pos0 - a.window + 1) / kKT : 0;
 
     // ---- this sequence's block table, 64 entries at a time: lane i holds entry 64 win + i, and a
-    // tile reads its physical block with readlane (no memory access per tile).  The first window
-    // is requested here, ahead of the Q loads, so the two latencies overlap.
-    const int32_t* bt = a.block_tables + size_t(b) * a.max_blocks;
+    // tile reads its physical block with readlane (no memory access per tile).  btv, requested
+    // above, holds the first window.
     int bt_win = 0;
-    int btv = lane < a.max_blocks ? bt[lane] : 0;
     auto phys_block = [&](int blk) {  // blk is uniform
         const int win = blk >> 6;
         if (win != bt_win) {  // a new window every 16384 keys
@@ -394,12 +400,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         // mask (diagonal and window-edge tiles only) and tile max
         float tmax = kNegInf;
         if (kt * kKT + kKT - 1 > pw_min || kt * kKT < lw_max) {
+            const uint32_t span = uint32_t(P - Lo);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = kt * kKT + 32 * mt + 8 * (i / 4) + 4 * h + (i % 4);
-                    s[mt][i] = key <= P && key >= Lo ? s[mt][i] : kNegInf;
+                    // key kt*64 + 4h + c (c = 32mt + 8(i/4) + i%4) is visible when Lo <= key <= P:
+                    // one unsigned comparison of key - Lo against P - Lo
+                    const uint32_t rel = uint32_t(kt * kKT + 4 * h - Lo + 32 * mt + 8 * (i / 4) + (i % 4));
+                    s[mt][i] = rel <= span ? s[mt][i] : kNegInf;
                     tmax = fmaxf(tmax, s[mt][i]);
                 }
         } else {
@@ -408,7 +417,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mt][i]);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = max_across_halves(tmax);
         // Lazy rescaling: the running max only moves on a column's first tile or when its max grew
         // by more than 2^8, so most tiles skip rescaling O and take p = exp2(s) directly;
         // probabilities then stay below 2^8, well inside bf16.
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     }
 
     // ---- normalise and write this column's row: d = 32dt + 8(i/4) + 4h + i%4
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = sum_across_halves(l_run);
     if (!col_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = a.out + (size_t(qrow0 + q0 + t) * a.num_q_heads + g * G + j) * D + 4 * h;
