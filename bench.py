@@ -57,6 +57,8 @@ def parse():
                     help="sliding-window attention: each query attends its last W keys (0: every key)")
     ap.add_argument("--fused", action="store_true",
                     help="decode: store the new tokens inside the attention launch (pkv_decode_store_attend)")
+    ap.add_argument("--unsplit", action="store_true",
+                    help="prefill: keep every work item whole (no key-range split of launches that leave CUs idle)")
     ap.add_argument("--ungrouped", action="store_true",
                     help="beam workloads: attend every beam on its own (pkv_paged_attn_decode); by default a "
                          "step whose requests share at least runner.GROUP_MIN_SHARED keys on average reads "
@@ -89,7 +91,7 @@ def log(*a):
 # ------------------------------------------------------------------------------------ profiles
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {"decode_split_kernel": "decode.hip", "decode_group_kernel": "decode.hip", "prefill_kernel": "prefill.hip",
-                  "kv_store_kernel": "kv_store.hip", "kv_store_quant_kernel": "kv_store.hip"}
+                  "prefill_merge_kernel": "prefill.hip", "kv_store_kernel": "kv_store.hip", "kv_store_quant_kernel": "kv_store.hip"}
 
 
 def source_hash(kernel):
@@ -149,7 +151,8 @@ def summarize(name, prof_dir, cmd, workload=None):
                 out.append(f"DERIVED {kern}: {avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f} VALU and "
                            f"{avg.get('SQ_INSTS_LDS', 0) / avg['SQ_INSTS_MFMA']:.2f} LDS instructions per MFMA; "
                            f"LDS bank conflicts {avg.get('SQ_LDS_BANK_CONFLICT', 0):.0f}")
-        for kern in ("decode_split_kernel", "decode_group_kernel", "prefill_kernel", "kv_store_quant_kernel"):
+        for kern in ("decode_split_kernel", "decode_group_kernel", "prefill_kernel", "prefill_merge_kernel",
+                     "kv_store_quant_kernel"):
             f = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "FETCH_SIZE"]
             w = [sum(v) / len(v) for (run, k, c), v in counters.items() if kern in k and c == "WRITE_SIZE"]
             if f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
@@ -439,7 +442,8 @@ def bench_prefill(args, cfg, wl=None, cpu=None):
     """The chunked prefill workload on the GPU (``wl``, ``cpu`` as in :func:`bench_decode`)."""
     import torch
     import workloads as W
-    from paged_kv_cache_kvcache_amd import BF16, desc_of, kv_store, paged_attn_prefill_ordered, prefill_work_order
+    from paged_kv_cache_kvcache_amd import (BF16, desc_of, kv_store, paged_attn_prefill_split, prefill_split_order,
+                                            prefill_split_workspace_bytes, prefill_work_order)
     from paged_kv_cache_kvcache_amd import runner as R
 
     dev = torch.device("cuda:0")
@@ -466,19 +470,27 @@ def bench_prefill(args, cfg, wl=None, cpu=None):
         tab, lens = kv.alloc.block_tables(ids, wl["num_blocks"])  # whole sequences, later segments included
         mb = max(1, -(-int(lens.max()) // 256))
         tab = np.ascontiguousarray(tab[:, :mb])
-        # the chunk's work items, heaviest first in CU-balanced rounds (pkv_prefill_work_order)
-        items, tile_rows = prefill_work_order(desc_of(kv.k_cache), Hq, cu, lk, True, args.window)
-        metas.append((cu, lk, slots, tab, mb, (items, tile_rows)))
+        # the chunk's work items, heaviest first in CU-balanced rounds, long ones cut into key-range
+        # pieces when the launch would leave CUs idle (pkv_prefill_split_order)
+        split = prefill_split_order(desc_of(kv.k_cache), Hq, cu, lk, True, args.window)
+        if args.unsplit:  # the same work order with every item whole
+            items, rows = prefill_work_order(desc_of(kv.k_cache), Hq, cu, lk, True, args.window)
+            whole = np.stack([items, np.zeros_like(items), np.full_like(items, 2**31 - 1), np.full_like(items, -1)], 1)
+            split = (whole, np.zeros((0, 4), np.int32), 0, rows)
+        metas.append((cu, lk, slots, tab, mb, split))
     host_s = time.perf_counter() - t0
     # device-resident inputs of every chunk
     dchunks, flops = [], 0
-    for ch, (cu, lk, slots, tab, mb, items) in zip(chunks, metas):
+    ws_bytes = max(prefill_split_workspace_bytes(desc_of(kv.k_cache), Hq, m[5][2], m[5][3]) for m in metas)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    for ch, (cu, lk, slots, tab, mb, split) in zip(chunks, metas):
         dv = lambda key: R.bf16_tensor(np.concatenate([prompts[i][key][ncached[i] + a:ncached[i] + b]
                                                        for i, a, b in ch]), dev)
         q, k, v = dv("q"), dv("k"), dv("v")
         to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         dchunks.append(dict(q=q, k=k, v=v, cu=to(cu), lk=to(lk), slots=to(slots), tab=to(tab).view(len(ch), mb),
-                            items=to(items[0]), tile_rows=items[1], max_q=int(np.diff(cu).max()), max_k=int(lk.max()),
+                            pieces=to(split[0]), merges=to(split[1]), n_slots=split[2], tile_rows=split[3],
+                            max_q=int(np.diff(cu).max()), max_k=int(lk.max()),
                             out=torch.empty_like(q)))
         for b in range(len(ch)):
             nq, L = int(cu[b + 1] - cu[b]), int(lk[b])
@@ -500,9 +512,9 @@ def bench_prefill(args, cfg, wl=None, cpu=None):
             kv_store(d["k"], d["v"], d["slots"], kv.k_cache, kv.v_cache)
             if timed is not None:
                 ev[timed][c][0].record(stream)
-            paged_attn_prefill_ordered(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache,
-                                       d["tab"], scale, d["items"], d["tile_rows"], True, args.window,
-                                       out=d["out"])
+            paged_attn_prefill_split(d["q"], d["cu"], d["lk"], d["max_q"], d["max_k"], kv.k_cache, kv.v_cache,
+                                     d["tab"], scale, d["pieces"], d["merges"], d["n_slots"], d["tile_rows"],
+                                     workspace, True, args.window, out=d["out"])
             if timed is not None:
                 ev[timed][c][1].record(stream)
 
@@ -527,9 +539,15 @@ def bench_prefill(args, cfg, wl=None, cpu=None):
     total_new = sum(n_new)
     log(f"[bench] prefill {nch} chunks, {total_new} new tokens, {flops / 1e9:.2f} GFLOP; prefill kernels "
         f"{kern_s * 1e6:.1f} us/step -> {tflops:.1f} TFLOP/s; step {elapsed / args.steps * 1e3:.3f} ms")
-    # counter traffic of one step (mean per dispatch x chunks), when taken on this workload and the
-    # current kernel source
-    traffic = stored_traffic("prefill_kernel", cfg["name"], nch) if args.seed == 0 and args.window == 0 else None
+    # counter traffic of one step (mean per dispatch x dispatches: one attention launch per chunk,
+    # one merge per chunk with split items), when taken on this workload and the current source
+    traffic = None
+    if args.seed == 0 and args.window == 0:
+        n_merge = sum(1 for d in dchunks if d["n_slots"] > 0)
+        traffic = stored_traffic("prefill_kernel", cfg["name"], nch)
+        if traffic is not None and n_merge:
+            merge = stored_traffic("prefill_merge_kernel", cfg["name"], n_merge)
+            traffic = None if merge is None else traffic + merge
     res = dict(
         metric="paged decode tokens/s + KV HBM GB/s (% of peak); prefill TFLOP/s",
         value=total_new * args.steps / elapsed, unit="prefill tokens/s", n_gpus=1, steps=args.steps,
@@ -539,7 +557,7 @@ def bench_prefill(args, cfg, wl=None, cpu=None):
                     shared_prefix=cfg["shared"], group=cfg["group"], chunk_tokens=cfg["chunk"], window=args.window,
                     q_heads=Hq,
                     kv_heads=Hkv, head_dim=D, block_size=256, chunks=nch, new_tokens=total_new,
-                    cached_tokens=sum(ncached), seed=args.seed),
+                    cached_tokens=sum(ncached), split_underfilled=not args.unsplit, seed=args.seed),
         prefill_kernel_us=kern_s * 1e6, prefill_tflops=tflops, host_admit_us=host_s * 1e6,
         roofline=dict(bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=tflops / BF16_PEAK_TFLOPS, traffic=traffic, kernel="prefill (all chunks of one step)",

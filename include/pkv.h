@@ -503,6 +503,64 @@ int pkv_paged_attn_prefill_ordered(const pkv_cache_desc* desc, const void* q, in
 int pkv_prefill_tile_rows(const pkv_cache_desc* desc, int32_t Hq, int32_t B, int32_t total_q,
                           int32_t* tile_rows);
 
+/* Split-K prefill for launches that leave CUs idle.  The pages cap a step at a budget of new
+ * tokens ("Nano-vLLM性能调优实战", §3.2 关键调度参数), so a chunk can hold few prompts; with
+ * fewer workgroups than the device has CUs, the launch lasts as long as its longest item (the
+ * last query tile of its longest prompt, which walks every key tile alone).  As decode splits its
+ * context, such a launch splits the key range of long items into pieces, each run by its own
+ * workgroups and kept as a partial state (output and row sum relative to the running maximum),
+ * and a second launch merges each item's pieces by log-sum-exp (the full-computation phase's
+ * FlashAttention-2 style attention, intelliparadigm.com Nano-vLLM article, §7.2 关键优化点).
+ *
+ * pkv_prefill_split_order: host-only, nothing is launched.  Inputs as pkv_prefill_work_order.
+ * When the launch has at least as many workgroups (items x num_kv_heads) as the device has CUs,
+ * no item is split: the pieces are the items of pkv_prefill_work_order, in its order, and there
+ * are no merges.  Otherwise every item longer than T key tiles is cut into up to 8 pieces of
+ * nearly equal length, T being the smallest value from 4 up that keeps the launch within one
+ * workgroup per CU (two workgroups sharing a CU each take more than twice as long per key tile as
+ * one alone).  Outputs:
+ *   - pieces (host int32[pieces_capacity][4]), *n_pieces records {(sequence << 16) | query tile,
+ *     first key tile, end key tile, slot}: a piece walks key tiles first .. end-1 of its item
+ *     (0 .. INT32_MAX: all of them) and, with slot >= 0, writes its partial state to that slot;
+ *     heaviest first in rounds as pkv_prefill_work_order orders items;
+ *   - merges (host int32[merges_capacity][4]), *n_merges records {(sequence << 16) | query tile,
+ *     first slot, pieces, 0}: the pieces of a split item hold consecutive slots;
+ *   - *n_slots partial slots, *tile_rows tokens per query tile.
+ * Errors as pkv_prefill_work_order; PKV_ERR_SMALL_BUFFER when either list exceeds its capacity
+ * ((total new tokens + B) x 8 pieces and (total new tokens + B) merges always suffice).
+ *
+ * pkv_prefill_split_workspace_bytes: the workspace that n_slots slots need (0 for bad arguments):
+ * n_slots x num_kv_heads x (head_dim + 4) x tile_rows x (Hq / num_kv_heads) floats.
+ *
+ * pkv_paged_attn_prefill_split: pkv_paged_attn_prefill_ordered over the pieces (device
+ * int32[n_pieces][4]) and then, when n_merges > 0, the merge of the split items (device
+ * int32[n_merges][4]), both enqueued on `stream`.  workspace: caller-owned device memory of at
+ * least pkv_prefill_split_workspace_bytes(desc, Hq, n_slots, tile_rows) bytes, 16-byte aligned,
+ * needed only when n_slots > 0; its contents before the call do not matter, and it must stay
+ * alive until the stream has passed the merge.  The lists, n_slots and tile_rows must be what
+ * pkv_prefill_split_order gave for the same cu_seqlens_q, seqlens_k, shapes and device; unsplit
+ * items give bitwise the outputs of pkv_paged_attn_prefill_ordered, split items the same
+ * attention within rounding.  Errors: those of the ordered call; a workspace too small:
+ * PKV_ERR_SMALL_BUFFER; n_merges and n_slots not both zero or both positive: PKV_ERR_INVALID.
+ * With device-data checks on, a piece or merge record outside the call's sequences, tiles or
+ * slots is recorded as error 5 (where = its index, value = its first field). */
+int pkv_prefill_split_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                            const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
+                            int32_t window, int32_t* pieces, int32_t pieces_capacity,
+                            int32_t* n_pieces, int32_t* merges, int32_t merges_capacity,
+                            int32_t* n_merges, int32_t* n_slots, int32_t* tile_rows);
+size_t pkv_prefill_split_workspace_bytes(const pkv_cache_desc* desc, int32_t Hq, int32_t n_slots,
+                                         int32_t tile_rows);
+int pkv_paged_attn_prefill_split(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                 int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks,
+                                 float softmax_scale, int32_t causal, int32_t window,
+                                 const int32_t* pieces, int32_t n_pieces, const int32_t* merges,
+                                 int32_t n_merges, int32_t n_slots, int32_t tile_rows,
+                                 void* workspace, size_t workspace_bytes, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -90,6 +90,12 @@ SIGNATURES = {
                                               _i32, _f32, _i32, _i32, _vp, _i32, _i32, _vp, _vp]),
     "pkv_prefill_tile_rows": (_i32, [_pdesc, _i32, _i32, _i32, _p32]),
     "pkv_prefill_work_order": (_i32, [_pdesc, _i32, _i32, _p32, _p32, _i32, _i32, _p32, _i32, _p32, _p32]),
+    "pkv_prefill_split_order": (_i32, [_pdesc, _i32, _i32, _p32, _p32, _i32, _i32, _p32, _i32, _p32, _p32, _i32,
+                                       _p32, _p32, _p32]),
+    "pkv_prefill_split_workspace_bytes": (_sz, [_pdesc, _i32, _i32, _i32]),
+    "pkv_paged_attn_prefill_split": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                            _i32, _f32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _sz,
+                                            _vp, _vp]),
 }
 
 _lib = None
@@ -523,6 +529,52 @@ def paged_attn_prefill_ordered(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seq
         int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         int(block_tables.shape[1]), float(softmax_scale), int(bool(causal)), int(window), _ptr(work_items),
         int(work_items.shape[0]), int(tile_rows), _ptr(out), _stream(stream)), "pkv_paged_attn_prefill_ordered")
+    return out
+
+
+def prefill_split_order(desc, Hq, cu_seqlens_q, seqlens_k, causal=True, window=0):
+    """pkv_prefill_split_order: (pieces int32[n][4], merges int32[m][4], n_slots, tile_rows), host
+    arrays; a launch that fills the device gets its work items unsplit and no merges."""
+    import numpy as np
+    cu, pcu = _host_i32(cu_seqlens_q)
+    lk, plk = _host_i32(seqlens_k)
+    B = len(lk)
+    if len(cu) != B + 1:
+        raise ValueError("cu_seqlens_q must have B + 1 entries")
+    items = int(cu[-1]) + B if B else 0
+    pieces = np.empty((max(8 * items, 1), 4), dtype=np.int32)
+    merges = np.empty((max(items, 1), 4), dtype=np.int32)
+    n, m, slots, rows = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().pkv_prefill_split_order(ctypes.byref(desc), int(Hq), B, pcu, plk, int(bool(causal)), int(window),
+                                         pieces.ctypes.data_as(_p32), pieces.shape[0], ctypes.byref(n),
+                                         merges.ctypes.data_as(_p32), merges.shape[0], ctypes.byref(m),
+                                         ctypes.byref(slots), ctypes.byref(rows)), "pkv_prefill_split_order")
+    return pieces[:n.value], merges[:m.value], slots.value, rows.value
+
+
+def prefill_split_workspace_bytes(desc, Hq, n_slots, tile_rows):
+    """pkv_prefill_split_workspace_bytes: the workspace of a split prefill call."""
+    return int(lib().pkv_prefill_split_workspace_bytes(ctypes.byref(desc), int(Hq), int(n_slots), int(tile_rows)))
+
+
+def paged_attn_prefill_split(q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache, block_tables,
+                             softmax_scale, pieces, merges, n_slots, tile_rows, workspace=None, causal=True, window=0,
+                             out=None, stream=None):
+    """Split-K varlen prefill over ``pieces`` (device int32[n][4]) then the merge of ``merges``
+    (device int32[m][4]), as :func:`prefill_split_order` gives them; ``workspace`` (device memory,
+    e.g. a uint8 tensor) of at least :func:`prefill_split_workspace_bytes` bytes when n_slots > 0."""
+    desc = desc_of(k_cache)
+    total_q, Hq, _ = q.shape
+    B = int(seqlens_k.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_prefill_split(
+        ctypes.byref(desc), _ptr(q), int(Hq), _ptr(cu_seqlens_q), _ptr(seqlens_k), B, int(total_q),
+        int(max_seqlen_q), int(max_seqlen_k), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), float(softmax_scale), int(bool(causal)), int(window), _ptr(pieces),
+        int(pieces.shape[0]), _ptr(merges), int(merges.shape[0]), int(n_slots), int(tile_rows), _ptr(workspace),
+        wbytes, _ptr(out), _stream(stream)), "pkv_paged_attn_prefill_split")
     return out
 
 

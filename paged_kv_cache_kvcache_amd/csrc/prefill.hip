@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <vector>
 #include <cmath>
@@ -71,6 +72,11 @@ struct PrefillArgs {
     int32_t check;   // launch the instantiation that validates cu_seqlens_q, key lengths and block ids
     const int32_t* items;  // NULL: the built-in order; else item i = (sequence << 16) | query tile
     int32_t n_items;
+    // split launches: piece i = {(sequence << 16) | query tile, first key tile, end key tile, slot}
+    // (items == NULL); a piece with slot >= 0 writes its partial state to slot `slot` of `part`
+    const int4* pieces;
+    float* part;
+    int32_t n_slots;
 };
 
 // Device-data checks (uniform in the workgroup, so a workgroup that fails leaves as a whole).
@@ -180,7 +186,24 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     const int g = blockIdx.x % a.num_kv_heads;
     int item = blockIdx.x / a.num_kv_heads;
     int b = -1, tile = 0, nq = 0;
-    if (a.items != nullptr) {  // the caller's order (the grid has exactly n_items x Hkv workgroups)
+    int kt_begin = 0, kt_end = INT_MAX, slot = -1;  // the key tiles this workgroup walks, its partial slot
+    if (a.pieces != nullptr) {  // a split launch (the grid has exactly n_items x Hkv workgroups)
+        const int4 pc = a.pieces[item];
+        b = pc.x >> 16;
+        tile = pc.x & 0xffff;
+        kt_begin = pc.y;
+        kt_end = pc.z;
+        slot = pc.w;
+        if (CHECK) {
+            const bool seq_ok = pc.x >= 0 && b < a.B;
+            const int n = seq_ok ? a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b] : 0;
+            if (!seq_ok || tile >= (n + QT - 1) / QT || kt_begin < 0 || kt_end < kt_begin || slot < -1 ||
+                slot >= a.n_slots) {
+                if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrRun, item, pc.x);
+                return;
+            }
+        }
+    } else if (a.items != nullptr) {  // the caller's order (the grid has exactly n_items x Hkv workgroups)
         const int it = a.items[item];
         b = it >> 16;
         tile = it & 0xffff;
@@ -193,7 +216,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
             }
         }
     }
-    for (int r = 0; b < 0 && a.items == nullptr; ++r) {
+    for (int r = 0; b < 0 && a.items == nullptr && a.pieces == nullptr; ++r) {
         int live = 0;
         for (int s = 0; s < a.B; ++s) {
             const int n = a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s];
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     int btv = lane < a.max_blocks ? bt[lane] : 0;
     const int Lk = a.seqlens_k[b];
     const int qrow0 = a.cu_seqlens_q[b];
-    if (a.items != nullptr) nq = a.cu_seqlens_q[b + 1] - qrow0;
+    if (a.items != nullptr || a.pieces != nullptr) nq = a.cu_seqlens_q[b + 1] - qrow0;
     if (CHECK && (Lk < 0 || Lk > int64_t(a.max_blocks) * pkv::kBlock || (a.causal && Lk < nq))) {
         if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrLength, b, Lk);
         return;
@@ -251,8 +274,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
     const int t_lo = QT >= 32 ? (32 * w) % QT : 0, t_hi = QT >= 32 ? t_lo + 31 : QT - 1;
     const int pw_max = last_key(t_hi), pw_min = last_key(t_lo);
     const int lw_min = first_key(pw_min), lw_max = first_key(pw_max);
-    // the workgroup's first tile holds the first key of its first token
+    // the workgroup's first tile holds the first key of its first token; a piece walks its own
+    // range of those tiles
     const int kt0 = a.window > 0 ? max(0, pos0 - a.window + 1) / kKT : 0;
+    const int kt_lo = max(kt0, kt_begin), kt_hi = min(ntiles, kt_end);
 
     // ---- this sequence's block table, 64 entries at a time: lane i holds entry 64 win + i, and a
     // tile reads its physical block with readlane (no memory access per tile).  btv, requested
@@ -325,7 +350,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    if (kt0 < ntiles) dma(kt0, lds[0]);
+    if (kt_lo < kt_hi) dma(kt_lo, lds[0]);
 
     // ---- Q^T operand: column col = query row, 8 consecutive d per k-step.  Q is multiplied by
     // softmax_scale * log2(e) (fp32, rounded once to bf16), so S comes out in log2 units.  Loaded
@@ -353,7 +378,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
         constexpr int buf = decltype(stage)::value;
         wait_dma();
         __syncthreads();
-        if (kt + 1 < ntiles) dma(kt + 1, lds[buf ^ 1]);
+        if (kt + 1 < kt_hi) dma(kt + 1, lds[buf ^ 1]);
         // every key of this tile is masked for this wavefront (past its last key, or before its window)
         if (kt * kKT > pw_max || kt * kKT + kKT - 1 < lw_min) return;
 
@@ -464,13 +489,27 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
             }
         }
     };
-    for (int kt = kt0; kt < ntiles; kt += 2) {
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
         step(kt, std::integral_constant<int, 0>{});
-        if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
+        if (kt + 1 < kt_hi) step(kt + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- normalise and write this column's row: d = 32dt + 8(i/4) + 4h + i%4
     const float l_tot = sum_across_halves(l_run);
+    if (slot >= 0) {
+        // partial state of this piece, every row of the tile: O unnormalised and the row sum, both
+        // relative to 2^m_run (m_run in log2 units; -inf with l = 0 when no key was visible).  One
+        // record of D + 4 floats per row (O, m, l, padding), rows of a (slot, KV head) consecutive.
+        float* pr = a.part + ((size_t(slot) * a.num_kv_heads + g) * kRows + rho) * size_t(D + 4);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<float4*>(pr + 32 * dt + 8 * i4 + 4 * h) =
+                    make_float4(o[dt][4 * i4], o[dt][4 * i4 + 1], o[dt][4 * i4 + 2], o[dt][4 * i4 + 3]);
+        if (h == 0) *reinterpret_cast<float2*>(pr + D) = make_float2(m_run, l_tot);
+        return;
+    }
     if (!col_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = a.out + (size_t(qrow0 + q0 + t) * a.num_q_heads + g * G + j) * D + 4 * h;
@@ -483,6 +522,79 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void prefill_kernel(Prefi
             v.y = pack_bf16x2(o[dt][4 * i4 + 2] * inv, o[dt][4 * i4 + 3] * inv);
             *reinterpret_cast<uint2*>(op + 32 * dt + 8 * i4) = v;
         }
+}
+
+// ---- merge of a split launch's pieces: the pieces' partial states (O, l relative to 2^m) of each
+// row combine by log-sum-exp, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with
+// M = max_p m_p.
+constexpr int kMaxPieces = 8;  // pieces per split item
+
+struct MergeArgs {
+    const int4* merges;  // {(sequence << 16) | query tile, first slot, pieces, 0}
+    const float* part;
+    const int32_t* cu_seqlens_q;
+    uint16_t* out;
+    int32_t B;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t n_slots;
+    int32_t check;
+};
+
+// A (split item, KV head) takes kRows / (kMergeThreads / (D / 8)) workgroups, each a run of its
+// rows; a thread owns 8 consecutive d of one row, so the threads of a row read its pieces' records
+// and write its output row side by side.
+constexpr int kMergeThreads = 256;
+
+template <int D, int G, int NW>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(MergeArgs a) {
+    constexpr int kRows = kWaveRows * NW, QT = kRows / G;
+    constexpr int DC = D / 8, RPB = kMergeThreads / DC, PARTS = kRows / RPB;  // rows per workgroup, workgroups per tile
+    const int run = blockIdx.x % PARTS, gm = blockIdx.x / PARTS;
+    const int g = gm % a.num_kv_heads, mi = gm / a.num_kv_heads;
+    const int4 rec = a.merges[mi];
+    const int b = rec.x >> 16, tile = rec.x & 0xffff, s0 = rec.y, np = rec.z;
+    if (a.check) {  // uniform in the workgroup
+        const bool seq_ok = rec.x >= 0 && b < a.B;
+        const int n = seq_ok ? a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b] : 0;
+        if (!seq_ok || tile >= (n + QT - 1) / QT || np < 1 || np > kMaxPieces || s0 < 0 || s0 > a.n_slots - np) {
+            if (threadIdx.x == 0 && g == 0 && run == 0) record_error(pkv::kErrRun, mi, rec.x);
+            return;
+        }
+    }
+    const int rho = run * RPB + threadIdx.x / DC, dc = threadIdx.x % DC;
+    const int j = rho / QT, t = rho % QT;
+    const int q = tile * QT + t;
+    if (q >= a.cu_seqlens_q[b + 1] - a.cu_seqlens_q[b]) return;
+    constexpr size_t RS = D + 4;  // floats per row record
+    const float* p0 = a.part + ((size_t(s0) * a.num_kv_heads + g) * kRows + rho) * RS;
+    const size_t pstep = size_t(a.num_kv_heads) * kRows * RS;  // next slot, same KV head and row
+    float2 ml[kMaxPieces];
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kMaxPieces; ++p) {
+        ml[p] = p < np ? *reinterpret_cast<const float2*>(p0 + p * pstep + D) : make_float2(-INFINITY, 0.f);
+        M = fmaxf(M, ml[p].x);
+    }
+    float L = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kMaxPieces; ++p) {
+        if (p < np && ml[p].x != -INFINITY) {
+            const float wgt = __builtin_amdgcn_exp2f(ml[p].x - M);
+            L += wgt * ml[p].y;
+            const float4 lo = *reinterpret_cast<const float4*>(p0 + p * pstep + 8 * dc);
+            const float4 hi = *reinterpret_cast<const float4*>(p0 + p * pstep + 8 * dc + 4);
+            acc[0] += wgt * lo.x; acc[1] += wgt * lo.y; acc[2] += wgt * lo.z; acc[3] += wgt * lo.w;
+            acc[4] += wgt * hi.x; acc[5] += wgt * hi.y; acc[6] += wgt * hi.z; acc[7] += wgt * hi.w;
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint4 v;
+    v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    *reinterpret_cast<uint4*>(a.out + (size_t(a.cu_seqlens_q[b] + q) * a.num_q_heads + g * G + j) * D + 8 * dc) = v;
 }
 
 template <int D, int G, int NW>
@@ -506,10 +618,31 @@ template <int D, int G>
 hipError_t launch(const PrefillArgs& a, int total_q, int num_cus, int nw_given, hipStream_t st) {
     const int nw = nw_given > 0 ? nw_given : choose_nw(total_q, a.B, a.num_kv_heads, G, num_cus);
     const int QT = nw * kWaveRows / G;
-    const long items = a.items != nullptr ? long(a.n_items) * a.num_kv_heads
-                                          : ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
+    const long items = a.items != nullptr || a.pieces != nullptr
+                           ? long(a.n_items) * a.num_kv_heads
+                           : ((long(total_q) + QT - 1) / QT + a.B) * a.num_kv_heads;
     if (items > INT32_MAX) return hipErrorInvalidValue;
     return nw == 8 ? launch_nw<D, G, 8>(a, items, st) : launch_nw<D, G, 4>(a, items, st);
+}
+
+template <int D, int G>
+hipError_t launch_merge(const MergeArgs& m, int n_merges, int nw, hipStream_t st) {
+    const int parts = kWaveRows * nw / (kMergeThreads / (D / 8));  // workgroups per (item, KV head)
+    const dim3 grid(unsigned(long(n_merges) * m.num_kv_heads * parts));
+    if (nw == 8) hipLaunchKernelGGL((prefill_merge_kernel<D, G, 8>), grid, dim3(kMergeThreads), 0, st, m);
+    else hipLaunchKernelGGL((prefill_merge_kernel<D, G, 4>), grid, dim3(kMergeThreads), 0, st, m);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_g(const MergeArgs& m, int n_merges, int G, int nw, hipStream_t st) {
+    switch (G) {
+        case 1: return launch_merge<D, 1>(m, n_merges, nw, st);
+        case 2: return launch_merge<D, 2>(m, n_merges, nw, st);
+        case 4: return launch_merge<D, 4>(m, n_merges, nw, st);
+        case 8: return launch_merge<D, 8>(m, n_merges, nw, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int D>
@@ -550,7 +683,9 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
                  const int32_t* seqlens_k, int32_t B, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
                  const void* k_cache, const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
                  float softmax_scale, int32_t causal, int32_t window, void* out, void* stream,
-                 const int32_t* items = nullptr, int32_t n_items = 0, int32_t tile_rows = 0) {
+                 const int32_t* items = nullptr, int32_t n_items = 0, int32_t tile_rows = 0,
+                 const int32_t* pieces = nullptr, const int32_t* merges = nullptr, int32_t n_merges = 0,
+                 int32_t n_slots = 0, float* part = nullptr) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     PKV_REQUIRE(desc->kv_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED, "prefill supports bf16 caches only");
@@ -573,7 +708,7 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
                 "window = %d: a sliding window needs causal attention and window >= 0", window);
     // a work list fixes the query tile: the launch must cut tiles exactly as the list did
     int nw = 0;
-    if (items != nullptr) {
+    if (items != nullptr || pieces != nullptr) {
         nw = tile_rows > 0 && tile_rows * G % kWaveRows == 0 ? tile_rows * G / kWaveRows : 0;
         PKV_REQUIRE(nw == 4 || nw == 8, PKV_ERR_INVALID,
                     "tile_rows %d is not a query tile of this kernel for group size %d (%d or %d)", tile_rows, G,
@@ -604,10 +739,27 @@ int prefill_impl(const pkv_cache_desc* desc, const void* q, int32_t Hq, const in
     a.check = pkv::device_checks();
     a.items = items;
     a.n_items = n_items;
+    a.pieces = reinterpret_cast<const int4*>(pieces);
+    a.part = part;
+    a.n_slots = n_slots;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int cus = current_num_cus();
-    const hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, nw, st) : launch_g<128>(a, total_q, G, cus, nw, st);
+    hipError_t e = D == 64 ? launch_g<64>(a, total_q, G, cus, nw, st) : launch_g<128>(a, total_q, G, cus, nw, st);
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    if (n_merges > 0) {
+        MergeArgs m{};
+        m.merges = reinterpret_cast<const int4*>(merges);
+        m.part = part;
+        m.cu_seqlens_q = cu_seqlens_q;
+        m.out = static_cast<uint16_t*>(out);
+        m.B = B;
+        m.num_kv_heads = Hkv;
+        m.num_q_heads = Hq;
+        m.n_slots = n_slots;
+        m.check = a.check;
+        e = D == 64 ? launch_merge_g<64>(m, n_merges, G, nw, st) : launch_merge_g<128>(m, n_merges, G, nw, st);
+        PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "prefill merge launch failed: %s", hipGetErrorString(e));
+    }
     return PKV_OK;
 }
 
@@ -649,20 +801,29 @@ extern "C" int pkv_paged_attn_prefill_ordered(const pkv_cache_desc* desc, const 
                         n_items, tile_rows);
 }
 
-extern "C" int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
-                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
-                                      int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items,
-                                      int32_t* tile_rows) {
+namespace {
+
+// One (sequence, query tile) work item of a prefill launch: code = (sequence << 16) | tile, and
+// the key tiles kt0 .. kt1 - 1 it walks (from the tile holding its first token's first key).
+struct PlanItem {
+    int32_t code;
+    int32_t kt0, kt1;
+};
+
+// The items of a prefill call cut into query tiles of *QT tokens (the tile the launch will use), in
+// sequence and tile order; PKV_OK or the failure recorded.
+int plan_items(const pkv_cache_desc* desc, int32_t Hq, int32_t B, const int32_t* cu_seqlens_q,
+               const int32_t* seqlens_k, int32_t causal, int32_t window, std::vector<PlanItem>& items, int* QT) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
-    PKV_REQUIRE(n_items != nullptr, PKV_ERR_INVALID, "NULL n_items");
-    *n_items = 0;
-    PKV_REQUIRE(B >= 0 && B <= 32767 && Hq > 0 && capacity >= 0 && window >= 0, PKV_ERR_INVALID,
-                "bad shape (B=%d, Hq=%d, capacity=%d, window=%d)", B, Hq, capacity, window);
+    PKV_REQUIRE(B >= 0 && B <= 32767 && Hq > 0 && window >= 0, PKV_ERR_INVALID,
+                "bad shape (B=%d, Hq=%d, window=%d)", B, Hq, window);
     PKV_REQUIRE(Hq % desc->num_kv_heads == 0, PKV_ERR_INVALID, "Hq %d is not a multiple of Hkv %d", Hq,
                 desc->num_kv_heads);
     const int G = Hq / desc->num_kv_heads;
     PKV_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, PKV_ERR_UNSUPPORTED, "query group size %d", G);
+    items.clear();
+    *QT = 4 * kWaveRows / G;
     if (B == 0) return PKV_OK;
     PKV_REQUIRE(cu_seqlens_q && seqlens_k, PKV_ERR_INVALID, "NULL pointer");
     PKV_REQUIRE(cu_seqlens_q[0] == 0, PKV_ERR_INVALID, "cu_seqlens_q[0] = %d", cu_seqlens_q[0]);
@@ -672,37 +833,174 @@ extern "C" int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, in
         PKV_REQUIRE(seqlens_k[b] >= 0 && (!causal || seqlens_k[b] >= nq), PKV_ERR_INVALID,
                     "seqlens_k[%d] = %d for %d new tokens", b, seqlens_k[b], nq);
     }
-    const int cus = current_num_cus();
-    const int QT = choose_nw(cu_seqlens_q[B], B, desc->num_kv_heads, G, cus) * kWaveRows / G;
-    if (tile_rows != nullptr) *tile_rows = QT;
-    // the items with their key tiles (+1 for a workgroup's fixed cost): heaviest first, ties in
-    // sequence and tile order
-    std::vector<uint64_t> key;
-    std::vector<int32_t> item;
+    *QT = choose_nw(cu_seqlens_q[B], B, desc->num_kv_heads, G, current_num_cus()) * kWaveRows / G;
     for (int b = 0; b < B; ++b) {
         const int nq = cu_seqlens_q[b + 1] - cu_seqlens_q[b], L = seqlens_k[b];
-        for (int t = 0; t * QT < nq; ++t) {
+        for (int t = 0; t * *QT < nq; ++t) {
             PKV_REQUIRE(t <= 0xffff, PKV_ERR_UNSUPPORTED, "sequence %d has more than 65536 query tiles", b);
-            const int pos0 = L - nq + t * QT, nqt = std::min(QT, nq - t * QT);
+            const int pos0 = L - nq + t * *QT, nqt = std::min(*QT, nq - t * *QT);
             const int kv_len = causal ? std::min(L, pos0 + nqt) : L;
             const int kt0 = window > 0 ? std::max(0, pos0 - window + 1) / kKT : 0;
-            const uint32_t w = uint32_t((kv_len + kKT - 1) / kKT - kt0 + 1);
-            key.push_back((uint64_t(~w) << 32) | uint32_t(item.size()));
-            item.push_back((b << 16) | t);
+            items.push_back({(b << 16) | t, kt0, std::max(kt0, (kv_len + kKT - 1) / kKT)});
         }
     }
-    const int n = int(item.size());
-    PKV_REQUIRE(n <= capacity && (work_items != nullptr || n == 0), PKV_ERR_SMALL_BUFFER,
-                "%d work items, capacity %d", n, capacity);
+    return PKV_OK;
+}
+
+// Launch order of work with the given weights: heaviest first (ties in index order), cut into
+// rounds of one workgroup per CU (`round` items), every odd round reversed so that the heavy items
+// of one round share CUs with the light ones of the next.
+std::vector<int> heaviest_first_rounds(const std::vector<uint32_t>& weight, int round) {
+    const int n = int(weight.size());
+    std::vector<uint64_t> key(n);
+    for (int i = 0; i < n; ++i) key[i] = (uint64_t(~weight[i]) << 32) | uint32_t(i);
     std::sort(key.begin(), key.end());
-    // rounds of one workgroup per CU: every odd round runs lightest first, so the heavy items of
-    // one round share CUs with the light ones of the next
-    const int round = std::max(1, cus / desc->num_kv_heads);
+    round = std::max(1, round);
     for (int r0 = round; r0 < n; r0 += 2 * round)
         std::reverse(key.begin() + r0, key.begin() + std::min(n, r0 + round));
-    for (int i = 0; i < n; ++i) work_items[i] = item[key[i] & 0xffffffffu];
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = int(key[i] & 0xffffffffu);
+    return order;
+}
+
+}  // namespace
+
+extern "C" int pkv_prefill_work_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                                      const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
+                                      int32_t window, int32_t* work_items, int32_t capacity, int32_t* n_items,
+                                      int32_t* tile_rows) {
+    PKV_REQUIRE(n_items != nullptr, PKV_ERR_INVALID, "NULL n_items");
+    *n_items = 0;
+    PKV_REQUIRE(capacity >= 0, PKV_ERR_INVALID, "capacity = %d", capacity);
+    std::vector<PlanItem> items;
+    int QT = 0;
+    const int rc = plan_items(desc, Hq, B, cu_seqlens_q, seqlens_k, causal, window, items, &QT);
+    if (rc != PKV_OK) return rc;
+    if (tile_rows != nullptr) *tile_rows = QT;
+    const int n = int(items.size());
+    PKV_REQUIRE(n <= capacity && (work_items != nullptr || n == 0), PKV_ERR_SMALL_BUFFER,
+                "%d work items, capacity %d", n, capacity);
+    // weight: the key tiles an item walks, +1 for a workgroup's fixed cost
+    std::vector<uint32_t> weight(n);
+    for (int i = 0; i < n; ++i) weight[i] = uint32_t(items[i].kt1 - items[i].kt0 + 1);
+    const std::vector<int> order = heaviest_first_rounds(weight, current_num_cus() / desc->num_kv_heads);
+    for (int i = 0; i < n; ++i) work_items[i] = items[order[i]].code;
     *n_items = n;
     return PKV_OK;
+}
+
+// Split order for launches that leave CUs idle.  A launch of fewer workgroups than the device has
+// CUs is bound by its longest item (the last query tile of the longest prompt walks every key
+// tile alone on a CU).  Such a launch cuts the key range of every item longer than T tiles into
+// up to kMaxPieces pieces of nearly equal length, each run by its own workgroups and written as a
+// partial state, and a merge launch combines the pieces by log-sum-exp (split-K, as decode does
+// over its context).  T starts at kMinPieceTiles (a piece also pays a workgroup's start) and grows
+// until the launch fits two workgroups per CU.  Launches that fill the device are not split.
+constexpr int kMinPieceTiles = 4;
+
+extern "C" int pkv_prefill_split_order(const pkv_cache_desc* desc, int32_t Hq, int32_t B,
+                                       const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t causal,
+                                       int32_t window, int32_t* pieces, int32_t pieces_capacity, int32_t* n_pieces,
+                                       int32_t* merges, int32_t merges_capacity, int32_t* n_merges,
+                                       int32_t* n_slots, int32_t* tile_rows) {
+    PKV_REQUIRE(n_pieces && n_merges && n_slots && tile_rows, PKV_ERR_INVALID, "NULL output count");
+    *n_pieces = *n_merges = *n_slots = 0;
+    PKV_REQUIRE(pieces_capacity >= 0 && merges_capacity >= 0, PKV_ERR_INVALID, "capacity %d, %d",
+                pieces_capacity, merges_capacity);
+    std::vector<PlanItem> items;
+    int QT = 0;
+    const int rc = plan_items(desc, Hq, B, cu_seqlens_q, seqlens_k, causal, window, items, &QT);
+    if (rc != PKV_OK) return rc;
+    *tile_rows = QT;
+    const int n = int(items.size()), Hkv = desc->num_kv_heads, cus = current_num_cus();
+    // pieces per item: 1 when the launch fills the device, else ceil(tiles / T) up to kMaxPieces
+    std::vector<int> np(n, 1);
+    if (long(n) * Hkv < cus) {
+        for (int T = kMinPieceTiles;; ++T) {
+            long wgs = 0;
+            for (int i = 0; i < n; ++i) {
+                const int tiles = items[i].kt1 - items[i].kt0;
+                np[i] = std::max(1, std::min(kMaxPieces, (tiles + T - 1) / T));
+                wgs += long(np[i]) * Hkv;
+            }
+            if (wgs <= cus) break;
+        }
+    }
+    struct Piece {
+        int32_t code, kt0, kt1, slot;
+    };
+    std::vector<Piece> list;
+    std::vector<int32_t> merge_list;
+    int slots = 0;
+    for (int i = 0; i < n; ++i) {
+        const PlanItem& it = items[i];
+        if (np[i] == 1) {
+            list.push_back({it.code, 0, INT_MAX, -1});
+            continue;
+        }
+        const int tiles = it.kt1 - it.kt0;
+        for (int p = 0; p < np[i]; ++p)
+            list.push_back({it.code, it.kt0 + tiles * p / np[i], it.kt0 + tiles * (p + 1) / np[i], slots + p});
+        merge_list.insert(merge_list.end(), {it.code, slots, np[i], 0});
+        slots += np[i];
+    }
+    const int npc = int(list.size()), nm = int(merge_list.size() / 4);
+    PKV_REQUIRE(npc <= pieces_capacity && (pieces != nullptr || npc == 0), PKV_ERR_SMALL_BUFFER,
+                "%d pieces, capacity %d", npc, pieces_capacity);
+    PKV_REQUIRE(nm <= merges_capacity && (merges != nullptr || nm == 0), PKV_ERR_SMALL_BUFFER,
+                "%d merges, capacity %d", nm, merges_capacity);
+    std::vector<uint32_t> weight(npc);
+    // weight: the key tiles a piece walks (a whole item: all of its tiles), +1 for the start
+    for (int i = 0, k = 0; i < n; ++i)
+        for (int p = 0; p < np[i]; ++p, ++k)
+            weight[k] = uint32_t(np[i] == 1 ? items[i].kt1 - items[i].kt0 + 1 : list[k].kt1 - list[k].kt0 + 1);
+    const std::vector<int> order = heaviest_first_rounds(weight, cus / Hkv);
+    for (int i = 0; i < npc; ++i) {
+        const Piece& pc = list[order[i]];
+        pieces[4 * i + 0] = pc.code;
+        pieces[4 * i + 1] = pc.kt0;
+        pieces[4 * i + 2] = pc.kt1;
+        pieces[4 * i + 3] = pc.slot;
+    }
+    std::copy(merge_list.begin(), merge_list.end(), merges);
+    *n_pieces = npc;
+    *n_merges = nm;
+    *n_slots = slots;
+    return PKV_OK;
+}
+
+extern "C" size_t pkv_prefill_split_workspace_bytes(const pkv_cache_desc* desc, int32_t Hq, int32_t n_slots,
+                                                    int32_t tile_rows) {
+    if (desc == nullptr || desc->num_kv_heads <= 0 || Hq <= 0 || Hq % desc->num_kv_heads != 0 || n_slots < 0 ||
+        tile_rows <= 0)
+        return 0;
+    const size_t rows = size_t(tile_rows) * size_t(Hq / desc->num_kv_heads);  // MFMA rows of a query tile
+    return size_t(n_slots) * size_t(desc->num_kv_heads) * size_t(desc->head_dim + 4) * rows * sizeof(float);
+}
+
+extern "C" int pkv_paged_attn_prefill_split(const pkv_cache_desc* desc, const void* q, int32_t Hq,
+                                            const int32_t* cu_seqlens_q, const int32_t* seqlens_k, int32_t B,
+                                            int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                            int32_t max_blocks, float softmax_scale, int32_t causal,
+                                            int32_t window, const int32_t* pieces, int32_t n_pieces,
+                                            const int32_t* merges, int32_t n_merges, int32_t n_slots,
+                                            int32_t tile_rows, void* workspace, size_t workspace_bytes, void* out,
+                                            void* stream) {
+    PKV_REQUIRE(n_pieces >= 0 && n_merges >= 0 && n_slots >= 0, PKV_ERR_INVALID,
+                "n_pieces = %d, n_merges = %d, n_slots = %d", n_pieces, n_merges, n_slots);
+    PKV_REQUIRE(pieces != nullptr || n_pieces == 0, PKV_ERR_INVALID, "NULL pieces");
+    PKV_REQUIRE(merges != nullptr || n_merges == 0, PKV_ERR_INVALID, "NULL merges");
+    PKV_REQUIRE((n_merges == 0) == (n_slots == 0), PKV_ERR_INVALID,
+                "%d merges over %d partial slots: both are zero or neither", n_merges, n_slots);
+    if (n_pieces == 0) return PKV_OK;
+    const size_t need = pkv_prefill_split_workspace_bytes(desc, Hq, n_slots, tile_rows);
+    PKV_REQUIRE(n_slots == 0 || (workspace != nullptr && workspace_bytes >= need), PKV_ERR_SMALL_BUFFER,
+                "%d partial slots need %zu bytes of workspace, %zu given", n_slots, need, workspace_bytes);
+    PKV_REQUIRE((uintptr_t(workspace) & 15) == 0, PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+    return prefill_impl(desc, q, Hq, cu_seqlens_q, seqlens_k, B, total_q, max_seqlen_q, max_seqlen_k, k_cache,
+                        v_cache, block_tables, max_blocks, softmax_scale, causal, window, out, stream, nullptr,
+                        n_pieces, tile_rows, pieces, merges, n_merges, n_slots, static_cast<float*>(workspace));
 }
 
 extern "C" int pkv_prefill_tile_rows(const pkv_cache_desc* desc, int32_t Hq, int32_t B, int32_t total_q,

@@ -14,7 +14,7 @@ import torch
 from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_group_shared_lens, decode_plan,
                decode_store_attend, paged_attn_decode_grouped,
                decode_workspace_bytes, desc_of, kv_store, kv_store_quant, lib, paged_attn_decode,
-               paged_attn_prefill_ordered, prefill_work_order)
+               paged_attn_prefill_split, prefill_split_order, prefill_split_workspace_bytes)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 # mean shared keys per group from which DecodeBatch reads a group's shared blocks once
@@ -63,6 +63,16 @@ class PagedKV:
         """int8 pools: quantise bf16/fp32 device rows [n][Hkv][D] into the cache at slots[n]; ``runs`` as
         :func:`store_runs` gives them, uploaded (built from a host copy of ``slots`` when None)."""
         kv_store_quant(k_rows, v_rows, slots, self.k_cache, self.v_cache, self.k_scale, self.v_scale, runs=runs)
+
+    def split_workspace(self, nbytes):
+        """Device scratch for split prefill partials, grown on demand and reused by later chunks
+        (calls on one stream never overlap); None when nothing is split."""
+        if nbytes <= 0:
+            return None
+        ws = getattr(self, "_split_ws", None)
+        if ws is None or ws.numel() < nbytes:
+            ws = self._split_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return ws
 
     def copy_on_write(self, src, dst, rows):
         """Enqueue the block copies src[i] -> dst[i] of rows 0..rows[i]-1 (host int32, from
@@ -339,20 +349,29 @@ def admit_and_store(kv, seq_ids, token_lists, k_rows, v_rows, k_scale_rows=None,
 
 
 def _attend_chunk(kv, q_new, k_new, v_new, cu, lk, slots, tab, softmax_scale, causal, out):
-    """Upload a chunk's metadata and its work order (pkv_prefill_work_order) in one copy, store the
-    new rows, and attend in that order."""
+    """Upload a chunk's metadata and its split work order (pkv_prefill_split_order: the work order,
+    with long items cut into key-range pieces when the launch would leave CUs idle) in one copy,
+    store the new rows, and attend in that order."""
     dev = kv.device
     B, n_new, mb = len(lk), len(slots), tab.shape[1]
-    items, tile_rows = prefill_work_order(desc_of(kv.k_cache), q_new.shape[1], cu, lk, causal)
-    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel(), items]).astype(np.int32), dev)
+    Hq = q_new.shape[1]
+    desc = desc_of(kv.k_cache)
+    pieces, merges, n_slots, tile_rows = prefill_split_order(desc, Hq, cu, lk, causal)
+    meta = _to_dev(np.concatenate([cu, lk, slots, tab.ravel(), pieces.ravel(), merges.ravel()]).astype(np.int32),
+                   dev)
     d_cu, d_lk = meta[:B + 1], meta[B + 1:2 * B + 1]
     d_slots = meta[2 * B + 1:2 * B + 1 + n_new]
-    d_tab = meta[2 * B + 1 + n_new:2 * B + 1 + n_new + B * mb].view(B, mb)
-    d_items = meta[2 * B + 1 + n_new + B * mb:]
+    o = 2 * B + 1 + n_new
+    d_tab = meta[o:o + B * mb].view(B, mb)
+    o += B * mb
+    d_pieces = meta[o:o + pieces.size].view(-1, 4)
+    d_merges = meta[o + pieces.size:].view(-1, 4)
     kv.store(d_slots, k_new, v_new)
     n_q = np.diff(cu)
-    return paged_attn_prefill_ordered(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache,
-                                      d_tab, softmax_scale, d_items, tile_rows, causal, out=out)
+    return paged_attn_prefill_split(q_new, d_cu, d_lk, int(n_q.max()), int(lk.max()), kv.k_cache, kv.v_cache,
+                                    d_tab, softmax_scale, d_pieces, d_merges, n_slots, tile_rows,
+                                    kv.split_workspace(prefill_split_workspace_bytes(desc, Hq, n_slots, tile_rows)),
+                                    causal, out=out)
 
 
 def prefill_segments(kv, segments, q_new, k_new, v_new, softmax_scale, causal=True, out=None):

@@ -396,3 +396,78 @@ def test_device_check_switch_and_error_word_arguments():
     assert P.lib().pkv_set_device_checks(1) == P.OK
     assert P.lib().pkv_set_device_checks(0) == P.OK
     assert P.lib().pkv_device_error(None, None, None, None) == P.ERR_INVALID  # code is required
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 300)])
+def test_prefill_split_order(causal, window):
+    """pkv_prefill_split_order on a launch with fewer workgroups than CUs: every item's key tiles
+    are covered once, by its pieces in key order (consecutive slots, one merge record) or whole;
+    the pieces per item are min(8, ceil(tiles / T)) for the smallest T from 4 up that fits the launch
+    in one workgroup per CU (256 CUs without a device); the workspace formula; and a launch that
+    fills the device stays the work order."""
+    d = _desc(num_kv_heads=8, head_dim=128, kv_dtype=P.BF16)
+    nq = np.array([300, 5, 190, 64], np.int32)
+    lk = np.array([1900, 2000, 1300, 64], np.int32)
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    pieces, merges, n_slots, qt = P.prefill_split_order(d, 16, cu, lk, causal, window)
+    assert qt == P.prefill_tile_rows(d, 16, 4, int(cu[-1]))
+    items = {(b << 16) | t for b in range(4) for t in range(-(-int(nq[b]) // qt))}
+    assert len(items) * 8 < 256  # underfilled: the case must split
+    assert len(merges) > 0 and len(pieces) * 8 <= 256
+    works = {code: _item_work(code, cu, lk, qt, causal, window) for code in items}
+    T = next(T for T in range(4, 10**6) if sum(max(1, min(8, -(-w // T))) for w in works.values()) * 8 <= 256)
+    by_item = {}
+    for code, a, b, slot in pieces.tolist():
+        by_item.setdefault(code, []).append((a, b, slot))
+    assert set(by_item) == items
+    split = {int(m[0]): (int(m[1]), int(m[2])) for m in merges}
+    for code, ps in by_item.items():
+        work = _item_work(code, cu, lk, qt, causal, window)
+        first = max(0, (int(lk[code >> 16]) - int(nq[code >> 16]) + (code & 0xffff) * qt) - window + 1) // 64 \
+            if window else 0
+        if code not in split:
+            assert ps == [(0, 2**31 - 1, -1)]
+            assert work <= T
+            continue
+        s0, npc = split[code]
+        ps = sorted(ps)
+        assert len(ps) == npc == min(8, -(-work // T)) and npc >= 2
+        assert [p[2] for p in ps] == list(range(s0, s0 + npc))
+        assert ps[0][0] == first and ps[-1][1] == first + work
+        assert all(ps[i][1] == ps[i + 1][0] for i in range(npc - 1))
+        assert all(b - a >= min(4, work // npc) for a, b, _ in ps)
+    assert sorted(s for m in merges for s in range(m[1], m[1] + m[2])) == list(range(n_slots))
+    G = 2
+    assert P.prefill_split_workspace_bytes(d, 16, n_slots, qt) == n_slots * 8 * (128 + 4) * qt * G * 4
+    assert P.prefill_split_workspace_bytes(d, 16, 0, qt) == 0
+    # a launch that fills the device: the work order itself, nothing split
+    rng = np.random.default_rng(5)
+    nq2 = rng.integers(100, 900, size=13).astype(np.int32)
+    cu2 = np.concatenate([[0], np.cumsum(nq2)]).astype(np.int32)
+    lk2 = (nq2 + 300).astype(np.int32)
+    p2, m2, s2, qt2 = P.prefill_split_order(d, 16, cu2, lk2, causal, window)
+    order, qt3 = P.prefill_work_order(d, 16, cu2, lk2, causal, window)
+    assert qt2 == qt3 and len(m2) == 0 and s2 == 0
+    assert (p2[:, 0] == order).all() and (p2[:, 1] == 0).all() and (p2[:, 2] == 2**31 - 1).all()
+    assert (p2[:, 3] == -1).all()
+
+
+def test_prefill_split_errors():
+    d = _desc(num_kv_heads=2, head_dim=64, kv_dtype=P.BF16)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    cu, lk = np.array([0, 200], np.int32), np.array([2000], np.int32)
+    pieces, merges = np.empty((1, 4), np.int32), np.empty((4, 4), np.int32)
+    n, m, s, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    rc = P.lib().pkv_prefill_split_order(ctypes.byref(d), 4, 1, cu.ctypes.data_as(p32), lk.ctypes.data_as(p32), 1, 0,
+                                         pieces.ctypes.data_as(p32), 1, ctypes.byref(n), merges.ctypes.data_as(p32),
+                                         4, ctypes.byref(m), ctypes.byref(s), ctypes.byref(t))
+    assert rc == P.ERR_SMALL_BUFFER and n.value == 0  # four items of which some are split: more than one piece
+    args = lambda pc, npc, mg, nm, ns, ws, wb: P.lib().pkv_paged_attn_prefill_split(
+        ctypes.byref(d), FAKE, 4, FAKE, FAKE, 1, 200, 200, 2000, FAKE, FAKE, FAKE, 8, 0.1, 1, 0, pc, npc, mg, nm, ns,
+        64, ws, wb, FAKE, None)
+    assert args(None, 1, FAKE, 1, 2, FAKE, 1 << 30) == P.ERR_INVALID  # pieces missing
+    assert args(FAKE, 1, None, 1, 2, FAKE, 1 << 30) == P.ERR_INVALID  # merges missing
+    assert args(FAKE, 1, FAKE, 1, 0, FAKE, 1 << 30) == P.ERR_INVALID  # merges without slots
+    assert args(FAKE, 1, FAKE, 1, 2, FAKE, 16) == P.ERR_SMALL_BUFFER  # workspace too small
+    assert args(FAKE, 1, FAKE, 1, 2, None, 0) == P.ERR_SMALL_BUFFER  # no workspace
+    assert args(FAKE, 0, None, 0, 0, None, 0) == P.OK  # nothing to do

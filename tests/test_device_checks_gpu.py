@@ -233,3 +233,23 @@ def test_grouped_decode_rejects_a_bad_group(checks, case):
     ref = P.paged_attn_decode(q[2:], kc, vc, t[2:], ln[2:], 400, 0.088)
     torch.cuda.synchronize()
     assert (out[2:].float() - ref.float()).abs().max().item() < 2e-2
+
+
+def test_split_prefill_rejects_a_piece_slot_outside_the_workspace(checks):
+    """Pieces of sequence 0's tile split over slots 0 and 1, then a piece of sequence 1 that names
+    slot 2 of a call with 2 slots (the workspace holds a third slot, so even an unchecked write
+    would stay in memory the test owns): error 5 for that piece, sequence 0 still merged."""
+    dev = checks
+    _, (kc, vc) = _caches(dev)
+    kc.normal_()
+    vc.normal_()
+    q = torch.randn(96, HQ, D, device=dev).to(torch.bfloat16)
+    out = torch.zeros_like(q)
+    desc = P.desc_of(kc)
+    ws = torch.zeros(P.prefill_split_workspace_bytes(desc, HQ, 3, 64), dtype=torch.uint8, device=dev)
+    pieces = _i32([[0, 0, 2, 0], [0, 2, 4, 1], [1 << 16, 0, 2**31 - 1, 2]], dev)
+    merges = _i32([[0, 0, 2, 0]], dev)
+    P.paged_attn_prefill_split(q, _i32([0, 64, 96], dev), _i32([256, 32], dev), 64, 256, kc, vc,
+                               _i32([[0, 1], [2, 3]], dev), 0.088, pieces, merges, 2, 64, ws, True, out=out)
+    _expect(RUN, 2, 1 << 16)
+    assert out[:64].abs().sum() > 0 and not out[64:].any()
