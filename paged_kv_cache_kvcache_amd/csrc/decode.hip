@@ -97,6 +97,22 @@ __device__ __forceinline__ float bcast_row(float x) {
     return dpp<kRowNewBcast + N>(x);
 }
 
+// x of lane 2u of each row of 16, in every lane of the row (u uniform and unrolled: DPP lane selects
+// are immediates).
+__device__ __forceinline__ uint32_t bcast_row_even(uint32_t x, int u) {
+    const float f = __uint_as_float(x);
+    switch (u) {
+        case 0: return __float_as_uint(bcast_row<0>(f));
+        case 1: return __float_as_uint(bcast_row<2>(f));
+        case 2: return __float_as_uint(bcast_row<4>(f));
+        case 3: return __float_as_uint(bcast_row<6>(f));
+        case 4: return __float_as_uint(bcast_row<8>(f));
+        case 5: return __float_as_uint(bcast_row<10>(f));
+        case 6: return __float_as_uint(bcast_row<12>(f));
+        default: return __float_as_uint(bcast_row<14>(f));
+    }
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -105,6 +121,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v;
+    v.x = static_cast<__bf16>(lo);
+    v.y = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// f rounded to the nearest bf16 value (ties to even), as fp32.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_lo(pack_bf16x2(f, 0.f)); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -197,6 +223,38 @@ struct Traits<PKV_I8, D> {
         for (int e = 0; e < E; ++e) v[e] = code(w[e / 4], e % 4);
     }
 };
+
+// acc[j] += sum_i p_j(row i) v(row i) over the 16 rows of a lane group, for bf16 V: rows 2u and
+// 2u + 1 go together through v_dot2_f32_bf16, whose operands are the two rows' bf16
+// probabilities (p holds each lane's own row, already bf16 values) and the two rows' values of one
+// d, gathered by one byte permute.  The fp32 path spends two FMAs and the widening of both values
+// on the same pair.
+template <int G, int E, int W>
+__device__ __forceinline__ void pv_bf16_pairs(float (&acc)[G][E], const uint32_t (&vw)[16][W], const float (&p)[G]) {
+    uint32_t pp[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) pp[j] = pack_bf16x2(p[j], dpp<kQuadXor1>(p[j]));  // even lane c: rows c, c + 1
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        uint32_t lo[W], hi[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            lo[k] = __builtin_amdgcn_perm(vw[2 * u + 1][k], vw[2 * u][k], 0x05040100u);  // d = 2k of both rows
+            hi[k] = __builtin_amdgcn_perm(vw[2 * u + 1][k], vw[2 * u][k], 0x07060302u);  // d = 2k + 1
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const bf16x2_t pu = __builtin_bit_cast(bf16x2_t, bcast_row_even(pp[j], u));
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                acc[j][2 * k] = __builtin_amdgcn_fdot2_f32_bf16(pu, __builtin_bit_cast(bf16x2_t, lo[k]),
+                                                               acc[j][2 * k], false);
+                acc[j][2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(pu, __builtin_bit_cast(bf16x2_t, hi[k]),
+                                                                   acc[j][2 * k + 1], false);
+            }
+        }
+    }
+}
 
 template <int W>
 __device__ __forceinline__ void load_piece(const char* p, uint32_t* w) {
@@ -421,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             const bool none = mn == kNegInf;
             const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
             p[j] = none ? 0.f : __builtin_amdgcn_exp2f(sc - mn);
+            if constexpr (DT == PKV_BF16) p[j] = round_bf16(p[j]);  // the probability P.V multiplies
             m[j] = mn;
             l[j] = l[j] * alpha + p[j];
 #pragma unroll
@@ -428,6 +487,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             p[j] *= vs;
         }
 
+        if constexpr (DT == PKV_BF16) pv_bf16_pairs(acc, vw, p);
+        else
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float v[E];
@@ -680,12 +741,15 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
             const bool none = mn == kNegInf;
             const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
             p[j] = none ? 0.f : __builtin_amdgcn_exp2f(sc - mn);
+            if constexpr (DT == PKV_BF16) p[j] = round_bf16(p[j]);  // the probability P.V multiplies
             m[j] = mn;
             l[j] = l[j] * alpha + p[j];
 #pragma unroll
             for (int e = 0; e < E; ++e) acc[j][e] *= alpha;
             p[j] *= vs;
         }
+        if constexpr (DT == PKV_BF16) pv_bf16_pairs(acc, vw, p);
+        else
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float v[E];
