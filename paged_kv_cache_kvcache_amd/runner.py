@@ -19,7 +19,7 @@ from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_grou
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
 # mean shared keys per group from which DecodeBatch reads a group's shared blocks once
 # (pkv_paged_attn_decode_grouped); measured crossover on MI355X, bf16, 16 / 8 heads, D 128
-GROUP_MIN_SHARED = 2048
+GROUP_MIN_SHARED = 1536
 
 
 def _to_dev(a, device, dtype=None):
