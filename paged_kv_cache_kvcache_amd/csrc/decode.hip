@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <type_traits>
 #include <vector>
 
 #include "pkv_device.h"
@@ -275,6 +276,30 @@ __device__ __forceinline__ void load_piece(const char* p, uint32_t* w) {
     }
 }
 
+// Buffer-descriptor form of load_piece: W dwords at byte offset off of the descriptor's range,
+// zeros where the range ends before them; nontemporal like load_piece.  Word 3 of a gfx9 buffer
+// descriptor: 32-bit data format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kNontemporal = 2;  // cache-policy bit of the buffer-load builtins: nt
+constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left alone
+template <int W>
+__device__ __forceinline__ void load_piece_buf(__amdgpu_buffer_rsrc_t rs, int off, uint32_t* w) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    if constexpr (W == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kNontemporal);
+    } else if constexpr (W == 2) {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kNontemporal);
+        w[0] = x.x; w[1] = x.y;
+    } else {
+#pragma unroll
+        for (int k = 0; k < W; k += 4) {
+            const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * k, 0, kNontemporal);
+            w[k] = x.x; w[k + 1] = x.y; w[k + 2] = x.z; w[k + 3] = x.w;
+        }
+    }
+}
+
 struct DecodeArgs {
     const void* q;
     const char* k_cache;
@@ -430,51 +455,92 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
             bt_win = win;
             const int e = blk0 + 64 * win + lane;
             btv = e < blk1 ? bt[e] : 0;
+            // wait here, on the rare reload: a wait at the join would hold every lookup (and the
+            // next block's loads behind it) until all loads in flight had landed
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
         }
         return __builtin_amdgcn_readlane(btv, (blk - blk0) & 63);
     };
-    const size_t lane_off = size_t(r) * RB + size_t(c) * PB;
 
     // Blocks whose quarter w holds valid tokens: blk0 .. blk_end-1 (only the last may be partial).
     const int blk_end = min(blk1, max(blk0, (ctx - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
-    auto tile_ptr = [&](const char* cache, int64_t phys) {
-        return cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB + lane_off;
+    // A wavefront's tile of one block: rows 64w..64w+63 of (block, KV head), read through a buffer
+    // descriptor whose range ends at the tile's last valid row, so rows past the context end read
+    // as zeros with no exec-masked loads.  The per-lane offsets are the same for every tile: only
+    // the descriptor (scalar registers) changes, and no load needs a 64-bit address of its own.
+    auto tile_rsrc = [&](const char* cache, int64_t phys, int valid) {
+        const char* base = cache + ((size_t(phys) * a.num_kv_heads + g) * pkv::kBlock + w * kTile) * RB;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, valid * RB, kBufferWord3);
     };
-    auto load_tile = [&](uint32_t (&dst)[16][W], const char* src, int valid) {
+    const int lane_off = r * RB + c * PB;
+    auto load_tile = [&](uint32_t (&dst)[16][W], __amdgpu_buffer_rsrc_t rs) {
+        // Opaque copy of the lane offset, so that the compiler folds each row's constant into the
+        // load's immediate offset instead of keeping one register per row across the loop.
+        int off = lane_off;
+        asm volatile("" : "+v"(off));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (4 * i + r < valid) {
-                load_piece<W>(src + size_t(4 * i) * RB, dst[i]);
-            } else {
-#pragma unroll
-                for (int k = 0; k < W; ++k) dst[i][k] = 0u;
-            }
+        for (int i = 0; i < 16; ++i) load_piece_buf<W>(rs, off + 4 * i * RB, dst[i]);
+    };
+
+    // Block t + 1's K tile is requested as soon as block t's scores are formed (the K registers
+    // are free then), and block t's V tile at the top of its step, right after block t - 1's P.V:
+    // a wavefront keeps loads in flight through its own arithmetic while holding one K tile and one
+    // V tile, as before.  Only K is carried from one step to the next.
+    uint32_t kw[16][W], vw[16][W];
+    auto tile_valid = [&](int blk) { return min(kTile, ctx - (blk * pkv::kBlock + w * kTile)); };
+    int64_t phys = 0;
+    int valid = 0;
+    // int8: the scales of the block whose K tile is in flight, requested before that tile so that
+    // waiting for them never waits for a tile
+    float ksn = 1.f, vsn = 1.f;
+    auto load_scales = [&](int64_t ph) {
+        if constexpr (DT == PKV_I8) {
+            ksn = a.k_scale[ph * a.num_kv_heads + g];
+            vsn = a.v_scale[ph * a.num_kv_heads + g];
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-
-    uint32_t kw[16][W], vw[16][W];
-    for (int blk = blk0; blk < blk_end; ++blk) {
-        const int64_t phys = phys_block(blk);
-        const int valid = min(kTile, ctx - (blk * pkv::kBlock + w * kTile));
-        load_tile(kw, tile_ptr(a.k_cache, phys), valid);
-        load_tile(vw, tile_ptr(a.v_cache, phys), valid);
-
+    if (blk0 < blk_end) {
+        phys = phys_block(blk0);
+        valid = tile_valid(blk0);
+        load_scales(phys);
+        load_tile(kw, tile_rsrc(a.k_cache, phys, valid));
+    }
+    // One step per block; PF: this step also requests the next block's K tile.  The last step is
+    // its own instantiation, so that the wait counts on every path know exactly which loads are in
+    // flight.
+    auto step = [&](int blk, auto prefetch) __attribute__((always_inline)) {
+        constexpr bool PF = decltype(prefetch)::value;
+        load_tile(vw, tile_rsrc(a.v_cache, phys, valid));
         float ks = a.scale_log2, vs = 1.f;
         if constexpr (DT == PKV_I8) {
-            ks *= a.k_scale[phys * a.num_kv_heads + g];
-            vs = a.v_scale[phys * a.num_kv_heads + g];
+            ks *= ksn;
+            vs = vsn;
         }
         const bool row_ok = 4 * c + r < valid && blk * pkv::kBlock + w * kTile + 4 * c + r >= lo;
 
-        float p[G];
+        float tot[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             float part[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) part[i] = T::dot(qr[j], kw[i]);
             // every lane must take part in the DPP exchanges: reduce first, mask afterwards
-            const float tot = transpose_reduce16(part, c);
-            const float sc = row_ok ? tot * ks : kNegInf;
+            tot[j] = transpose_reduce16(part, c);
+            __builtin_amdgcn_sched_barrier(0);  // one head's 16 partial sums live at a time
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PF) {
+            phys = phys_block(blk + 1);
+            valid = tile_valid(blk + 1);
+            load_scales(phys);
+            load_tile(kw, tile_rsrc(a.k_cache, phys, valid));
+        }
+
+        float p[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float sc = row_ok ? tot[j] * ks : kNegInf;
             const float mn = fmaxf(m[j], row_max16(sc));
             const bool none = mn == kNegInf;
             const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
@@ -518,7 +584,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
                 for (int e = 0; e < E; ++e) acc[j][e] = fmaf(pi, v[e], acc[j][e]);
             }
         }
-    }
+    };
+    for (int blk = blk0; blk + 1 < blk_end; ++blk) step(blk, std::true_type{});
+    if (blk0 < blk_end) step(blk_end - 1, std::false_type{});
 
     // ---- merge the four lane groups of this wavefront, then the four wavefronts through LDS
     __shared__ float s_m[kWaves][G], s_l[kWaves][G];
