@@ -26,6 +26,21 @@ def test_decode_crosses_block_table_window(max_splits):
     check_tol(host_out(out), oracle_decode(wl), "bf16", f"long decode max_splits={max_splits}")
 
 
+@pytest.mark.parametrize("name,dtype,fused", [("long_decode", "bf16", False), ("long_decode", "bf16", True),
+                                              ("int8_decode", "i8", False), ("tiny_fp32", "f32", False)])
+def test_decode_next_block_loads_across_window(name, dtype, fused):
+    """The split kernel requests each block's K tile while the previous block is still being
+    attended; across a block-table window reload (67 and 79 blocks in one split) and partial last
+    tiles, with rows nobody writes holding NaN (int8: -128), the result still matches the oracle."""
+    cfg = W.config(name, B=3, ctx=[20000, 17000, 300], pool=None)  # pool sized from the lengths
+    assert cfg["dtype"] == dtype
+    wl = W.decode_workload(cfg, 1)
+    fill = -128 if dtype == "i8" else float("nan")
+    say(f"long decode {name} lens={wl['lens']} fused={fused}")
+    out, _, _ = gpu_decode(wl, "cuda", max_splits=1, fill=fill, fused=fused)
+    check_tol(host_out(out), oracle_decode(wl), dtype, f"long decode {name} fused={fused}")
+
+
 def test_prefill_crosses_block_table_window():
     """96 new tokens after a 16,904-token cached prefix (67 blocks, two windows), next to a short
     prompt; physical blocks shuffled over the pool."""
