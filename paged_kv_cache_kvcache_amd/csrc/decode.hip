@@ -18,10 +18,6 @@
 //   holds elements c*E .. c*E+E-1 of each row, E = head_dim / 16.  Load i of the four groups thus
 //   covers four consecutive rows: one contiguous run of 4 * row_bytes per instruction.
 //   The G query heads that share the KV head live in registers (E elements per head per lane).
-//   Tiles are read through a buffer descriptor per tile whose range ends at the last valid row
-//   (rows past the context end read as zeros).  The next block's K tile is requested as soon as
-//   the current scores are formed, and each block's V tile at the top of its step, so a
-//   wavefront has loads in flight during its own arithmetic.
 //
 // Scores
 //   Each lane forms 16 partial dot products per head (one per row it read).  A 4-step
