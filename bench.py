@@ -63,6 +63,10 @@ def parse():
                     help="beam workloads: attend every beam on its own (pkv_paged_attn_decode); by default a "
                          "step whose requests share at least runner.GROUP_MIN_SHARED keys on average reads "
                          "each request's shared blocks once (pkv_paged_attn_decode_grouped)")
+    ap.add_argument("--group-splits", type=int, default=0,
+                    help="beam configs: cut each request's shared keys into up to this many splits "
+                         "(pkv_paged_attn_decode_grouped_split; 1: one workgroup per request and KV head; "
+                         "0: the runner's choice, about one workgroup per CU)")
     ap.add_argument("--grouped", action="store_true",
                     help="beam workloads: always read each request's shared blocks once")
     ap.add_argument("--graph", action="store_true",
@@ -698,7 +702,8 @@ def bench_beam(args, cfg):
     # the beams of a request are consecutive: grouped attention reads their shared blocks once
     batch = R.DecodeBatch(kv, Hq, list(range(B)), max_ctx, args.max_splits, cow=True,
                           group_size=0 if args.ungrouped else NBM,
-                          group_min_shared=0 if args.grouped else R.GROUP_MIN_SHARED)
+                          group_min_shared=0 if args.grouped else R.GROUP_MIN_SHARED,
+                          group_splits=args.group_splits)
     steps = []
     for s in range(nsteps):
         inp = W.decode_step_inputs(cfg, args.seed, s, B)
@@ -787,7 +792,8 @@ def bench_beam(args, cfg):
         ms_per_step=elapsed / args.steps * 1e3, higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16", data="synthetic",
         config=dict(workload=cfg["name"], requests=NR, beams=NBM, context=f"U[{cfg['ctx'][0]}, {cfg['ctx'][1]}]",
-                    q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256, seed=args.seed),
+                    q_heads=Hq, kv_heads=Hkv, head_dim=D, block_size=256, group_splits=batch.group_splits,
+                    seed=args.seed),
         attention=f"grouped by request in {sum(log_grouped)} of {len(log_grouped)} timed steps, per beam otherwise",
         decode_kernel_us=dec_s * 1e6, decode_gbs_all_beam_reads=dec_gbs,
         copies_per_step=sum(log_copies) / args.steps, copy_kernel_us=copy_s * 1e6,

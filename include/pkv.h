@@ -421,6 +421,38 @@ int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const void* q, int
                                   const int32_t* shared_lens, float softmax_scale, void* out,
                                   void* stream);
 
+/* Grouped decode over splits.  With one workgroup per (group, KV head), a launch lasts as long as
+ * its longest group while the CUs of shorter groups idle; as decode splits a context and merges the
+ * pieces by log-sum-exp (the max_splits knob, intelliparadigm.com Nano-vLLM article, closing
+ * paragraph), each group's shared keys are cut into splits of bps blocks, each walked by its own
+ * workgroups, and a second launch merges every (member, query head)'s splits.
+ *
+ * pkv_decode_grouped_workspace_bytes: the workspace a call with these arguments needs, 0 when it
+ * does not split (bad arguments also give 0): B x Hq x S x (head_dim + 2) floats, with S the
+ * number of splits below.
+ *
+ * pkv_paged_attn_decode_grouped_split: arguments as pkv_paged_attn_decode_grouped, plus
+ *   - max_shared_len: at least every shared_lens entry (device data) and at most
+ *     max_context_len; the splits cover ceil(max_shared_len / 256) blocks;
+ *   - max_splits >= 1: S = ceil(nsh / bps) splits of bps = ceil(nsh / min(max_splits, nsh))
+ *     blocks, nsh = ceil(max_shared_len / 256); only the last split walks the members' own keys
+ *     (those past the shared prefix); S = 1 is the unsplit call;
+ *   - workspace (device, 16-byte aligned, caller-owned, at least
+ *     pkv_decode_grouped_workspace_bytes bytes when that is nonzero; contents on entry ignored).
+ * A bad max_shared_len or max_splits is PKV_ERR_INVALID, a short workspace PKV_ERR_SMALL_BUFFER;
+ * other errors as pkv_paged_attn_decode_grouped.  With device-data checks on, a shared length above
+ * max_shared_len is recorded as error 3 and that group's outputs are left unwritten.  The output
+ * equals that of pkv_paged_attn_decode_grouped up to fp32 rounding order. */
+size_t pkv_decode_grouped_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim, int32_t max_shared_len,
+                                          int32_t max_splits);
+int pkv_paged_attn_decode_grouped_split(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                        const void* k_cache, const void* v_cache, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_tables, int32_t max_blocks,
+                                        const int32_t* context_lens, int32_t max_context_len,
+                                        int32_t group_size, const int32_t* shared_lens, int32_t max_shared_len,
+                                        int32_t max_splits, float softmax_scale, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Varlen paged prefill attention (bf16 cache, bf16 q/out, fp32 accumulation): the engine's
  * full-computation phase, attention over the whole prompt with FlashAttention-2 named as the

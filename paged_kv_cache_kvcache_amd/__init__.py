@@ -80,6 +80,9 @@ SIGNATURES = {
     "pkv_decode_group_shared_lens": (_i32, [_p32, _i32, _p32, _i32, _i32, _p32]),
     "pkv_paged_attn_decode_grouped": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                              _i32, _vp, _f32, _vp, _vp]),
+    "pkv_decode_grouped_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode_grouped_split": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                                   _i32, _i32, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_decode_store_attend": (_i32, [_pdesc, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i32, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _sz, _vp]),
     "pkv_paged_attn_prefill": (_i32, [_pdesc, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
@@ -448,6 +451,35 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, m
         ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), int(group_size),
         _ptr(shared_lens), float(softmax_scale), _ptr(out), _stream(stream)), "pkv_paged_attn_decode_grouped")
+    return out
+
+
+def decode_grouped_workspace_bytes(B, Hq, head_dim, max_shared_len, max_splits):
+    """pkv_decode_grouped_workspace_bytes: the workspace of a grouped decode over splits (0: no split)."""
+    return int(lib().pkv_decode_grouped_workspace_bytes(int(B), int(Hq), int(head_dim), int(max_shared_len),
+                                                        int(max_splits)))
+
+
+def paged_attn_decode_grouped_split(q, k_cache, v_cache, block_tables, context_lens, max_context_len, softmax_scale,
+                                    group_size, shared_lens, max_shared_len, max_splits, workspace=None, out=None,
+                                    k_scale=None, v_scale=None, stream=None):
+    """pkv_paged_attn_decode_grouped_split: grouped decode with each group's shared keys split over up
+    to ``max_splits`` workgroups per KV head and merged by log-sum-exp; ``max_shared_len`` bounds
+    every entry of ``shared_lens``; ``workspace`` (device memory) of at least
+    :func:`decode_grouped_workspace_bytes` bytes when that is nonzero."""
+    desc = desc_of(k_cache)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_grouped_workspace_bytes(B, Hq, D, max_shared_len, max_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_grouped_split(
+        ctypes.byref(desc), _ptr(q), int(B), int(Hq), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), int(group_size),
+        _ptr(shared_lens), int(max_shared_len), int(max_splits), float(softmax_scale), _ptr(out), _ptr(workspace),
+        nbytes, _stream(stream)), "pkv_paged_attn_decode_grouped_split")
     return out
 
 

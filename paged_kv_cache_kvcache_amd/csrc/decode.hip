@@ -338,6 +338,8 @@ struct DecodeArgs {
     // shared_lens[group] keys sit in the same physical blocks
     int32_t group_size;
     const int32_t* shared_lens;
+    int32_t max_shared_len;  // grouped decode over splits: the bound on every shared_lens entry
+    int32_t reduce_all;      // the reduce merges every split slot of a row (grouped decode over splits)
 };
 
 // Device-data checks of one (sequence, split): every block id it reads is in the pool, and so is
@@ -657,7 +659,8 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     if (CHECK && (ctx < 0 || ctx > a.max_context_len)) return;
     const int nblk = (ctx + pkv::kBlock - 1) / pkv::kBlock;
     const int lo_blk = (a.window > 0 ? max(0, ctx - a.window) : 0) / pkv::kBlock;
-    const int active = min(a.splits, (nblk - lo_blk + a.blocks_per_split - 1) / a.blocks_per_split);
+    const int active = a.reduce_all ? a.splits
+                                    : min(a.splits, (nblk - lo_blk + a.blocks_per_split - 1) / a.blocks_per_split);
     const size_t base = (size_t(b) * a.num_q_heads + h) * a.splits;
     if constexpr (CHECK) {
         for (int s = 0; s < active; ++s)
@@ -691,12 +694,19 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
     using T = Traits<DT, D>;
     constexpr int E = T::E, W = T::W, RB = T::kRowBytes, PB = W * 4;
 
-    const int g = blockIdx.y, grp = blockIdx.z;
+    const int g = blockIdx.y, grp = blockIdx.z, split = blockIdx.x;
     const int M = a.group_size, gq = a.num_q_heads / a.num_kv_heads;  // GM == M * gq
     const int b0 = grp * M;
     const int shared = a.shared_lens[grp];
+    // partial slot of query row j of this group and split (grouped decode over splits)
+    auto part_of = [&](int j) {
+        return (size_t(b0 + j / gq) * a.num_q_heads + g * gq + j % gq) * a.splits + split;
+    };
     if (CHECK) {  // uniform in the workgroup
-        bool ok = shared >= 0;
+        // a rejected group's partial states are marked (denominator -1), so the reduce leaves its
+        // outputs unwritten instead of merging whatever the workspace held
+        if (a.splits > 1 && threadIdx.x < GM) a.ws_ml[2 * part_of(threadIdx.x) + 1] = -1.f;
+        bool ok = shared >= 0 && (a.splits == 1 || shared <= a.max_shared_len);
         int bad = 0, val = shared;
         for (int m = 0; ok && m < M; ++m) {
             const int ctx = a.context_lens[b0 + m];
@@ -707,7 +717,7 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
             }
         }
         if (!ok) {
-            if (threadIdx.x == 0 && g == 0) record_error(pkv::kErrLength, bad, val);
+            if (threadIdx.x == 0 && g == 0 && split == 0) record_error(pkv::kErrLength, bad, val);
             return;
         }
         // the shared blocks are one set for every member, and every block read is in the pool
@@ -727,7 +737,7 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
                     const bool blk = bad_blk != 0;
                     const int at = __ffsll(static_cast<unsigned long long>(blk ? bad_blk : bad_sh)) - 1;
                     const int first = __shfl(v, at, 64);
-                    if (threadIdx.x == 0 && g == 0)
+                    if (threadIdx.x == 0 && g == 0 && split == 0)
                         record_error(blk ? pkv::kErrBlock : pkv::kErrShared, b0 + m, blk ? first : e0 + at);
                     return;
                 }
@@ -855,15 +865,19 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
     const int32_t* bt0 = a.block_tables + size_t(b0) * a.max_blocks;
     const int nsh = (shared + pkv::kBlock - 1) / pkv::kBlock;
     const int first = shared / pkv::kBlock;
-    int bt_win = 0;
-    int btv = lane < nsh ? bt0[lane] : 0;
-    int mm = -1, nblk = 0, blk_end = min(nsh, max(0, (shared - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
+    // over splits: split s walks shared blocks s bps .. s bps + bps - 1, and only the last split
+    // walks the members' own keys
+    const int sb0 = split * a.blocks_per_split;
+    const int sb1 = a.splits > 1 ? min(nsh, sb0 + a.blocks_per_split) : nsh;
+    int bt_win = sb0 >> 6;
+    int btv = 64 * bt_win + lane < nsh ? bt0[64 * bt_win + lane] : 0;
+    int mm = -1, nblk = sb0, blk_end = min(sb1, max(sb0, (shared - w * kTile + pkv::kBlock - 1) / pkv::kBlock));
     int wctx = shared, wlo = 0;
     const int32_t* bt = bt0;
     auto next_unit = [&]() __attribute__((always_inline)) {
         Unit u{0, 0, 0, 0, 0, false};
         while (nblk >= blk_end) {  // next member with blocks for this wavefront
-            if (mm + 1 >= M) return u;
+            if (mm + 1 >= M || split + 1 < a.splits) return u;
             ++mm;
             wctx = a.context_lens[b0 + mm];
             bt = a.block_tables + size_t(b0 + mm) * a.max_blocks;
@@ -956,6 +970,15 @@ __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
                 num += f * s_acc[ww][j][d];
                 den += f * s_l[ww][j];
             }
+        }
+        if (a.splits > 1) {  // this split's partial state: O and row sum relative to 2^Mx
+            const size_t part = part_of(j);
+            a.ws_acc[part * D + d] = num;
+            if (d == 0) {
+                a.ws_ml[2 * part] = Mx;
+                a.ws_ml[2 * part + 1] = den;
+            }
+            continue;
         }
         const float o = den > 0.f ? num / den : 0.f;
         const size_t oi = (size_t(b0 + j / gq) * a.num_q_heads + g * gq + j % gq) * D + d;
@@ -1250,7 +1273,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq
 
 template <int DT, int D, int GM>
 hipError_t launch_group_gm(const DecodeArgs& a, int n_groups, hipStream_t st) {
-    const dim3 grid(1, unsigned(a.num_kv_heads), unsigned(n_groups));
+    const dim3 grid(unsigned(a.splits), unsigned(a.num_kv_heads), unsigned(n_groups));
     if (a.check) hipLaunchKernelGGL((decode_group_kernel<DT, D, GM, true>), grid, dim3(kThreads), 0, st, a);
     else hipLaunchKernelGGL((decode_group_kernel<DT, D, GM, false>), grid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
@@ -1408,13 +1431,29 @@ extern "C" int pkv_decode_group_shared_lens(const int32_t* block_tables, int32_t
     return PKV_OK;
 }
 
-extern "C" int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
-                                             const void* k_cache, const void* v_cache, const float* k_scale,
-                                             const float* v_scale, const int32_t* block_tables,
-                                             int32_t max_blocks, const int32_t* context_lens,
-                                             int32_t max_context_len, int32_t group_size,
-                                             const int32_t* shared_lens, float softmax_scale, void* out,
-                                             void* stream) {
+namespace {
+
+template <int D, bool F32_OUT>
+void reduce_all_splits(const DecodeArgs& a, int B, int Hq, bool check, hipStream_t st) {
+    if (check) hipLaunchKernelGGL((decode_reduce_kernel<D, F32_OUT, true>), dim3(Hq, B), dim3(D), 0, st, a);
+    else hipLaunchKernelGGL((decode_reduce_kernel<D, F32_OUT, false>), dim3(Hq, B), dim3(D), 0, st, a);
+}
+
+// Splits of a grouped launch: the shared blocks of the longest shared prefix in at most
+// max_splits runs of bps blocks (S = 1: no split).
+void group_plan(int32_t max_shared_len, int32_t max_splits, int* S, int* bps) {
+    const int nsh = (std::max(0, max_shared_len) + pkv::kBlock - 1) / pkv::kBlock;
+    const int want = std::max(1, std::min(max_splits, std::max(1, nsh)));
+    *bps = std::max(1, (nsh + want - 1) / want);
+    *S = std::max(1, (nsh + *bps - 1) / *bps);
+    if (*S == 1) *bps = 0;
+}
+
+int grouped_impl(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq, const void* k_cache,
+                 const void* v_cache, const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                 int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len, int32_t group_size,
+                 const int32_t* shared_lens, int32_t max_shared_len, int32_t max_splits, float softmax_scale,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = pkv::check_desc(desc);
     if (rc != PKV_OK) return rc;
     const int Hkv = desc->num_kv_heads, D = desc->head_dim;
@@ -1460,6 +1499,20 @@ extern "C" int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const v
     a.check = pkv::device_checks();
     a.group_size = group_size;
     a.shared_lens = shared_lens;
+    int S = 1, bps = 0;
+    group_plan(max_shared_len, max_splits, &S, &bps);
+    if (S > 1) {
+        const size_t need = size_t(B) * Hq * S * (size_t(D) + 2) * sizeof(float);
+        PKV_REQUIRE(workspace != nullptr && workspace_bytes >= need, PKV_ERR_SMALL_BUFFER,
+                    "%d splits need %zu bytes of workspace, %zu given", S, need, workspace_bytes);
+        PKV_REQUIRE((uintptr_t(workspace) & 15) == 0, PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+        a.splits = S;
+        a.blocks_per_split = bps;
+        a.max_shared_len = max_shared_len;
+        a.reduce_all = 1;
+        a.ws_acc = static_cast<float*>(workspace);
+        a.ws_ml = a.ws_acc + size_t(B) * Hq * S * D;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int ng = B / group_size;
     hipError_t e;
@@ -1469,7 +1522,52 @@ extern "C" int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const v
         default: e = launch_group<PKV_I8>(a, ng, GM, D, st); break;
     }
     PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "grouped decode launch failed: %s", hipGetErrorString(e));
+    if (S > 1) {
+        const bool f32 = desc->kv_dtype == PKV_F32, chk = a.check != 0;
+        if (D == 64) f32 ? reduce_all_splits<64, true>(a, B, Hq, chk, st) : reduce_all_splits<64, false>(a, B, Hq, chk, st);
+        else f32 ? reduce_all_splits<128, true>(a, B, Hq, chk, st) : reduce_all_splits<128, false>(a, B, Hq, chk, st);
+        e = hipGetLastError();
+        PKV_REQUIRE(e == hipSuccess, PKV_ERR_HIP, "grouped decode reduce launch failed: %s", hipGetErrorString(e));
+    }
     return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pkv_paged_attn_decode_grouped(const pkv_cache_desc* desc, const void* q, int32_t B, int32_t Hq,
+                                             const void* k_cache, const void* v_cache, const float* k_scale,
+                                             const float* v_scale, const int32_t* block_tables,
+                                             int32_t max_blocks, const int32_t* context_lens,
+                                             int32_t max_context_len, int32_t group_size,
+                                             const int32_t* shared_lens, float softmax_scale, void* out,
+                                             void* stream) {
+    return grouped_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
+                        max_context_len, group_size, shared_lens, 0, 1, softmax_scale, out, nullptr, 0, stream);
+}
+
+extern "C" size_t pkv_decode_grouped_workspace_bytes(int32_t B, int32_t Hq, int32_t head_dim,
+                                                     int32_t max_shared_len, int32_t max_splits) {
+    if (B <= 0 || Hq <= 0 || head_dim <= 0 || max_shared_len < 0 || max_splits < 0) return 0;
+    int S, bps;
+    group_plan(max_shared_len, max_splits, &S, &bps);
+    return S > 1 ? size_t(B) * Hq * S * (size_t(head_dim) + 2) * sizeof(float) : 0;
+}
+
+extern "C" int pkv_paged_attn_decode_grouped_split(const pkv_cache_desc* desc, const void* q, int32_t B,
+                                                   int32_t Hq, const void* k_cache, const void* v_cache,
+                                                   const float* k_scale, const float* v_scale,
+                                                   const int32_t* block_tables, int32_t max_blocks,
+                                                   const int32_t* context_lens, int32_t max_context_len,
+                                                   int32_t group_size, const int32_t* shared_lens,
+                                                   int32_t max_shared_len, int32_t max_splits, float softmax_scale,
+                                                   void* out, void* workspace, size_t workspace_bytes,
+                                                   void* stream) {
+    PKV_REQUIRE(max_shared_len >= 0 && max_shared_len <= max_context_len && max_splits >= 1, PKV_ERR_INVALID,
+                "max_shared_len = %d (0..max_context_len %d), max_splits = %d (>= 1)", max_shared_len,
+                max_context_len, max_splits);
+    return grouped_impl(desc, q, B, Hq, k_cache, v_cache, k_scale, v_scale, block_tables, max_blocks, context_lens,
+                        max_context_len, group_size, shared_lens, max_shared_len, max_splits, softmax_scale, out,
+                        workspace, workspace_bytes, stream);
 }
 
 int pkv::read_error_decode(void* stream, int32_t* out) { return read_clear_error(stream, out); }

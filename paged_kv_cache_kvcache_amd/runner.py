@@ -12,11 +12,17 @@ import numpy as np
 import torch
 
 from . import (BF16, BLOCK, F32, I8, Allocator, _check, copy_blocks, decode_group_shared_lens, decode_plan,
-               decode_store_attend, paged_attn_decode_grouped,
+               decode_grouped_workspace_bytes, decode_store_attend, paged_attn_decode_grouped,
+               paged_attn_decode_grouped_split,
                decode_workspace_bytes, desc_of, kv_store, kv_store_quant, lib, paged_attn_decode,
                paged_attn_prefill_split, prefill_split_order, prefill_split_workspace_bytes)
 
 TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}
+# grouped decode over splits (DecodeBatch(group_splits=0)): splits ~ CUs / (groups x KV heads), at
+# most this many; measured on MI355X, bf16, 16 / 8 heads, 4 beams over 8k-32k-token prompts: 1, 2, 4
+# and 8 requests run best at 16, 16, 4 and 4 splits, 32 requests unsplit
+GROUP_MAX_SPLITS = 16
+
 # mean shared keys per group from which DecodeBatch reads a group's shared blocks once
 # (pkv_paged_attn_decode_grouped); measured crossover on MI355X, bf16, 16 / 8 heads, D 128
 GROUP_MIN_SHARED = 1536
@@ -88,7 +94,7 @@ class DecodeBatch:
     (``fused``: the step's store and attention in one launch, pkv_decode_store_attend)."""
 
     def __init__(self, kv, Hq, seq_ids, max_context_len, max_splits=0, fused=False, window=0, cow=False,
-                 group_size=0, group_min_shared=GROUP_MIN_SHARED):
+                 group_size=0, group_min_shared=GROUP_MIN_SHARED, group_splits=0):
         self.kv = kv
         self.Hq = int(Hq)
         self.ids = np.asarray(seq_ids, dtype=np.int64)
@@ -105,6 +111,14 @@ class DecodeBatch:
         # sequence reads them, and the per-sequence kernel is faster there.
         self.group_size = int(group_size)
         self.group_min_shared = int(group_min_shared)
+        # > 1: a grouped step cuts each group's shared keys into up to group_splits splits, merged
+        # by log-sum-exp (pkv_paged_attn_decode_grouped_split), so that a launch of few groups does
+        # not leave CUs idle; 0: about one workgroup per CU, at most GROUP_MAX_SPLITS splits
+        if group_splits <= 0 and group_size:
+            cus = torch.cuda.get_device_properties(kv.device).multi_processor_count
+            group_splits = max(1, min(GROUP_MAX_SPLITS, cus // max(1, len(seq_ids) // group_size * kv.Hkv)))
+        self.group_splits = max(1, int(group_splits))
+        self.max_shared = 0
         self.grouped = False  # the path the last uploaded step takes
         if self.fused and self.window:
             raise ValueError("the fused store+attend step has no sliding window")
@@ -133,6 +147,7 @@ class DecodeBatch:
         self._cow = self._meta[nmeta:nmeta + ncow]
         self._groups_at = nmeta + ncow
         self.shared_lens = self._meta[self._groups_at:self._groups_at + ngroups]  # per group
+        self._group_ws = None
         self.n_copies = 0
         # the split plan the library uses: a window of W keys spans at most ceil((W + 255) / 256) blocks
         span = min(self.max_context_len, self.window + BLOCK - 1) if self.window else self.max_context_len
@@ -174,6 +189,7 @@ class DecodeBatch:
             sh = pin[self._groups_at:self._groups_at + ng]
             decode_group_shared_lens(tab, lens, self.group_size, out=sh)
             self.host_shared_lens = sh
+            self.max_shared = int(sh.max()) if ng else 0
             self.grouped = bool(sh.mean() >= self.group_min_shared)
             if self.grouped:
                 return
@@ -211,6 +227,16 @@ class DecodeBatch:
                                   seq_order=self.seq_order)
 
     def attend(self, q, softmax_scale, out=None):
+        if self.grouped and self.group_splits > 1:
+            if self._group_ws is None:  # sized for the largest plan: group_splits splits
+                nb = decode_grouped_workspace_bytes(self.B, self.Hq, self.kv.D, BLOCK * self.group_splits,
+                                                    self.group_splits)
+                self._group_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=self.kv.device)
+            return paged_attn_decode_grouped_split(q, self.kv.k_cache, self.kv.v_cache, self.block_tables,
+                                                   self.context_lens, self.max_context_len, softmax_scale,
+                                                   self.group_size, self.shared_lens, self.max_shared,
+                                                   self.group_splits, workspace=self._group_ws, out=out,
+                                                   k_scale=self.kv.k_scale, v_scale=self.kv.v_scale)
         if self.grouped:
             return paged_attn_decode_grouped(q, self.kv.k_cache, self.kv.v_cache, self.block_tables,
                                              self.context_lens, self.max_context_len, softmax_scale, self.group_size,

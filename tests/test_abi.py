@@ -153,6 +153,34 @@ def test_grouped_decode_rejects_bad_arguments():
     assert _grouped(d, B=0) == P.OK
 
 
+def test_grouped_split_workspace_and_rejections():
+    """pkv_decode_grouped_workspace_bytes: B x Hq x S x (D + 2) floats with S = ceil(nsh / bps),
+    bps = ceil(nsh / min(max_splits, nsh)), nsh = ceil(max_shared_len / 256); 0 without a split.
+    pkv_paged_attn_decode_grouped_split rejects bad bounds and a short workspace on the host."""
+    for B, Hq, D, msl, ms in [(8, 16, 128, 20000, 4), (4, 8, 64, 300, 8), (4, 8, 64, 256, 8), (2, 4, 128, 9000, 5),
+                              (2, 4, 128, 9000, 1), (2, 4, 128, 0, 3)]:
+        nsh = -(-msl // 256)
+        want = max(1, min(ms, max(1, nsh)))
+        bps = max(1, -(-nsh // want))
+        S = max(1, -(-nsh // bps))
+        assert P.decode_grouped_workspace_bytes(B, Hq, D, msl, ms) == (B * Hq * S * (D + 2) * 4 if S > 1 else 0)
+    assert P.decode_grouped_workspace_bytes(8, 16, 128, 20000, 4) == 8 * 16 * 4 * 130 * 4  # 79 blocks: 4 x 20
+    assert P.decode_grouped_workspace_bytes(0, 16, 128, 20000, 4) == 0
+
+    d = _desc()  # 2 KV heads, D 64
+
+    def call(max_shared=500, max_splits=2, ws=FAKE, ws_bytes=1 << 30, max_ctx=600):
+        return P.lib().pkv_paged_attn_decode_grouped_split(ctypes.byref(d), FAKE, 4, 4, FAKE, FAKE, None, None, FAKE,
+                                                           3, FAKE, max_ctx, 2, FAKE, max_shared, max_splits, 0.125,
+                                                           FAKE, ws, ws_bytes, None)
+    assert call(max_shared=700) == P.ERR_INVALID      # above max_context_len
+    assert call(max_shared=-1) == P.ERR_INVALID
+    assert call(max_splits=0) == P.ERR_INVALID
+    assert call(ws=None, ws_bytes=0) == P.ERR_SMALL_BUFFER   # two splits of the 2 shared blocks need one
+    assert call(ws_bytes=16) == P.ERR_SMALL_BUFFER
+    assert call(ws=ctypes.c_void_p((1 << 20) + 4)) == P.ERR_INVALID  # misaligned workspace
+
+
 def _shared_lens_by_definition(tab, lens, m):
     """Per group: the shortest member's length, cut at 256 x the first block entry where the
     members' tables differ (only entries below that length count)."""

@@ -139,7 +139,7 @@ class Both:
         check_tol(out.float().cpu().numpy().astype(np.float64), ref, "bf16" if self.mode == "bf16" else "i8", what)
 
 
-    def decode_grouped(self, ids, group_size, hq, what):
+    def decode_grouped(self, ids, group_size, hq, what, splits=()):
         """pkv_paged_attn_decode_grouped over groups of ``group_size`` consecutive ``ids`` against
         the oracle's plain decode of every sequence; returns the groups' shared lengths."""
         lens = [self.oa.seq_len(i) for i in ids]
@@ -163,6 +163,19 @@ class Both:
         ref = OT.decode(W.bf16_bits_to_f32(bits), *self.oc[:2], tab.tolist(), lens, 1.0 / math.sqrt(self.d),
                         *(self.oc[2:] if self.mode != "bf16" else (None, None)))
         check_tol(out.float().cpu().numpy().astype(np.float64), ref, "bf16" if self.mode == "bf16" else "i8", what)
+        # the same groups over splits of their shared keys (pkv_paged_attn_decode_grouped_split),
+        # with every split count up to more splits than shared blocks; max_shared_len above the
+        # longest shared length, so trailing splits of every group are empty
+        for ms in splits:
+            max_sh = min(max(lens), int(shared.max()) + 300)
+            need = P.decode_grouped_workspace_bytes(len(ids), hq, self.d, max_sh, ms)
+            ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device=self.device)  # NaN bytes
+            got = P.paged_attn_decode_grouped_split(q, self.kv.k_cache, self.kv.v_cache, _dev(tab, self.device),
+                                                    _dev(dlens, self.device), max(lens), 1.0 / math.sqrt(self.d),
+                                                    group_size, _dev(shared, self.device), max_sh, ms,
+                                                    workspace=ws, k_scale=ks, v_scale=vs)
+            check_tol(got.float().cpu().numpy().astype(np.float64), ref, "bf16" if self.mode == "bf16" else "i8",
+                      f"{what} split {ms} (workspace {need} bytes)")
         return shared.tolist()
 
 
@@ -199,6 +212,29 @@ def test_grouped_decode_matches_oracle(gpu, mode, hq, hkv, d, m):
         say(f"  {mode} hq={hq} hkv={hkv} d={d} m={m} step {step}: shared {shared}, lengths {lens}")
         both.oa.check_invariants()
     assert seen_partial or m == 1  # some member read keys beyond its group's shared ones
+
+
+@pytest.mark.parametrize("mode,hq,hkv,d,m", [("bf16", 8, 4, 128, 4), ("bf16", 2, 2, 64, 8), ("i8", 8, 8, 128, 1),
+                                             ("i8q", 4, 2, 128, 2)])
+def test_grouped_split_decode_matches_oracle(gpu, mode, hq, hkv, d, m):
+    """pkv_paged_attn_decode_grouped_split against the oracle: groups of m forks over prompts of
+    different lengths (2,000-4,700 tokens, 8-19 blocks), members that diverge inside a group, and
+    1, 2, 3, 7 and 64 splits of the shared keys (the short groups' last splits are empty)."""
+    both = Both(mode, gpu, seed=40 + m, hkv=hkv, d=d, nb=260)
+    rnd = np.random.default_rng(100 + m)
+    groups = []
+    for r, n in enumerate([4700, 2000, 3333]):
+        both.add(100 * r, rnd.integers(0, 1000, size=n).tolist())
+        for k in range(1, m):
+            both.fork(100 * r, 100 * r + k)
+        groups.append([100 * r + k for k in range(m)])
+    flat = lambda: [i for g in groups for i in g]
+    for step in range(3):
+        if step == 1:  # the first member of every group runs ahead of the others
+            both.step([g[0] for g in groups])
+        both.step(flat())
+        shared = both.decode_grouped(flat(), m, hq, f"{mode} m={m} step {step}", splits=(1, 2, 3, 7, 64))
+        say(f"  {mode} hq={hq} hkv={hkv} d={d} m={m} step {step}: shared {shared}")
 
 
 @pytest.mark.parametrize("mode", ["bf16", "i8", "i8q"])
@@ -268,10 +304,12 @@ def test_decode_batch_with_copy_on_write(gpu, fused):
         both.check_caches(f"fused={fused} step {step}")
 
 
-@pytest.mark.parametrize("min_shared", [0, 1 << 30])
-def test_decode_batch_grouped(gpu, min_shared):
+@pytest.mark.parametrize("min_shared,group_splits", [(0, 0), (0, 1), (1 << 30, 0)])
+def test_decode_batch_grouped(gpu, min_shared, group_splits):
     """DecodeBatch with group_size: two requests of two beams each, steps with copy-on-write and a
-    re-fork; min_shared 0 takes the grouped kernel every step, a huge one the per-sequence one."""
+    re-fork; min_shared 0 takes the grouped kernel every step, a huge one the per-sequence one;
+    group_splits 0 lets the runner split the two groups' shared keys (few groups: many splits), 1
+    keeps one workgroup per group and KV head."""
     both = Both("bf16", gpu, seed=13)
     rnd = np.random.default_rng(8)
     both.add(0, rnd.integers(0, 1000, size=700).tolist())
@@ -279,7 +317,9 @@ def test_decode_batch_grouped(gpu, min_shared):
     both.fork(0, 1000)
     both.fork(1, 1001)
     ids = [0, 1000, 1, 1001]
-    batch = R.DecodeBatch(both.kv, HQ, ids, 800, cow=True, group_size=2, group_min_shared=min_shared)
+    batch = R.DecodeBatch(both.kv, HQ, ids, 800, cow=True, group_size=2, group_min_shared=min_shared,
+                          group_splits=group_splits)
+    assert (batch.group_splits > 1) == (group_splits == 0)  # two groups leave most CUs idle unsplit
     for step in range(4):
         if step == 2:  # the second beam of request 0 is replaced by a fork of the first
             both.free(1000)
