@@ -204,9 +204,13 @@ def test_ordered_prefill_rejects_an_item_outside_the_call(checks):
 SHARED = 8
 
 
-@pytest.mark.parametrize("case", ["tables differ", "shared past a context", "block outside the pool"])
-def test_grouped_decode_rejects_a_bad_group(checks, case):
-    """pkv_paged_attn_decode_grouped, two groups of two sequences: group 0 is bad in one way, group 1
+@pytest.mark.parametrize("case,split", [("tables differ", False), ("shared past a context", False),
+                                        ("block outside the pool", False), ("tables differ", True),
+                                        ("shared past a context", True), ("block outside the pool", True),
+                                        ("shared past its bound", True)])
+def test_grouped_decode_rejects_a_bad_group(checks, case, split):
+    """pkv_paged_attn_decode_grouped (split: pkv_paged_attn_decode_grouped_split over two splits, the
+    workspace filled with NaN bytes), two groups of two sequences: group 0 is bad in one way, group 1
     is valid.  Group 0's outputs stay unwritten, group 1's match the plain decode."""
     dev = checks
     _, (kc, vc) = _caches(dev)
@@ -220,6 +224,8 @@ def test_grouped_decode_rejects_a_bad_group(checks, case):
         expect = (SHARED, 1, 1)
     elif case == "shared past a context":
         shared[0] = 500
+        expect = (LENGTH, 0, 500 if split else 400)  # over splits, the bound (400) is checked first
+    elif case == "shared past its bound":  # 400 shared keys, but the call's bound is 300
         expect = (LENGTH, 0, 400)
     else:
         tab[1][1] = tab[0][1] = NB  # shared, but outside the pool
@@ -227,7 +233,14 @@ def test_grouped_decode_rejects_a_bad_group(checks, case):
     q = torch.randn(4, HQ, D, device=dev).to(torch.bfloat16)
     out = torch.full_like(q, 7.0)
     t, ln = _i32(tab, dev), _i32(lens, dev)
-    P.paged_attn_decode_grouped(q, kc, vc, t, ln, 400, 0.088, 2, _i32(shared, dev), out=out)
+    if split:
+        bound = 300 if case == "shared past its bound" else 400
+        ws = torch.full((P.decode_grouped_workspace_bytes(4, HQ, D, bound, 2),), 0xFF, dtype=torch.uint8, device=dev)
+        assert ws.numel() > 0  # the call splits
+        P.paged_attn_decode_grouped_split(q, kc, vc, t, ln, 400, 0.088, 2, _i32(shared, dev), bound, 2, workspace=ws,
+                                          out=out)
+    else:
+        P.paged_attn_decode_grouped(q, kc, vc, t, ln, 400, 0.088, 2, _i32(shared, dev), out=out)
     _expect(*expect)
     assert bool((out[:2] == 7.0).all())
     ref = P.paged_attn_decode(q[2:], kc, vc, t[2:], ln[2:], 400, 0.088)
