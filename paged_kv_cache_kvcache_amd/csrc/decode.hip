@@ -18,6 +18,10 @@
 //   holds elements c*E .. c*E+E-1 of each row, E = head_dim / 16.  Load i of the four groups thus
 //   covers four consecutive rows: one contiguous run of 4 * row_bytes per instruction.
 //   The G query heads that share the KV head live in registers (E elements per head per lane).
+//   Tiles are read through a buffer descriptor per tile whose range ends at the last valid row
+//   (rows past the context end read as zeros).  The next block's K tile is requested as soon as
+//   the current scores are formed, and each block's V tile at the top of its step, so a
+//   wavefront has loads in flight during its own arithmetic.
 //
 // Scores
 //   Each lane forms 16 partial dot products per head (one per row it read).  A 4-step
@@ -688,7 +692,9 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
 // each member's remaining keys for its own Gq rows only, and writes the members' outputs: the
 // shared keys cross HBM once per group instead of once per member.  The per-block work is that of
 // decode_split_kernel (same lane layout, reductions and online softmax), with rows outside the
-// member skipped while its own keys are read.
+// member skipped while its own keys are read.  Over splits (blockIdx.x, pkv_paged_attn_decode_
+// grouped_split), split s walks shared blocks s*bps .. s*bps + bps - 1, the last split also the
+// members' own keys, and each writes its partial state for the split reduce.
 template <int DT, int D, int GM, bool CHECK>
 __global__ __launch_bounds__(kThreads) void decode_group_kernel(DecodeArgs a) {
     using T = Traits<DT, D>;
