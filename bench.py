@@ -67,6 +67,9 @@ def parse():
                     help="beam configs: cut each request's shared keys into up to this many splits "
                          "(pkv_paged_attn_decode_grouped_split; 1: one workgroup per request and KV head; "
                          "0: the runner's choice, about one workgroup per CU)")
+    ap.add_argument("--requests", type=int, default=0,
+                    help="beam configs: this many requests instead of the workload's (few requests: few "
+                         "groups, where --group-splits matters)")
     ap.add_argument("--grouped", action="store_true",
                     help="beam workloads: always read each request's shared blocks once")
     ap.add_argument("--graph", action="store_true",
@@ -971,6 +974,8 @@ def main():
         elif cfg["kind"] == "store":
             res = bench_int8_store(args, cfg)
         elif cfg["kind"] == "beam":
+            if args.requests > 0:
+                cfg = W.config(args.config, B=args.requests)
             res = bench_beam(args, cfg)
         else:
             res = bench_prefill(args, cfg)
