@@ -26,6 +26,12 @@ GROUP_MAX_SPLITS = 16
 # mean shared keys per group from which DecodeBatch reads a group's shared blocks once
 # (pkv_paged_attn_decode_grouped); measured crossover on MI355X, bf16, 16 / 8 heads, D 128
 GROUP_MIN_SHARED = 1536
+# ... and whose shared keys hold more K/V bytes than this (the 256 MB MALL): below it the
+# per-sequence kernel's re-reads of the shared blocks hit the MALL, and it wins the step (measured
+# on MI355X, 4 beams over 16k-32k-token prompts: 1 and 2 requests, about 100 and 200 MB, per
+# sequence 0.089-0.099 ms against 0.109-0.113 ms grouped; 4 requests, about 400 MB, 0.193 against
+# 0.146 ms)
+GROUP_MIN_SHARED_BYTES = 256 << 20
 
 
 def _to_dev(a, device, dtype=None):
@@ -106,9 +112,11 @@ class DecodeBatch:
         self.window = int(window)  # > 0: sliding-window attention over the last `window` keys
         self.cow = bool(cow)  # sequences share blocks (forks): appends copy shared partial blocks
         # > 0: sequences k*group_size .. k*group_size + group_size - 1 are forks of one request.  A step
-        # whose groups share at least group_min_shared keys on average reads them once per group
-        # (pkv_paged_attn_decode_grouped); shorter shared prefixes stay in the caches when every
-        # sequence reads them, and the per-sequence kernel is faster there.
+        # whose groups share at least group_min_shared keys on average, and more than
+        # GROUP_MIN_SHARED_BYTES of K/V in all, reads them once per group
+        # (pkv_paged_attn_decode_grouped); shorter or fewer shared prefixes stay in the caches when
+        # every sequence reads them, and the per-sequence kernel is faster there.  group_min_shared
+        # = 0 takes the grouped kernel every step.
         self.group_size = int(group_size)
         self.group_min_shared = int(group_min_shared)
         # > 1: a grouped step cuts each group's shared keys into up to group_splits splits, merged
@@ -190,7 +198,9 @@ class DecodeBatch:
             decode_group_shared_lens(tab, lens, self.group_size, out=sh)
             self.host_shared_lens = sh
             self.max_shared = int(sh.max()) if ng else 0
-            self.grouped = bool(sh.mean() >= self.group_min_shared)
+            shared_bytes = int(sh.sum()) * self.kv.Hkv * self.kv.D * self.kv.k_cache.element_size() * 2
+            self.grouped = self.group_min_shared == 0 or bool(
+                sh.mean() >= self.group_min_shared and shared_bytes >= GROUP_MIN_SHARED_BYTES)
             if self.grouped:
                 return
         # longest contexts first; when the whole launch is resident at once, balanced per CU
